@@ -1,0 +1,253 @@
+"""CPU oracle for the 4-bit block-dequant matmul and the int8 tied head.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package.
+Only the tests, the smoke check and the benchmark's CPU-baseline leg call it.
+It shares no code with the HIP library (``w4_block_dequant_amd``) and does not
+import it; the two meet only in the tests, which feed both the same seeded
+inputs from the separate ``synth`` module.
+
+The arithmetic lives in plain C (``oracle.c``, built with gcc, no fast-math,
+no FMA contraction); this file only builds the shared object and marshals
+numpy arrays.  What each function computes, and the passage of the page
+"ONNX export, quantization and the browser runtime" it follows, is stated in
+``oracle.h``.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+closed forms, exhaustive enumeration, exact rational arithmetic and special
+cases (see that file's header).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+          "-Wall", "-Wextra"]
+
+OK, BAD_SHAPE, NONFINITE, NO_MEMORY = 0, 1, 2, 3
+BLOCK = 32
+
+
+class OracleError(RuntimeError):
+    """A nonzero status from the C oracle."""
+
+    def __init__(self, fn: str, status: int):
+        names = {BAD_SHAPE: "BAD_SHAPE", NONFINITE: "NONFINITE", NO_MEMORY: "NO_MEMORY"}
+        super().__init__(f"{fn}: status {status} ({names.get(status, '?')})")
+        self.status = status
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile ``src`` into the shared object ``out`` with gcc (about a second)."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+_SIGS = {
+    "orc_pack_u4": (None, [_P, _I64, _P]),
+    "orc_unpack_u4": (None, [_P, _I64, _P]),
+    "orc_w4_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "orc_w4_unpack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "orc_w4_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "orc_matmul_f64": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "orc_w4_matmul": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
+    "orc_i8_quantize_head": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "orc_i8_dequantize_head": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P]),
+    "orc_i8_head_logits": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _P]),
+    "orc_i8_embed": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _P]),
+}
+
+
+def load_library(path: str):
+    """Load a compiled oracle (the default one, or a variant a test built)."""
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def _stale() -> bool:
+    if not os.path.exists(_LIB):
+        return True
+    t = os.path.getmtime(_LIB)
+    return any(os.path.getmtime(p) > t for p in (_SRC, _HDR))
+
+
+def lib():
+    """The default oracle library, built on first use if missing or stale."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if _stale():
+                build()
+            _lib = load_library(_LIB)
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(fn: str, st: int):
+    if st != OK:
+        raise OracleError(fn, st)
+
+
+class Oracle:
+    """numpy front end over one compiled oracle library."""
+
+    def __init__(self, clib=None):
+        self._l = clib if clib is not None else lib()
+
+    # -- nibble packing -------------------------------------------------------
+    def pack_u4(self, v):
+        v = _c(v, np.uint8).reshape(-1)
+        assert v.size % 2 == 0
+        out = np.empty(v.size // 2, np.uint8)
+        self._l.orc_pack_u4(_ptr(v), v.size, _ptr(out))
+        return out
+
+    def unpack_u4(self, packed):
+        p = _c(packed, np.uint8).reshape(-1)
+        v = np.empty(p.size * 2, np.uint8)
+        self._l.orc_unpack_u4(_ptr(p), v.size, _ptr(v))
+        return v
+
+    # -- 4-bit block format -----------------------------------------------------
+    def quantize_pack(self, W):
+        """W fp32 [K, N] -> (Wq uint8 [K, N/2], scales fp32 [K/32, N], zeros uint8 [K/32, N/2])."""
+        W = _c(W, np.float32)
+        K, N = W.shape
+        Wq = np.zeros((K, N // 2), np.uint8)
+        s = np.zeros((K // BLOCK, N), np.float32)
+        z = np.zeros((K // BLOCK, N // 2), np.uint8)
+        _check("orc_w4_quantize_pack",
+               self._l.orc_w4_quantize_pack(_ptr(W), K, N, _ptr(Wq), _ptr(s), _ptr(z)))
+        return Wq, s, z
+
+    def unpack(self, Wq, zeros, K, N):
+        """-> (q uint8 [K, N], z uint8 [K/32, N])."""
+        q = np.zeros((K, N), np.uint8)
+        z = np.zeros((K // BLOCK, N), np.uint8)
+        _check("orc_w4_unpack", self._l.orc_w4_unpack(_ptr(_c(Wq, np.uint8)),
+                                                      _ptr(_c(zeros, np.uint8)), K, N,
+                                                      _ptr(q), _ptr(z)))
+        return q, z
+
+    def dequantize(self, Wq, scales, zeros, K, N):
+        """-> W_hat fp32 [K, N]."""
+        out = np.zeros((K, N), np.float32)
+        _check("orc_w4_dequantize",
+               self._l.orc_w4_dequantize(_ptr(_c(Wq, np.uint8)), _ptr(_c(scales, np.float32)),
+                                         _ptr(_c(zeros, np.uint8)), K, N, _ptr(out)))
+        return out
+
+    def matmul_f64(self, x, W, bias=None):
+        """x fp32 [M, K], W fp32 [K, N] -> (y fp32 [M, N], bound fp64 [M, N])."""
+        x = _c(x, np.float32)
+        W = _c(W, np.float32)
+        M, K = x.shape
+        K2, N = W.shape
+        assert K == K2
+        b = None if bias is None else _c(bias, np.float32)
+        y = np.zeros((M, N), np.float32)
+        bound = np.zeros((M, N), np.float64)
+        _check("orc_matmul_f64", self._l.orc_matmul_f64(_ptr(x), M, K, _ptr(W), N, _ptr(b),
+                                                        _ptr(y), _ptr(bound)))
+        return y, bound
+
+    def w4_matmul(self, x, Wq, scales, zeros, bias=None):
+        """y = x . dequantize(Wq, scales, zeros) (+ bias) -> (y [M, N], bound [M, N])."""
+        x = _c(x, np.float32)
+        M, K = x.shape
+        N = _c(scales, np.float32).shape[1]
+        b = None if bias is None else _c(bias, np.float32)
+        y = np.zeros((M, N), np.float32)
+        bound = np.zeros((M, N), np.float64)
+        _check("orc_w4_matmul",
+               self._l.orc_w4_matmul(_ptr(x), M, K, _ptr(_c(Wq, np.uint8)),
+                                     _ptr(_c(scales, np.float32)), _ptr(_c(zeros, np.uint8)),
+                                     N, _ptr(b), _ptr(y), _ptr(bound)))
+        return y, bound
+
+    # -- int8 head -------------------------------------------------------------
+    def i8_quantize_head(self, E, ldq=None):
+        """E fp32 [K, N] -> (Q int8 [K, ldq], hs fp32 [N])."""
+        E = _c(E, np.float32)
+        K, N = E.shape
+        ldq = N if ldq is None else ldq
+        Q = np.zeros((K, ldq), np.int8)
+        hs = np.zeros(N, np.float32)
+        _check("orc_i8_quantize_head",
+               self._l.orc_i8_quantize_head(_ptr(E), K, N, ldq, _ptr(Q), _ptr(hs)))
+        return Q, hs
+
+    def i8_dequantize_head(self, Q, hs):
+        Q = _c(Q, np.int8)
+        hs = _c(hs, np.float32)
+        K, ldq = Q.shape
+        N = hs.size
+        out = np.zeros((K, N), np.float32)
+        _check("orc_i8_dequantize_head",
+               self._l.orc_i8_dequantize_head(_ptr(Q), ldq, _ptr(hs), K, N, _ptr(out)))
+        return out
+
+    def i8_head_logits(self, x_last, Q, hs):
+        """x_last fp32 [K] -> (logits fp32 [N], bound fp64 [N])."""
+        x = _c(x_last, np.float32).reshape(-1)
+        Q = _c(Q, np.int8)
+        hs = _c(hs, np.float32)
+        K, ldq = Q.shape
+        assert x.size == K
+        N = hs.size
+        out = np.zeros(N, np.float32)
+        bound = np.zeros(N, np.float64)
+        _check("orc_i8_head_logits",
+               self._l.orc_i8_head_logits(_ptr(x), K, _ptr(Q), ldq, _ptr(hs), N, _ptr(out),
+                                          _ptr(bound)))
+        return out, bound
+
+    def i8_embed(self, tokens, Q, hs):
+        """tokens int64 [T] -> fp32 [T, K] rows of the dequantized table."""
+        t = _c(tokens, np.int64).reshape(-1)
+        Q = _c(Q, np.int8)
+        hs = _c(hs, np.float32)
+        K, ldq = Q.shape
+        N = hs.size
+        out = np.zeros((t.size, K), np.float32)
+        _check("orc_i8_embed", self._l.orc_i8_embed(_ptr(t), t.size, _ptr(Q), ldq, _ptr(hs),
+                                                    K, N, _ptr(out)))
+        return out
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

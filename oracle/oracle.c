@@ -1,0 +1,226 @@
+/*
+ * CPU oracle: plain, slow, obviously correct.  TEST INFRASTRUCTURE ONLY (see
+ * oracle.h).  Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off.
+ * No intrinsics, no threads, no blocking: every output is one loop over its
+ * definition.  fp32 steps are written as fp32 expressions (x86-64 evaluates
+ * float in float); fp64 steps are explicit casts to double.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define BLOCK 32
+
+static int bad_w4_shape(int64_t K, int64_t N)
+{
+    return K < 0 || N < 0 || K % BLOCK != 0 || N % 2 != 0;
+}
+
+void orc_pack_u4(const uint8_t *v, int64_t count, uint8_t *out)
+{
+    for (int64_t i = 0; i < count / 2; ++i)
+        out[i] = (uint8_t)((v[2 * i] & 15) | ((v[2 * i + 1] & 15) << 4));
+}
+
+void orc_unpack_u4(const uint8_t *in, int64_t count, uint8_t *v)
+{
+    for (int64_t i = 0; i < count / 2; ++i) {
+        v[2 * i] = (uint8_t)(in[i] & 15);
+        v[2 * i + 1] = (uint8_t)(in[i] >> 4);
+    }
+}
+
+/* clamp a float that holds an integer value into [lo, hi] and return it as int */
+static int clamp_int(float v, int lo, int hi)
+{
+    if (v < (float)lo) return lo;
+    if (v > (float)hi) return hi;
+    return (int)v;
+}
+
+/* One block: 32 weights w[r * stride], r = 0..31.  Writes s, z and q[0..31]. */
+static int quantize_block(const float *w, int64_t stride, float *s_out, uint8_t *z_out,
+                          uint8_t *q_out)
+{
+    float lo = 0.0f, hi = 0.0f; /* the range always contains 0 */
+    for (int r = 0; r < BLOCK; ++r) {
+        float v = w[r * stride];
+        if (!isfinite(v)) return ORC_NONFINITE;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+    }
+    float range = hi - lo;
+    float s = range / 15.0f;
+    if (!isfinite(s)) return ORC_NONFINITE;
+    if (s == 0.0f) { /* all-zero block: every code and the zero point are 0 */
+        *s_out = 0.0f;
+        *z_out = 0;
+        for (int r = 0; r < BLOCK; ++r) q_out[r] = 0;
+        return ORC_OK;
+    }
+    float zr = rintf(-lo / s);
+    int z = clamp_int(zr, 0, 15);
+    for (int r = 0; r < BLOCK; ++r) {
+        float t = rintf(w[r * stride] / s);
+        q_out[r] = (uint8_t)clamp_int(t + (float)z, 0, 15);
+    }
+    *s_out = s;
+    *z_out = (uint8_t)z;
+    return ORC_OK;
+}
+
+int orc_w4_quantize_pack(const float *W, int64_t K, int64_t N,
+                         uint8_t *Wq, float *scales, uint8_t *zeros)
+{
+    if (bad_w4_shape(K, N)) return ORC_BAD_SHAPE;
+    int64_t nb = K / BLOCK;
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    uint8_t *z = (uint8_t *)malloc((size_t)(nb * N) + 1);
+    if (!q || !z) { free(q); free(z); return ORC_NO_MEMORY; }
+    int st = ORC_OK;
+    uint8_t qcol[BLOCK];
+    for (int64_t b = 0; b < nb && st == ORC_OK; ++b) {
+        for (int64_t n = 0; n < N; ++n) {
+            st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[b * N + n], &z[b * N + n],
+                                qcol);
+            if (st != ORC_OK) break;
+            for (int r = 0; r < BLOCK; ++r) q[(b * BLOCK + r) * N + n] = qcol[r];
+        }
+    }
+    if (st == ORC_OK) {
+        orc_pack_u4(q, K * N, Wq);
+        orc_pack_u4(z, nb * N, zeros);
+    }
+    free(q);
+    free(z);
+    return st;
+}
+
+int orc_w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N,
+                  uint8_t *q, uint8_t *z)
+{
+    if (bad_w4_shape(K, N)) return ORC_BAD_SHAPE;
+    orc_unpack_u4(Wq, K * N, q);
+    orc_unpack_u4(zeros, (K / BLOCK) * N, z);
+    return ORC_OK;
+}
+
+int orc_w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                      int64_t K, int64_t N, float *W_hat)
+{
+    if (bad_w4_shape(K, N)) return ORC_BAD_SHAPE;
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    uint8_t *z = (uint8_t *)malloc((size_t)((K / BLOCK) * N) + 1);
+    if (!q || !z) { free(q); free(z); return ORC_NO_MEMORY; }
+    orc_w4_unpack(Wq, zeros, K, N, q, z);
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t blk = (k / BLOCK) * N + n;
+            int diff = (int)q[k * N + n] - (int)z[blk];
+            /* the fp64 product of a small integer and a float is exact; the
+             * cast is the single fp32 rounding of the dequantized value */
+            W_hat[k * N + n] = (float)((double)diff * (double)scales[blk]);
+        }
+    }
+    free(q);
+    free(z);
+    return ORC_OK;
+}
+
+int orc_matmul_f64(const float *x, int64_t M, int64_t K, const float *W, int64_t N,
+                   const float *bias, float *y, double *bound)
+{
+    if (M < 0 || K < 0 || N < 0) return ORC_BAD_SHAPE;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = (double)x[m * K + k] * (double)W[k * N + n];
+                acc += p;
+                mag += fabs(p);
+            }
+            if (bias) {
+                acc += (double)bias[n];
+                mag += fabs((double)bias[n]);
+            }
+            y[m * N + n] = (float)acc;
+            if (bound) bound[m * N + n] = 1e-5 * mag + 1e-6;
+        }
+    }
+    return ORC_OK;
+}
+
+int orc_w4_matmul(const float *x, int64_t M, int64_t K,
+                  const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t N,
+                  const float *bias, float *y, double *bound)
+{
+    if (M < 0 || bad_w4_shape(K, N)) return ORC_BAD_SHAPE;
+    float *W_hat = (float *)malloc((size_t)(K * N) * sizeof(float) + 1);
+    if (!W_hat) return ORC_NO_MEMORY;
+    int st = orc_w4_dequantize(Wq, scales, zeros, K, N, W_hat);
+    if (st == ORC_OK) st = orc_matmul_f64(x, M, K, W_hat, N, bias, y, bound);
+    free(W_hat);
+    return st;
+}
+
+int orc_i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq,
+                         int8_t *Q, float *hs)
+{
+    if (K < 0 || N < 0 || ldq < N) return ORC_BAD_SHAPE;
+    for (int64_t n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = E[k * N + n];
+            if (!isfinite(v)) return ORC_NONFINITE;
+            if (fabsf(v) > amax) amax = fabsf(v);
+        }
+        float s = amax / 127.0f;
+        hs[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int qv = 0;
+            if (s != 0.0f) qv = clamp_int(rintf(E[k * N + n] / s), -127, 127);
+            Q[k * ldq + n] = (int8_t)qv;
+        }
+    }
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = N; n < ldq; ++n) Q[k * ldq + n] = 0;
+    return ORC_OK;
+}
+
+int orc_i8_dequantize_head(const int8_t *Q, int64_t ldq, const float *hs,
+                           int64_t K, int64_t N, float *E_hat)
+{
+    if (K < 0 || N < 0 || ldq < N) return ORC_BAD_SHAPE;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            E_hat[k * N + n] = (float)((double)Q[k * ldq + n] * (double)hs[n]);
+    return ORC_OK;
+}
+
+int orc_i8_head_logits(const float *x, int64_t K, const int8_t *Q, int64_t ldq,
+                       const float *hs, int64_t N, float *logits, double *bound)
+{
+    if (K < 0 || N < 0 || ldq < N) return ORC_BAD_SHAPE;
+    float *E_hat = (float *)malloc((size_t)(K * N) * sizeof(float) + 1);
+    if (!E_hat) return ORC_NO_MEMORY;
+    orc_i8_dequantize_head(Q, ldq, hs, K, N, E_hat);
+    int st = orc_matmul_f64(x, 1, K, E_hat, N, NULL, logits, bound);
+    free(E_hat);
+    return st;
+}
+
+int orc_i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
+                 const float *hs, int64_t K, int64_t N, float *out)
+{
+    if (T < 0 || K < 0 || N < 0 || ldq < N) return ORC_BAD_SHAPE;
+    for (int64_t t = 0; t < T; ++t)
+        if (tokens[t] < 0 || tokens[t] >= N) return ORC_BAD_SHAPE;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t tok = tokens[t];
+        for (int64_t k = 0; k < K; ++k)
+            out[t * K + k] = (float)((double)Q[k * ldq + tok] * (double)hs[tok]);
+    }
+    return ORC_OK;
+}

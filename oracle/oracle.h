@@ -1,0 +1,110 @@
+/*
+ * CPU oracle for the 4-bit block-dequant weight matmul and the int8 tied LM head.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This code exists to check the HIP library; it is
+ * never part of the product path.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header, table or
+ * helper with the HIP library and includes nothing from it.
+ *
+ * Source of the method: the page "ONNX export, quantization and the browser
+ * runtime", section "Quantization (train/quantize.py)", steps 1-4:
+ *   - every body weight is a plain [K, N] constant followed by a bias Add;
+ *   - it is stored 4-bit, asymmetric, in blocks of 32 along K, with one fp32
+ *     scale and one uint4 zero point per block, as packed UINT4 tensors, and a
+ *     blocked DequantizeLinear restores fp32;
+ *   - the tied embedding / LM head is stored once as int8 with one scale per
+ *     token, in the head's [768, 50257] layout;
+ *   - the head is applied to the last position only.
+ * The same page, paragraph after the steps: the runtime folds the dequantize
+ * nodes and runs plain fp32 kernels, so the matmul computes x . W_hat with
+ * W_hat the fp32 output of the dequantization.
+ *
+ * Readings where the page is silent: pairs of nibbles run along N (flat
+ * row-major packing of the [K, N] code tensor, element 2i in the low nibble);
+ * the block range includes 0; rounding is IEEE round-half-to-even; scale,
+ * zero and code arithmetic is fp32 with no contraction; accumulation is fp64
+ * with one final rounding.
+ *
+ * Every function is plain loops, no blocking, no fusion; status 0 = OK.
+ */
+#ifndef W4_ORACLE_H
+#define W4_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ORC_OK = 0,
+    ORC_BAD_SHAPE = 1, /* K % 32 != 0, N odd, negative size, ldq < N      */
+    ORC_NONFINITE = 2, /* a non-finite weight, or a scale that overflowed */
+    ORC_NO_MEMORY = 3  /* malloc failed                                    */
+};
+
+/* Pack count (even) 4-bit values, one per byte in v[0..count), two per byte:
+ * out[i] = v[2i] | v[2i+1] << 4 (the low nibble holds the even element).     */
+void orc_pack_u4(const uint8_t *v, int64_t count, uint8_t *out);
+
+/* Inverse of orc_pack_u4: v[2i] = in[i] & 15, v[2i+1] = in[i] >> 4.          */
+void orc_unpack_u4(const uint8_t *in, int64_t count, uint8_t *v);
+
+/* Block quantizer (page section "Quantization", step 2).
+ * W      fp32 [K, N] row-major, K % 32 == 0, N even.
+ * Wq     uint8 [K, N/2]: packed codes q[k, n], pairs along n.
+ * scales fp32 [K/32, N]: scale of block b = rows 32b..32b+31 of column n.
+ * zeros  uint8 [K/32, N/2]: packed zero points z[b, n], pairs along n.
+ * Per block: lo = min(0, min w), hi = max(0, max w); s = (hi - lo) / 15;
+ * s == 0 gives s = z = q = 0; z = clamp(rint(-lo / s), 0, 15);
+ * q = clamp(rint(w / s) + z, 0, 15).                                        */
+int orc_w4_quantize_pack(const float *W, int64_t K, int64_t N,
+                         uint8_t *Wq, float *scales, uint8_t *zeros);
+
+/* Unpack codes and zero points: q uint8 [K, N], z uint8 [K/32, N].         */
+int orc_w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N,
+                  uint8_t *q, uint8_t *z);
+
+/* Blocked dequantization: W_hat[k, n] = fl32((q[k, n] - z[k/32, n]) * s[k/32, n]). */
+int orc_w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                      int64_t K, int64_t N, float *W_hat);
+
+/* Plain matmul with fp64 accumulation:
+ * y[m, n] = fl32(sum_k x[m, k] * W[k, n] + bias[n])  (bias may be NULL),
+ * bound[m, n] = 1e-5 * (sum_k |x[m, k] * W[k, n]| + |bias[n]|) + 1e-6,
+ * the per-output tolerance a fp32 implementation is held to (bound may be NULL). */
+int orc_matmul_f64(const float *x, int64_t M, int64_t K, const float *W, int64_t N,
+                   const float *bias, float *y, double *bound);
+
+/* The 4-bit matmul as the page's runtime executes it: dequantize, then matmul. */
+int orc_w4_matmul(const float *x, int64_t M, int64_t K,
+                  const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t N,
+                  const float *bias, float *y, double *bound);
+
+/* int8 head quantizer (step 3): per column (token) n of E fp32 [K, N]:
+ * hs[n] = max_k |E[k, n]| / 127, Q[k, n] = clamp(rint(E[k, n] / hs[n]), -127, 127),
+ * a zero column gives hs = 0 and Q = 0.  Q int8 [K, ldq]; the padding columns
+ * N..ldq-1 are written as 0.                                                */
+int orc_i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq,
+                         int8_t *Q, float *hs);
+
+/* Per-token dequantization of the table: E_hat[k, n] = fl32(Q[k, n] * hs[n]), [K, N]. */
+int orc_i8_dequantize_head(const int8_t *Q, int64_t ldq, const float *hs,
+                           int64_t K, int64_t N, float *E_hat);
+
+/* Last-token logits (step 4): logits[n] = fl32(sum_k x[k] * E_hat[k, n]) for the
+ * one row x [K], accumulated in fp64, with the per-output bound as above.  */
+int orc_i8_head_logits(const float *x, int64_t K, const int8_t *Q, int64_t ldq,
+                       const float *hs, int64_t N, float *logits, double *bound);
+
+/* Token lookup from the same table (step 3: Gather along axis 1, then
+ * Transpose): out[t, k] = E_hat[k, tokens[t]], out fp32 [T, K].
+ * A token outside [0, N) is ORC_BAD_SHAPE.                                  */
+int orc_i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
+                 const float *hs, int64_t K, int64_t N, float *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_ORACLE_H */

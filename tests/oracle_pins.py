@@ -1,0 +1,506 @@
+"""Pins for the CPU oracle: checks against what the method and mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+on a violation.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutations.py`` runs them on copies of the oracle with planted
+mistakes and requires every mutant to fail at least one pin.
+
+None of these recomputes the oracle's formula and compares: each check is a
+different route to the same fact.
+  * packing: the low-nibble-first convention's worked examples and an
+    exhaustive round trip over all 256 bytes (the page's "raw packed UINT4",
+    low nibble first, pairs along N);
+  * quantizer: exact reproduction of weights that lie on a power-of-two grid;
+    the round-trip bound |w - w_hat| <= s/2 (plus fp32 rounding slack) for
+    every weight; brute-force nearest code in exact rational arithmetic;
+    degenerate blocks in closed form;
+  * dequantization: every (q, z) pair against the exactly rounded rational
+    product;
+  * matmul: exact rational sums on tiny shapes, one-hot rows, constant-0.5
+    weights ("halved row sums"), zero activations;
+  * head: one-hot rows, sign symmetry, full use of [-127, 127], the
+    round-trip bound, exact rational logits;
+  * embedding lookup: rows of the dequantized table;
+  * byte budget: the GPT-2 small q4 file size the page prints.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle as oracle_mod
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+BLOCK = 32
+
+
+# --------------------------------------------------------------------------
+# exact-arithmetic helpers
+# --------------------------------------------------------------------------
+def F(v) -> Fraction:
+    """Exact rational value of a float32/float64 scalar."""
+    return Fraction(float(v))
+
+
+def f32_round(fr: Fraction) -> np.float32:
+    """The fp32 value nearest to the rational ``fr`` (ties to even significand)."""
+    if fr == 0:
+        return np.float32(0.0)
+    c = np.float32(float(fr))
+    cands = {float(c)}
+    for d in (np.inf, -np.inf):
+        n = np.nextafter(c, np.float32(d))
+        if np.isfinite(n):
+            cands.add(float(n))
+    best = None
+    for v in cands:
+        err = abs(Fraction(v) - fr)
+        key = (err, int(np.float32(v).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, v)
+    return np.float32(best[1])
+
+
+def ulp32(v) -> float:
+    return float(np.spacing(np.float32(abs(v))))
+
+
+# --------------------------------------------------------------------------
+# packing
+# --------------------------------------------------------------------------
+def pin_pack_worked_examples(orc):
+    # low nibble first: element 0 sits in bits 0..3, element 1 in bits 4..7
+    assert orc.pack_u4([3, 10]).tolist() == [0xA3]
+    assert orc.pack_u4([1, 2, 3, 4]).tolist() == [0x21, 0x43]
+    assert orc.pack_u4([15, 0, 0, 15]).tolist() == [0x0F, 0xF0]
+    assert orc.unpack_u4([0xA3]).tolist() == [3, 10]
+    assert orc.unpack_u4([0x21, 0x43]).tolist() == [1, 2, 3, 4]
+
+
+def pin_pack_exhaustive(orc):
+    every_byte = np.arange(256, dtype=np.uint8)
+    v = orc.unpack_u4(every_byte)
+    assert v.max() <= 15
+    assert np.array_equal(orc.pack_u4(v), every_byte)
+    # all 16 x 16 (even, odd) pairs, in every position of a row
+    pairs = np.array([(a, b) for a in range(16) for b in range(16)], np.uint8).reshape(-1)
+    packed = orc.pack_u4(pairs)
+    assert np.array_equal(orc.unpack_u4(packed), pairs)
+    # a byte's value identifies the pair: 16 * odd + even
+    assert np.array_equal(packed, (pairs[1::2].astype(int) * 16 + pairs[0::2]).astype(np.uint8))
+
+
+# --------------------------------------------------------------------------
+# quantizer
+# --------------------------------------------------------------------------
+def _on_grid(K, N, seed):
+    """Weights w = (q - z) * 2**e per block, with code 0 and 15 both present."""
+    g = np.random.default_rng(seed)
+    nb = K // BLOCK
+    e = g.integers(-10, -3, size=(nb, N))
+    z = g.integers(0, 16, size=(nb, N)).astype(np.uint8)
+    q = g.integers(0, 16, size=(K, N)).astype(np.uint8)
+    for b in range(nb):
+        for n in range(N):
+            r0, r1 = g.choice(BLOCK, size=2, replace=False)
+            q[b * BLOCK + r0, n] = 0
+            q[b * BLOCK + r1, n] = 15
+    s = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    srow = np.repeat(s, BLOCK, axis=0)
+    zrow = np.repeat(z, BLOCK, axis=0)
+    W = ((q.astype(np.float32) - zrow.astype(np.float32)) * srow).astype(np.float32)
+    return W, q, z, s
+
+
+def pin_quantize_on_grid(orc):
+    for K, N, seed in ((32, 2, 1), (64, 6, 2), (96, 10, 3), (256, 34, 4)):
+        W, q, z, s = _on_grid(K, N, seed)
+        Wq, sc, zp = orc.quantize_pack(W)
+        assert Wq.shape == (K, N // 2) and sc.shape == (K // BLOCK, N)
+        assert zp.shape == (K // BLOCK, N // 2)
+        assert np.array_equal(sc, s), "scale of an on-grid block must be its exact 2**e"
+        q2, z2 = orc.unpack(Wq, zp, K, N)
+        assert np.array_equal(z2, z), "zero points of on-grid blocks must be exact"
+        assert np.array_equal(q2, q), "codes of on-grid weights must be exact"
+        # the bytes themselves follow the packing convention, row-major over [K, N]
+        assert np.array_equal(Wq.reshape(-1), orc.pack_u4(q.reshape(-1)))
+        assert np.array_equal(zp.reshape(-1), orc.pack_u4(z.reshape(-1)))
+        assert np.array_equal(orc.dequantize(Wq, sc, zp, K, N), W), "on-grid w_hat == w"
+
+
+def pin_quantize_ties_half_even(orc):
+    """Weights exactly halfway between two codes take the even multiple of s.
+
+    The page does not state a tie rule.  The format is ONNX's blocked
+    QuantizeLinear/DequantizeLinear pair, whose rounding is to nearest with
+    ties to even (also IEEE's default mode and numpy's ``round``); this pin
+    fixes that reading.
+    """
+    g = np.random.default_rng(13)
+    K, N = 64, 8
+    nb = K // BLOCK
+    W = np.zeros((K, N), np.float32)
+    want = np.zeros((K, N), np.uint8)
+    for b in range(nb):
+        for n in range(N):
+            e = int(g.integers(-9, -4))
+            s = np.float32(2.0 ** e)
+            z = int(g.integers(1, 15))
+            rows = g.permutation(BLOCK)
+            for i, r in enumerate(rows):
+                k = b * BLOCK + r
+                if i == 0:
+                    c = 0
+                elif i == 1:
+                    c = 15
+                else:
+                    c = int(g.integers(0, 15))
+                    t = (c - z) + 0.5                 # w / s, exactly halfway
+                    W[k, n] = np.float32(t) * s
+                    lo_int = c - z                    # the two neighbours of t
+                    even = lo_int if lo_int % 2 == 0 else lo_int + 1
+                    want[k, n] = even + z
+                    continue
+                W[k, n] = np.float32(c - z) * s
+                want[k, n] = c
+    Wq, sc, zp = orc.quantize_pack(W)
+    q, _ = orc.unpack(Wq, zp, K, N)
+    assert np.array_equal(q, want), "ties must round to the even multiple"
+
+
+def _test_weights():
+    """A spread of block contents: normal, heavy-tailed, same-sign, tiny, huge."""
+    out = []
+    g = np.random.default_rng(7)
+    out.append(synth.weights(128, 64, cfg=100))
+    t = g.standard_t(2, size=(64, 32)).astype(np.float32) * np.float32(0.02)
+    out.append(t)
+    out.append(np.abs(g.standard_normal((64, 16))).astype(np.float32) + np.float32(0.3))
+    out.append(-np.abs(g.standard_normal((64, 16))).astype(np.float32) - np.float32(0.3))
+    out.append((g.standard_normal((32, 8)) * 1e-30).astype(np.float32))
+    out.append((g.standard_normal((32, 8)) * 1e30).astype(np.float32))
+    sub = (g.standard_normal((32, 8)) * 1e-41).astype(np.float32)  # subnormal fp32
+    out.append(sub)
+    return out
+
+
+def pin_round_trip_bound(orc):
+    for W in _test_weights():
+        K, N = W.shape
+        Wq, s, zp = orc.quantize_pack(W)
+        What = orc.dequantize(Wq, s, zp, K, N)
+        q, z = orc.unpack(Wq, zp, K, N)
+        assert q.max() <= 15 and z.max() <= 15
+        srow = np.repeat(s, BLOCK, axis=0).astype(np.float64)
+        err = np.abs(W.astype(np.float64) - What.astype(np.float64))
+        # s/2 from rounding to the nearest code, plus the fp32 roundings of
+        # w / s and of (q - z) * s (each at most 15 * 2**-24 * s); in the
+        # subnormal range the absolute spacing 2**-149 replaces the relative one
+        lim = srow * (0.5 + 2.0 ** -19) + 2.0 ** -148
+        assert np.all(err <= lim), f"round-trip error {np.max(err / np.maximum(srow, 1e-300))} s"
+
+
+def pin_nearest_code_bruteforce(orc):
+    g = np.random.default_rng(11)
+    cases = [synth.weights(32, 4, cfg=101),
+             (g.standard_normal((32, 4)) * 0.3 + 0.1).astype(np.float32),
+             np.abs(g.standard_normal((32, 2))).astype(np.float32)]
+    for W in cases:
+        K, N = W.shape
+        Wq, s, zp = orc.quantize_pack(W)
+        q, z = orc.unpack(Wq, zp, K, N)
+        for n in range(N):
+            sn = F(s[0, n])
+            assert sn > 0
+            zn = int(z[0, n])
+            for k in range(K):
+                w = F(W[k, n])
+                t = w / sn
+                frac = t - (t.numerator // t.denominator)
+                if abs(frac - Fraction(1, 2)) < Fraction(1, 2 ** 20):
+                    continue  # tie zone: decided by the rounding convention
+                errs = [abs(w - (qq - zn) * sn) for qq in range(16)]
+                best = min(errs)
+                assert errs[int(q[k, n])] == best, (k, n, int(q[k, n]), errs.index(best))
+            # codes 0 and 15 sit within s/2 of the ends of the 0-inclusive range
+            lo = min(min(F(v) for v in W[:, n]), Fraction(0))
+            hi = max(max(F(v) for v in W[:, n]), Fraction(0))
+            slack = sn * Fraction(1, 2 ** 18)
+            assert abs(lo - (0 - zn) * sn) <= sn / 2 + slack
+            assert abs(hi - (15 - zn) * sn) <= sn / 2 + slack
+            # the block's minimum maps to code 0 when it is negative
+            if lo < 0:
+                kmin = int(np.argmin(W[:, n]))
+                assert int(q[kmin, n]) == 0
+
+
+def pin_degenerate_blocks(orc):
+    K, N = 32, 8
+    W = np.zeros((K, N), np.float32)
+    W[:, 1] = 0.5                     # constant positive block
+    W[:, 2] = -0.25                   # constant negative block
+    W[7, 3] = 3.0                     # one nonzero weight
+    W[:, 4] = -0.0                    # negative zeros
+    W[:, 5] = np.float32(1e-45)       # smallest subnormal
+    Wq, s, zp = orc.quantize_pack(W)
+    q, z = orc.unpack(Wq, zp, K, N)
+    What = orc.dequantize(Wq, s, zp, K, N)
+    # all-zero block: everything 0
+    for n in (0, 4, 6, 7):
+        assert s[0, n] == 0 and z[0, n] == 0 and not q[:, n].any() and not What[:, n].any()
+    # constant c > 0: range [0, c], zero point 0, every code 15
+    assert z[0, 1] == 0 and np.all(q[:, 1] == 15)
+    assert s[0, 1] == f32_round(Fraction(1, 2) / 15)
+    assert np.all(What[:, 1] == np.float32(0.5)), "15 * fl32(0.5/15) rounds back to 0.5"
+    # constant c < 0: range [c, 0], zero point 15, every code 0
+    assert z[0, 2] == 15 and np.all(q[:, 2] == 0)
+    assert np.all(What[:, 2] == f32_round(-15 * F(s[0, 2])))
+    # one nonzero weight: it takes code 15, the zeros code z = 0
+    assert z[0, 3] == 0 and q[7, 3] == 15 and np.count_nonzero(q[:, 3]) == 1
+    assert What[7, 3] == np.float32(3.0)
+    # a range of one subnormal ulp: s = fl32(2**-149 / 15) rounds to 0
+    assert s[0, 5] == 0 and not q[:, 5].any()
+
+
+def pin_shape_and_value_errors(orc):
+    for shape in ((31, 4), (32, 3), (33, 2)):
+        try:
+            orc.quantize_pack(np.zeros(shape, np.float32))
+        except oracle_mod.OracleError as e:
+            assert e.status == oracle_mod.BAD_SHAPE
+        else:
+            raise AssertionError(f"shape {shape} accepted")
+    for bad in (np.nan, np.inf, -np.inf):
+        W = np.zeros((32, 2), np.float32)
+        W[5, 1] = bad
+        try:
+            orc.quantize_pack(W)
+        except oracle_mod.OracleError as e:
+            assert e.status == oracle_mod.NONFINITE
+        else:
+            raise AssertionError(f"{bad} accepted")
+    W = np.zeros((32, 2), np.float32)
+    W[0, 0], W[1, 0] = 3e38, -3e38      # hi - lo overflows fp32
+    try:
+        orc.quantize_pack(W)
+    except oracle_mod.OracleError as e:
+        assert e.status == oracle_mod.NONFINITE
+    else:
+        raise AssertionError("overflowing range accepted")
+
+
+# --------------------------------------------------------------------------
+# dequantization
+# --------------------------------------------------------------------------
+def pin_dequant_all_pairs(orc):
+    # 16 blocks x 16 columns: block b, column n has zero point (b + n) % 16 and
+    # its 32 rows hold codes 0..15 twice, so all 256 (q, z) pairs occur
+    nb, N = 16, 16
+    K = nb * BLOCK
+    z = np.array([[(b + n) % 16 for n in range(N)] for b in range(nb)], np.uint8)
+    q = np.array([[(k % 16) for _ in range(N)] for k in range(K)], np.uint8)
+    g = np.random.default_rng(5)
+    s = np.abs(g.standard_normal((nb, N))).astype(np.float32) * np.float32(0.01)
+    s[0, :4] = [np.float32(1e-40), np.float32(3e-39), np.float32(1e30), np.float32(2.0 ** 100)]
+    Wq = orc.pack_u4(q.reshape(-1)).reshape(K, N // 2)
+    zp = orc.pack_u4(z.reshape(-1)).reshape(nb, N // 2)
+    What = orc.dequantize(Wq, s, zp, K, N)
+    seen = set()
+    for k in range(K):
+        for n in range(N):
+            b = k // BLOCK
+            qq, zz = int(q[k, n]), int(z[b, n])
+            seen.add((qq, zz))
+            want = f32_round((qq - zz) * F(s[b, n]))
+            got = What[k, n]
+            assert got == want or (want == 0 and got == 0), (k, n, got, want)
+    assert len(seen) == 256
+
+
+# --------------------------------------------------------------------------
+# matmul
+# --------------------------------------------------------------------------
+def _exact_check(y, bound, x, What, bias):
+    M, K = x.shape
+    N = What.shape[1]
+    for m in range(M):
+        for n in range(N):
+            terms = [F(x[m, k]) * F(What[k, n]) for k in range(K)]
+            exact = sum(terms, Fraction(0))
+            mag = sum((abs(t) for t in terms), Fraction(0))
+            if bias is not None:
+                exact += F(bias[n])
+                mag += abs(F(bias[n]))
+            # fp64 accumulation error plus one fp32 rounding
+            tol = Fraction(ulp32(float(exact))) / 2 + (K + 2) * Fraction(1, 2 ** 53) * mag
+            assert abs(F(y[m, n]) - exact) <= tol, (m, n, float(y[m, n]), float(exact))
+            want_bound = float(Fraction(1, 10 ** 5) * mag + Fraction(1, 10 ** 6))
+            assert abs(bound[m, n] - want_bound) <= 1e-12 * want_bound, (bound[m, n], want_bound)
+
+
+def pin_matmul_exact_small(orc):
+    for M, K, N, outl in ((1, 32, 2, False), (3, 64, 6, True), (2, 96, 4, False)):
+        W = synth.weights(K, N, cfg=102, slot=M)
+        x = synth.activations(M, K, cfg=102, slot=M, outliers=outl)
+        b = synth.bias(N, cfg=102, slot=M)
+        Wq, s, zp = orc.quantize_pack(W)
+        What = orc.dequantize(Wq, s, zp, K, N)
+        for bias in (None, b):
+            y, bound = orc.w4_matmul(x, Wq, s, zp, bias)
+            _exact_check(y, bound, x, What, bias)
+            y2, bound2 = orc.matmul_f64(x, What, bias)
+            assert np.array_equal(y, y2) and np.array_equal(bound, bound2)
+
+
+def pin_matmul_special_cases(orc):
+    K, N = 64, 10
+    W = synth.weights(K, N, cfg=103)
+    b = synth.bias(N, cfg=103)
+    Wq, s, zp = orc.quantize_pack(W)
+    What = orc.dequantize(Wq, s, zp, K, N)
+    # one-hot rows pick out rows of W_hat; with a bias, one fp32 addition
+    x = np.eye(K, dtype=np.float32)
+    y, _ = orc.w4_matmul(x, Wq, s, zp)
+    assert np.array_equal(y, What)
+    y, _ = orc.w4_matmul(x, Wq, s, zp, b)
+    assert np.array_equal(y, What + b[None, :])
+    # zero activations give the bias exactly
+    y, _ = orc.w4_matmul(np.zeros((2, K), np.float32), Wq, s, zp, b)
+    assert np.array_equal(y, np.stack([b, b]))
+    # constant 0.5 weights quantize losslessly; y = half the row sums
+    Wc = np.full((K, N), 0.5, np.float32)
+    Wq2, s2, zp2 = orc.quantize_pack(Wc)
+    xi = np.random.default_rng(9).integers(-20, 21, size=(3, K)).astype(np.float32)
+    y, _ = orc.w4_matmul(xi, Wq2, s2, zp2)
+    half = (xi.sum(axis=1, dtype=np.float64) * 0.5).astype(np.float32)
+    assert np.array_equal(y, np.repeat(half[:, None], N, axis=1))
+    # empty reductions and empty outputs
+    y, bound = orc.w4_matmul(np.zeros((2, 0), np.float32), np.zeros((0, N // 2), np.uint8),
+                             np.zeros((0, N), np.float32), np.zeros((0, N // 2), np.uint8), b)
+    assert np.array_equal(y, np.stack([b, b]))
+    y, _ = orc.w4_matmul(np.zeros((0, K), np.float32), Wq, s, zp, b)
+    assert y.shape == (0, N)
+
+
+# --------------------------------------------------------------------------
+# int8 head and embedding
+# --------------------------------------------------------------------------
+def pin_head_quantizer(orc):
+    K, N = 96, 40
+    E = synth.head_table(K, N, cfg=104)
+    E[:, 3] = 0.0                                  # zero column
+    E[:, 4] = -E[:, 5]                             # mirrored column
+    Q, hs = orc.i8_quantize_head(E, ldq=48)
+    assert Q.shape == (K, 48) and not Q[:, N:].any(), "padding columns are 0"
+    assert Q[:, :N].min() >= -127
+    assert hs[3] == 0 and not Q[:, 3].any()
+    assert hs[4] == hs[5] and np.array_equal(Q[:, 4], -Q[:, 5]), "Q(-E) = -Q(E)"
+    Qn, hsn = orc.i8_quantize_head(-E)
+    assert np.array_equal(hsn, hs) and np.array_equal(Qn, -Q[:, :N])
+    for n in range(N):
+        if n == 3:
+            continue
+        assert np.max(np.abs(Q[:, n].astype(int))) == 127, "the largest entry uses 127"
+        # the column maximum lies on the grid: max|E| = 127 * hs up to one rounding
+        amax = F(np.max(np.abs(E[:, n])))
+        assert abs(127 * F(hs[n]) - amax) <= 127 * Fraction(ulp32(hs[n])) / 2
+        err = np.abs(E[:, n].astype(np.float64) - Q[:, n].astype(np.float64) * float(hs[n]))
+        assert np.all(err <= float(hs[n]) * (0.5 + 2.0 ** -17))
+    # nearest-code check in exact arithmetic on one column
+    n = 7
+    for k in range(K):
+        e = F(E[k, n])
+        t = e / F(hs[n])
+        if abs(abs(t - (t.numerator // t.denominator)) - Fraction(1, 2)) < Fraction(1, 2 ** 20):
+            continue
+        errs = {c: abs(e - c * F(hs[n])) for c in range(-127, 128)}
+        assert errs[int(Q[k, n])] == min(errs.values())
+    # zero point is 0: the dequantized table is odd in Q
+    Eh = orc.i8_dequantize_head(Q, hs)
+    assert np.all(Eh[:, 3] == 0)
+
+
+def pin_head_logits(orc):
+    K, N = 64, 12
+    E = synth.head_table(K, N, cfg=105)
+    Q, hs = orc.i8_quantize_head(E, ldq=16)
+    Eh = orc.i8_dequantize_head(Q, hs)
+    for n in range(N):
+        for k in range(K):
+            assert Eh[k, n] == f32_round(int(Q[k, n]) * F(hs[n]))
+    # one-hot rows
+    for k in (0, 17, K - 1):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        logits, _ = orc.i8_head_logits(x, Q, hs)
+        assert np.array_equal(logits, Eh[k])
+    # exact rational logits
+    x = synth.activations(1, K, cfg=105, outliers=True)[0]
+    logits, bound = orc.i8_head_logits(x, Q, hs)
+    _exact_check(logits[None, :], bound[None, :], x[None, :], Eh, None)
+
+
+def pin_embedding(orc):
+    K, N = 48, 30
+    E = synth.head_table(K, N, cfg=106)
+    Q, hs = orc.i8_quantize_head(E, ldq=32)
+    Eh = orc.i8_dequantize_head(Q, hs)
+    toks = np.array([0, 5, 29, 5, 17], np.int64)
+    out = orc.i8_embed(toks, Q, hs)
+    assert out.shape == (5, K)
+    for t, tok in enumerate(toks):
+        assert np.array_equal(out[t], Eh[:, tok])
+    # the lookup is the head's transpose: the logits of one-hot e_k, read at
+    # the looked-up tokens, equal column k of the looked-up rows
+    logits, _ = orc.i8_head_logits(np.eye(K, dtype=np.float32)[3], Q, hs)
+    assert np.array_equal(logits[toks], out[:, 3])
+    for bad in (-1, N):
+        try:
+            orc.i8_embed(np.array([bad], np.int64), Q, hs)
+        except oracle_mod.OracleError as e:
+            assert e.status == oracle_mod.BAD_SHAPE
+        else:
+            raise AssertionError("token out of range accepted")
+
+
+# --------------------------------------------------------------------------
+# byte budget against the page's printed file size
+# --------------------------------------------------------------------------
+def pin_file_size(orc):
+    with open(os.path.join(GOLDEN, "gpt2_small_q4_file_size.json")) as f:
+        g = json.load(f)
+    body = 0
+    for K, N in synth.GPT2_SHAPES:
+        Wq, s, zp = orc.quantize_pack(synth.weights(K, N, cfg=107))
+        body += synth.GPT2_LAYERS * (Wq.nbytes + s.nbytes + zp.nbytes)
+    Q, hs = orc.i8_quantize_head(np.zeros((synth.GPT2_HIDDEN, synth.GPT2_VOCAB), np.float32))
+    rest = g["fp32_position_table_bytes"] + g["fp32_bias_and_norm_bytes"]
+    total = body + Q.nbytes + hs.nbytes + rest
+    assert abs(total / 1e6 - g["q4_shipped_MB"]) < 0.5, total
+    # the fp32 model of the same architecture
+    params = sum(synth.GPT2_LAYERS * K * N for K, N in synth.GPT2_SHAPES)
+    fp32 = 4 * (params + synth.GPT2_HIDDEN * synth.GPT2_VOCAB) + rest
+    assert abs(fp32 / 1e6 - g["fp32_MB"]) < 0.5, fp32
+
+
+ALL_PINS = [
+    pin_pack_worked_examples,
+    pin_pack_exhaustive,
+    pin_quantize_on_grid,
+    pin_quantize_ties_half_even,
+    pin_round_trip_bound,
+    pin_nearest_code_bruteforce,
+    pin_degenerate_blocks,
+    pin_shape_and_value_errors,
+    pin_dequant_all_pairs,
+    pin_matmul_exact_small,
+    pin_matmul_special_cases,
+    pin_head_quantizer,
+    pin_head_logits,
+    pin_embedding,
+    pin_file_size,
+]

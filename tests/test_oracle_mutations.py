@@ -1,0 +1,99 @@
+"""Plausible mistakes planted in copies of the CPU oracle must each fail a pin.
+
+Each mutant is the oracle's C source with one textual change, compiled into a
+temporary directory with the oracle's own flags.  The mistakes cover every
+step: nibble order, the block range, rounding, the scale divisor, the code
+formula, the zero point's sign, the dequantization formula and its block
+index, the matmul's bias, indexing and accumulation precision, the bound, and
+the head's scale and rounding.  A mutant that passes every pin would mean the
+pins cannot tell that mistake from the correct oracle.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "pack_high_nibble_first": (
+        "out[i] = (uint8_t)((v[2 * i] & 15) | ((v[2 * i + 1] & 15) << 4));",
+        "out[i] = (uint8_t)((v[2 * i + 1] & 15) | ((v[2 * i] & 15) << 4));"),
+    "unpack_high_nibble_first": (
+        "v[2 * i] = (uint8_t)(in[i] & 15);\n        v[2 * i + 1] = (uint8_t)(in[i] >> 4);",
+        "v[2 * i + 1] = (uint8_t)(in[i] & 15);\n        v[2 * i] = (uint8_t)(in[i] >> 4);"),
+    "range_without_zero": (
+        "float lo = 0.0f, hi = 0.0f;",
+        "float lo = w[0], hi = w[0];"),
+    "round_half_away": (
+        "float t = rintf(w[r * stride] / s);",
+        "float t = roundf(w[r * stride] / s);"),
+    "round_down": (
+        "float t = rintf(w[r * stride] / s);",
+        "float t = floorf(w[r * stride] / s);"),
+    "scale_over_16": (
+        "float s = range / 15.0f;",
+        "float s = range / 16.0f;"),
+    "code_from_range_start": (
+        "q_out[r] = (uint8_t)clamp_int(t + (float)z, 0, 15);",
+        "q_out[r] = (uint8_t)clamp_int(rintf((w[r * stride] - lo) / s), 0, 15);"),
+    "zero_point_sign": (
+        "float zr = rintf(-lo / s);",
+        "float zr = rintf(lo / s);"),
+    "dequant_drops_zero_point": (
+        "int diff = (int)q[k * N + n] - (int)z[blk];",
+        "int diff = (int)q[k * N + n];"),
+    "dequant_scales_transposed": (
+        "int64_t blk = (k / BLOCK) * N + n;",
+        "int64_t blk = n * (K / BLOCK) + (k / BLOCK);"),
+    "quantize_scale_stored_transposed": (
+        "st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[b * N + n], &z[b * N + n],",
+        "st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[n * nb + b], &z[b * N + n],"),
+    "matmul_drops_bias": (
+        "acc += (double)bias[n];",
+        "acc += 0.0;"),
+    "matmul_weight_transposed": (
+        "double p = (double)x[m * K + k] * (double)W[k * N + n];",
+        "double p = (double)x[m * K + k] * (double)W[n * K + k];"),
+    "matmul_fp32_accumulation": (
+        "double acc = 0.0, mag = 0.0;",
+        "float acc = 0.0f; double mag = 0.0;"),
+    "bound_uses_abs_of_sum": (
+        "if (bound) bound[m * N + n] = 1e-5 * mag + 1e-6;",
+        "if (bound) bound[m * N + n] = 1e-5 * fabs(acc) + 1e-6;"),
+    "head_scale_over_128": (
+        "float s = amax / 127.0f;",
+        "float s = amax / 128.0f;"),
+    "head_truncates": (
+        "if (s != 0.0f) qv = clamp_int(rintf(E[k * N + n] / s), -127, 127);",
+        "if (s != 0.0f) qv = clamp_int(truncf(E[k * N + n] / s), -127, 127);"),
+    "embed_wrong_scale": (
+        "out[t * K + k] = (float)((double)Q[k * ldq + tok] * (double)hs[tok]);",
+        "out[t * K + k] = (float)((double)Q[k * ldq + tok] * (double)hs[k]);"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTATIONS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    d = tmp_path / name
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(oracle.__file__), "oracle.h"), d / "oracle.h")
+    (d / "oracle.c").write_text(source.replace(old, new))
+    so = oracle.build(str(d / "oracle.c"), str(d / "liboracle_mutant.so"))
+    orc = oracle.Oracle(oracle.load_library(so))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, oracle.OracleError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
