@@ -1,0 +1,330 @@
+"""Benchmark of the 4-bit block-dequant decode matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary]
+
+The step is one decode body pass of the 3.8B-dense-shaped model at M = 1:
+32 layers x 4 W4 matmuls (3072x9216 QKV, 3072x3072 out, 3072x16384
+gate+up, 8192x3072 down), 2.32 GB of packed weights, i.e. 128 launches of
+the fused dequant-GEMV on one stream, captured once in a HIP graph and
+replayed.  The weights are far larger than the 256 MB Infinity Cache, so
+every pass streams them from HBM.  `value` is the pass's algorithmic bytes
+(packed weights, scales, zero points, x and y, each counted once) divided
+by the measured time per pass.
+
+Also reported on the same JSON line:
+  * roofline: the GEMV kernel's algorithmic bytes per launch over its
+    average launch duration (HIP events around each launch on the launch
+    stream), against the 8 TB/s HBM peak;
+  * cpu_baseline: the CPU oracle (dequantize, then fp64 matmul, one thread)
+    on the first layers of the same body, in the same unit;
+  * parity: GPU outputs of those layers against the oracle's, per output;
+  * secondary: the GPT-2-small-shaped decode pass (48 matmuls with bias),
+    the int8 head [768, 50257], the GPT-2 prefill pass at M = 58 plus the
+    last-row head, and the 3.8B pass at M = 16.
+Inputs are seeded synthetic data of the workloads' shapes and distributions
+(see synth.py); nothing is read from disk.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "W4 decode GEMV achieved HBM GB/s (% of peak) + body-pass tokens/s, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--skip-secondary", action="store_true")
+    p.add_argument("--skip-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU-oracle time budget for the baseline sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding or collectives).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import w4_block_dequant_amd as w4
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------------ setup
+    pool = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
+
+    class Mat:
+        __slots__ = ("layer", "slot", "K", "N", "Wq", "s", "z", "b", "x", "y", "bytes", "flops")
+
+    def build_body(name, cfg, M, with_bias, outliers):
+        shapes = synth.body(name)
+        ahead = 16                  # bounded look-ahead: at most 16 fp32 matrices on the host
+        futs = {}
+        mats = []
+        for i, (l, s, K, N) in enumerate(shapes):
+            for j in range(i, min(i + ahead, len(shapes))):
+                if j not in futs:
+                    lj, sj, Kj, Nj = shapes[j]
+                    futs[j] = pool.submit(synth.weights, Kj, Nj, cfg, lj, sj)
+            W = torch.from_numpy(futs.pop(i).result()).to(dev)
+            m = Mat()
+            m.layer, m.slot, m.K, m.N = l, s, K, N
+            m.Wq, m.s, m.z = w4.w4_quantize_pack(W)
+            del W
+            m.b = torch.from_numpy(synth.bias(N, cfg, l, s)).to(dev) if with_bias else None
+            m.x = torch.from_numpy(synth.activations(M, K, cfg, l, s, outliers=outliers)).to(dev)
+            m.y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            wbytes = K * N // 2 + (K // 32) * N * 4 + (K // 32) * N // 2
+            m.bytes = wbytes + 4 * M * K + 4 * M * N + (4 * N if with_bias else 0)
+            m.flops = 2 * M * K * N
+            mats.append(m)
+        torch.cuda.synchronize()
+        return mats
+
+    def with_x(mats, cfg, M, outliers):
+        out = []
+        for m in mats:
+            n = Mat()
+            for a in Mat.__slots__:
+                setattr(n, a, getattr(m, a))
+            n.x = torch.from_numpy(synth.activations(M, m.K, cfg, m.layer, m.slot,
+                                                     outliers=outliers)).to(dev)
+            n.y = torch.empty((M, m.N), dtype=torch.float32, device=dev)
+            wbytes = m.K * m.N // 2 + (m.K // 32) * m.N * 4 + (m.K // 32) * m.N // 2
+            n.bytes = wbytes + 4 * M * m.K + 4 * M * m.N + (4 * m.N if m.b is not None else 0)
+            n.flops = 2 * M * m.K * m.N
+            out.append(n)
+        return out
+
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+
+    def run_pass(mats, head=None):
+        for m in mats:
+            w4.w4_matmul(m.x, m.Wq, m.s, m.z, m.b, out=m.y, workspace=ws)
+        if head is not None:
+            head()
+
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, steps, warmup):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def hold_gpu():
+        """Queue a long GPU job so the launches that follow are timed back to back."""
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)
+        else:
+            a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+            for _ in range(20):
+                a.fill_(1)
+
+    def per_launch_ms(mats, reps=3):
+        """Duration of each matmul launch (HIP events on the launch stream)."""
+        res = np.zeros((reps, len(mats)))
+        for r in range(reps):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in mats]
+            hold_gpu()
+            for (a, b), m in zip(evs, mats):
+                a.record()
+                w4.w4_matmul(m.x, m.Wq, m.s, m.z, m.b, out=m.y, workspace=ws)
+                b.record()
+            torch.cuda.synchronize()
+            res[r] = [a.elapsed_time(b) for a, b in evs]
+        return res.mean(axis=0)
+
+    log("building the 3.8B-dense-shaped body (2.32 GB packed) ...")
+    t = time.perf_counter()
+    dense = build_body("dense38", synth.CFG_DENSE38, 1, with_bias=False, outliers=False)
+    log(f"  built in {time.perf_counter() - t:.1f} s")
+
+    # ------------------------------------------------------------ timed steps
+    graph = capture(lambda: run_pass(dense))
+    ms, wall = time_graph(graph, args.steps, args.warmup)
+    pass_bytes = sum(m.bytes for m in dense)
+    pass_flops = sum(m.flops for m in dense)
+    value = pass_bytes / (ms * 1e-3) / 1e9
+    log(f"dense38 M=1 pass: {ms:.4f} ms, {value:.1f} GB/s, {1e3 / ms:.1f} tok/s")
+
+    # ------------------------------------------------------ per-kernel roofline
+    dur = per_launch_ms(dense)
+    launches = len(dense)
+    avg_bytes = pass_bytes / launches
+    avg_ms = float(dur.mean())
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    per_shape = {}
+    for slot, (K, N) in enumerate(synth.DENSE38_SHAPES):
+        d = [dur[i] for i, m in enumerate(dense) if m.slot == slot]
+        b = dense[slot].bytes
+        per_shape[f"{K}x{N}"] = {"us": round(1e3 * float(np.mean(d)), 3),
+                                 "GB_s": round(b / (np.mean(d) * 1e-3) / 1e9, 1)}
+    log(f"GEMV per launch: {1e3 * avg_ms:.2f} us avg, {achieved:.1f} GB/s; {per_shape}")
+
+    # ------------------------------------------------ parity + CPU baseline
+    import oracle
+    orc = oracle.default()
+    parity = {"checked_outputs": 0, "max_err_over_bound": 0.0, "ok": True}
+    cpu = None
+    if not args.skip_cpu:
+        torch.cuda.synchronize()
+        cpu_time, cpu_bytes, done = 0.0, 0, 0
+        for m in dense:
+            W = synth.weights(m.K, m.N, synth.CFG_DENSE38, m.layer, m.slot)
+            Wq, s, z = orc.quantize_pack(W)
+            x = m.x.cpu().numpy()
+            t0 = time.perf_counter()
+            y_ref, bound = orc.w4_matmul(x, Wq, s, z)
+            cpu_time += time.perf_counter() - t0
+            cpu_bytes += m.bytes
+            done += 1
+            y = m.y.cpu().numpy()
+            r = float(np.max(np.abs(y.astype(np.float64) - y_ref) / bound))
+            parity["checked_outputs"] += y.size
+            parity["max_err_over_bound"] = max(parity["max_err_over_bound"], r)
+            parity["ok"] &= bool(r <= 1.0)
+            if cpu_time >= args.cpu_seconds:
+                break
+        cpu_gbs = cpu_bytes / cpu_time / 1e9
+        cpu = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {done} of the 128 M=1 matmuls of the 3.8B-dense body "
+                         f"({cpu_bytes / 1e6:.1f} MB of W4), dequantize then fp64 matmul, "
+                         f"{cpu_time:.1f} s",
+               "tokens_per_s_equiv": round(cpu_gbs * 1e9 / pass_bytes, 4)}
+        log(f"CPU oracle: {cpu_gbs:.3f} GB/s over {done} matmuls; parity {parity}")
+
+    # ------------------------------------------------------------- secondary
+    secondary = {}
+    if not args.skip_secondary:
+        # 3.8B body at M = 16 (batched decode), same weights
+        d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
+        g16 = capture(lambda: run_pass(d16))
+        ms16, _ = time_graph(g16, 3, 1)
+        fl16 = sum(m.flops for m in d16)
+        secondary["dense38_m16_pass"] = {
+            "ms": round(ms16, 4), "tokens_per_s": round(16e3 / ms16, 1),
+            "TFLOP_s": round(fl16 / (ms16 * 1e-3) / 1e12, 3),
+            "frac_fp32_mfma_peak": round(fl16 / (ms16 * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
+        del d16, g16
+        del graph
+        dense.clear()
+        torch.cuda.empty_cache()
+
+        gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)
+        gg = capture(lambda: run_pass(gpt2))
+        msg, _ = time_graph(gg, 200, 20)
+        gb = sum(m.bytes for m in gpt2)
+        secondary["gpt2_decode_pass"] = {
+            "ms": round(msg, 5), "tokens_per_s": round(1e3 / msg, 1),
+            "GB_s": round(gb / (msg * 1e-3) / 1e9, 1),
+            "note": "55 MB body: resident in the 256 MB Infinity Cache across passes"}
+
+        E = torch.from_numpy(synth.head_table()).to(dev)
+        heads = {}
+        for ldq in (synth.GPT2_VOCAB, 50272):
+            Q, hs = w4.i8_quantize_head(E, ldq=ldq)
+            xl = torch.from_numpy(synth.activations(1, synth.GPT2_HIDDEN, synth.CFG_HEAD)).to(dev)[0]
+            out = torch.empty(synth.GPT2_VOCAB, device=dev)
+            gh = capture(lambda: w4.i8_head_logits(xl, Q, hs, out=out, workspace=ws))
+            msh, _ = time_graph(gh, 200, 20)
+            hb = synth.GPT2_HIDDEN * ldq + 4 * synth.GPT2_VOCAB * 2 + 4 * synth.GPT2_HIDDEN
+            heads[str(ldq)] = {"us": round(1e3 * msh, 3), "GB_s": round(hb / (msh * 1e-3) / 1e9, 1)}
+            heads[str(ldq)]["Q"] = Q
+            heads[str(ldq)]["hs"] = hs
+        secondary["i8_head_768x50257"] = {k: {a: b for a, b in v.items() if a in ("us", "GB_s")}
+                                         for k, v in heads.items()}
+
+        pre = with_x(gpt2, synth.CFG_GPT2_PREFILL, synth.GPT2_PROMPT, outliers=False)
+        Qh, hsh = heads["50272"]["Q"], heads["50272"]["hs"]
+        last = pre[-1]
+        lg = torch.empty(synth.GPT2_VOCAB, device=dev)
+
+        def head_last():
+            # the head reads the last prompt row of the final projection's input
+            w4.i8_head_logits(last.x[-1], Qh, hsh, out=lg, workspace=ws)
+
+        gp = capture(lambda: run_pass(pre, head_last))
+        msp, _ = time_graph(gp, 20, 3)
+        fp = sum(m.flops for m in pre) + 2 * synth.GPT2_HIDDEN * synth.GPT2_VOCAB
+        secondary["gpt2_prefill_m58_pass_plus_head"] = {
+            "ms": round(msp, 4), "tokens_per_s": round(synth.GPT2_PROMPT * 1e3 / msp, 1),
+            "TFLOP_s": round(fp / (msp * 1e-3) / 1e12, 3)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; weights N(0,0.02) quantized on the GPU, x N(0,1))",
+        "config": {
+            "workload": "3.8B-dense-shaped decode body pass, M=1: 32 layers x (3072x9216, "
+                        "3072x3072, 3072x16384, 8192x3072) W4 matmuls, uint4 block-32 "
+                        "asymmetric, fp32 scales, packed uint4 zeros",
+            "launches_per_step": launches,
+            "algorithmic_bytes_per_step": pass_bytes,
+            "flops_per_step": pass_flops,
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "body_pass_tokens_per_s": round(1e3 / ms, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_gemv_fast", "avg_launch_us": round(1e3 * avg_ms, 3),
+                     "avg_bytes_per_launch": round(avg_bytes), "per_shape": per_shape},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

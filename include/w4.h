@@ -1,0 +1,164 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) 4-bit block-dequant weight matmul and
+ * the int8 tied LM head.
+ *
+ * The method (page "ONNX export, quantization and the browser runtime",
+ * section "Quantization (train/quantize.py)"):
+ *   step 1  every body weight is a plain [K, N] constant followed by a bias Add;
+ *   step 2  it is stored 4-bit: asymmetric, blocks of 32 along K, one fp32
+ *           scale and one uint4 zero point per block, as packed UINT4, and a
+ *           blocked DequantizeLinear gives w_hat = (q - z) * scale;
+ *   step 3  the tied embedding / LM head is one int8 table [768, 50257] with
+ *           one scale per token; the token lookup gathers its columns;
+ *   step 4  the head is applied to the last position only.
+ * The paragraph after the steps: the runtime folds the dequantization and
+ * runs fp32 kernels, so every matmul here computes x . w_hat in fp32.
+ *
+ * Layouts (all row-major, all device memory owned by the caller):
+ *   x       fp32  [M, K]
+ *   Wq      uint8 [K, N/2]     Wq[k, j] = q[k, 2j] | q[k, 2j+1] << 4
+ *   scales  fp32  [K/32, N]    scale of rows 32b..32b+31 of column n
+ *   zeros   uint8 [K/32, N/2]  packed like Wq: z[b, 2j] low nibble, z[b, 2j+1] high
+ *   bias    fp32  [N]          may be NULL
+ *   y       fp32  [M, N]
+ *   Q       int8  [K, ldq]     head table, ldq >= N; hs fp32 [N] one scale per token
+ * The pairing of nibbles along N (flat row-major UINT4 packing of the [K, N]
+ * code tensor, element 2i in the low nibble) is a reading: the page says
+ * only "raw packed UINT4"; low nibble first is fixed.
+ *
+ * Conventions:
+ *   - Return value: W4_OK (0) or a W4_ERR_* code; nothing is thrown.  Every
+ *     argument is checked on the host before any HIP call, so a bad call
+ *     enqueues nothing.  W4_ERR_LAUNCH carries the HIP error of the launch.
+ *   - Sizes are int64_t.  Empty sizes are valid: M == 0 or N == 0 enqueue
+ *     nothing; K == 0 makes every output equal to the bias (or 0).
+ *   - Pointers are device pointers (16-byte aligned for Wq, scales, zeros and
+ *     the head table Q; 4-byte aligned for fp32 arrays).  A pointer may be NULL
+ *     only when the buffer it names is empty, or where marked "may be NULL".
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Calls only enqueue work on it: they never synchronize, and never
+ *     allocate device memory.  Scratch memory is the caller's `workspace`.
+ *   - Data-dependent failures that the host cannot see (a non-finite weight)
+ *     are reported through the optional device word `d_status`: the kernel
+ *     stores W4_ERR_NONFINITE there and leaves it untouched otherwise, so the
+ *     caller zeroes it first and reads it after synchronizing.
+ *   - All kernels are built for gfx950 only; any other current device gives
+ *     W4_ERR_DEVICE.  The library holds no per-call state and is safe to call
+ *     from several host threads; two calls that share a workspace must be
+ *     ordered on one stream.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4_ABI_VERSION 1
+
+enum {
+    W4_OK = 0,
+    W4_ERR_NULL_PTR = 1,    /* a required pointer is NULL                         */
+    W4_ERR_BAD_SHAPE = 2,   /* negative size, K % 32 != 0, N odd, ldq < N, bad token */
+    W4_ERR_MISALIGNED = 3,  /* a pointer breaks the alignment rule above          */
+    W4_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required            */
+    W4_ERR_DEVICE = 5,      /* no current HIP device, or it is not gfx950         */
+    W4_ERR_LAUNCH = 6,      /* the kernel launch failed (HIP error)               */
+    W4_ERR_NONFINITE = 7    /* device status only: a non-finite input value       */
+};
+
+/* Version of this header's ABI (W4_ABI_VERSION). */
+int w4_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *w4_strerror(int status);
+
+/* ---------------------------------------------------------------------------
+ * Block quantizer and packer (step 2).  W fp32 [K, N] -> Wq, scales, zeros.
+ * Per block (32 rows of one column): lo = min(0, min w), hi = max(0, max w),
+ * s = (hi - lo) / 15 in fp32 with a correctly rounded division; s == 0 gives
+ * s = z = q = 0; else z = clamp(rint(-lo / s), 0, 15) and
+ * q = clamp(rint(w / s) + z, 0, 15), rint rounding half to even (a reading:
+ * ONNX QuantizeLinear's rule; the page states none).  The zero-inclusive
+ * range is also a reading: it keeps real 0 representable, so a block whose
+ * weights share one sign still meets |w - w_hat| <= s / 2.
+ * Output bytes are a deterministic function of W (bit-for-bit reproducible).
+ * d_status (may be NULL): set to W4_ERR_NONFINITE if a weight is not finite
+ * or a scale overflows; the outputs of such a block are unspecified.
+ * ------------------------------------------------------------------------- */
+int w4_quantize_pack(const float *W, int64_t K, int64_t N,
+                     uint8_t *Wq, float *scales, uint8_t *zeros,
+                     int *d_status, void *stream);
+
+/* Unpack codes and zero points one per byte: q uint8 [K, N], z uint8 [K/32, N]. */
+int w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N,
+              uint8_t *q, uint8_t *z, void *stream);
+
+/* Blocked dequantization (step 2): W_hat fp32 [K, N],
+ * W_hat[k, n] = fl32((q[k, n] - z[k/32, n]) * scales[k/32, n]) -- one fp32
+ * multiply of an exact small integer, so the result is bit-exact.          */
+int w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                  int64_t K, int64_t N, float *W_hat, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * 4-bit matmul (steps 1-2 with the folded-fp32 runtime):
+ *   y[m, n] = sum_k x[m, k] * w_hat[k, n] + bias[n]
+ * computed in fp32 (never TF32 or lower).  Accuracy: every output is within
+ * 1e-5 * (sum_k |x[m, k] * w_hat[k, n]| + |bias[n]|) + 1e-6 of the exact
+ * value.  M == 1 runs the fused dequant-GEMV; M > 1 runs the dequant-to-LDS
+ * fp32-MFMA kernel.  Results are deterministic (no floating-point atomics).
+ * bias may be NULL.  The workspace holds split-K partial sums and per-tile
+ * arrival counters: it must be at least w4_matmul_workspace_bytes(M, K, N)
+ * bytes, zero-filled once when first allocated; every call leaves its
+ * counters at zero again, so the same workspace serves any later call.
+ * ------------------------------------------------------------------------- */
+size_t w4_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+int w4_matmul(const float *x, int64_t M, int64_t K,
+              const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t N,
+              const float *bias, float *y,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Argument check of w4_matmul without any HIP call (same return codes,
+ * minus W4_ERR_DEVICE / W4_ERR_LAUNCH); usable on a machine with no GPU.   */
+int w4_check_matmul_args(const float *x, int64_t M, int64_t K,
+                         const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                         int64_t N, const float *bias, const float *y,
+                         const void *workspace, size_t workspace_bytes);
+
+/* ---------------------------------------------------------------------------
+ * int8 tied head (step 3).  E fp32 [K, N] -> Q int8 [K, ldq], hs fp32 [N]:
+ * hs[n] = max_k |E[k, n]| / 127 (correctly rounded fp32 division),
+ * Q[k, n] = clamp(rint(E[k, n] / hs[n]), -127, 127); a zero column gives
+ * hs = 0 and Q = 0; padding columns N..ldq-1 are written as 0.  Bit-exact.
+ * d_status (may be NULL) reports a non-finite entry.                       */
+int i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq,
+                     int8_t *Q, float *hs, int *d_status, void *stream);
+
+/* Last-token logits (step 4): logits[n] = sum_k x_last[k] * fl32(Q[k, n] * hs[n]),
+ * fp32, within the same bound as w4_matmul.  x_last is the last row of the
+ * activations (the caller passes x + (M - 1) * K).  Any ldq >= N works;
+ * ldq % 16 == 0 takes the 16-byte-load path.  The workspace rule is that of
+ * w4_matmul, with size i8_head_workspace_bytes(K, N).                      */
+size_t i8_head_workspace_bytes(int64_t K, int64_t N);
+
+int i8_head_logits(const float *x_last, int64_t K, const int8_t *Q, int64_t ldq,
+                   const float *hs, int64_t N, float *logits,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Token lookup from the same table (step 3: gather along axis 1, then
+ * transpose): out[t, k] = fl32(Q[k, tokens[t]] * hs[tokens[t]]), fp32 [T, K],
+ * bit-exact.  tokens int64 [T] on the device; an id outside [0, N) sets
+ * d_status (may be NULL) to W4_ERR_BAD_SHAPE and yields a zero row.        */
+int i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
+             const float *hs, int64_t K, int64_t N, float *out,
+             int *d_status, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

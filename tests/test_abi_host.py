@@ -1,0 +1,131 @@
+"""The C-ABI library on a machine without a GPU: exports, host-side checks, plans.
+
+No compute call is made here.  Every entry point validates its arguments on
+the host before touching HIP, so each error code below is produced without a
+device; a well-formed call reaches the device check and reports
+W4_ERR_DEVICE when no gfx950 is present.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import w4_block_dequant_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+NO_GPU = not torch.cuda.is_available()
+A = 1 << 12  # a fake, 4 KiB-aligned "device address": never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for must in ("w4_quantize_pack", "w4_matmul", "i8_head_logits", "w4_unpack", "w4_dequantize",
+                 "i8_quantize_head", "i8_embed", "w4_matmul_workspace_bytes",
+                 "i8_head_workspace_bytes", "w4_check_matmul_args", "w4_strerror",
+                 "w4_abi_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_strings():
+    assert w4.w4_abi_version() == 1
+    for code in range(8):
+        assert w4.w4_strerror(code)
+    assert w4.w4_strerror(99) == "unknown status"
+
+
+def check(M, K, N, x=A, Wq=A, s=A, z=A, bias=None, y=A, ws=A, wsb=None):
+    if wsb is None:
+        wsb = w4.w4_matmul_workspace_bytes(M, K, N)
+    return w4.library().w4_check_matmul_args(x, M, K, Wq, s, z, N, bias, y, ws, wsb)
+
+
+def test_matmul_shape_checks():
+    assert check(1, 768, 768) == w4.W4_OK
+    assert check(-1, 768, 768) == w4.W4_ERR_BAD_SHAPE
+    assert check(1, 100, 768) == w4.W4_ERR_BAD_SHAPE       # K % 32 != 0
+    assert check(1, 768, 767) == w4.W4_ERR_BAD_SHAPE       # N odd
+    assert check(1, -32, 768) == w4.W4_ERR_BAD_SHAPE
+    assert check(1, 1 << 30, 1 << 30) == w4.W4_ERR_BAD_SHAPE  # beyond the index range
+    # empty problems need no pointers at all
+    assert check(0, 768, 768, x=None, Wq=None, s=None, z=None, y=None) == w4.W4_OK
+    assert check(4, 768, 0, x=None, Wq=None, s=None, z=None, y=None) == w4.W4_OK
+    assert check(1, 0, 768, x=None, Wq=None, s=None, z=None) == w4.W4_OK
+
+
+def test_matmul_pointer_checks():
+    assert check(1, 768, 768, x=None) == w4.W4_ERR_NULL_PTR
+    assert check(1, 768, 768, Wq=None) == w4.W4_ERR_NULL_PTR
+    assert check(1, 768, 768, y=None) == w4.W4_ERR_NULL_PTR
+    assert check(1, 768, 768, Wq=A + 8) == w4.W4_ERR_MISALIGNED
+    assert check(1, 768, 768, s=A + 4) == w4.W4_ERR_MISALIGNED
+    assert check(1, 768, 768, x=A + 4) == w4.W4_ERR_MISALIGNED
+    assert check(1, 768, 768, y=A + 2) == w4.W4_ERR_MISALIGNED
+    assert check(1, 768, 768, bias=A + 1) == w4.W4_ERR_MISALIGNED
+    assert check(1, 768, 768, bias=A + 4) == w4.W4_OK
+
+
+def test_workspace_rules():
+    K, N = 3072, 9216
+    need = w4.w4_matmul_workspace_bytes(1, K, N)
+    assert need > 0                      # this shape splits K across workgroups
+    assert check(1, K, N, ws=None, wsb=0) == w4.W4_ERR_WORKSPACE
+    assert check(1, K, N, ws=A, wsb=need - 1) == w4.W4_ERR_WORKSPACE
+    assert check(1, K, N, ws=A, wsb=need) == w4.W4_OK
+    assert check(1, K, N, ws=A + 16, wsb=need) == w4.W4_ERR_MISALIGNED
+    assert w4.w4_matmul_workspace_bytes(1, 100, N) == 0   # invalid shape
+    # split-K workspace: a counter per 256-column tile plus the partial sums
+    tiles = (N + 255) // 256
+    assert need >= tiles * 4 + 256 * tiles * 4
+
+
+def test_every_body_shape_is_planned():
+    import synth
+    for K, N in synth.GPT2_SHAPES + synth.DENSE38_SHAPES:
+        assert check(1, K, N, ws=A, wsb=w4.w4_matmul_workspace_bytes(1, K, N)) == w4.W4_OK
+    assert w4.i8_head_workspace_bytes(768, 50257) > 0
+
+
+@pytest.mark.skipif(not NO_GPU, reason="needs a machine without a GPU")
+def test_valid_calls_report_no_device():
+    lib = w4.library()
+    need = w4.w4_matmul_workspace_bytes(1, 768, 768)
+    st = lib.w4_matmul(A, 1, 768, A, A, A, 768, None, A, A if need else None, need, None)
+    assert st == w4.W4_ERR_DEVICE
+    assert lib.w4_quantize_pack(A, 64, 64, A, A, A, None, None) == w4.W4_ERR_DEVICE
+
+
+def test_entry_points_reject_before_any_hip_call():
+    lib = w4.library()
+    assert lib.w4_quantize_pack(A, 33, 64, A, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_quantize_pack(None, 32, 64, A, A, A, None, None) == w4.W4_ERR_NULL_PTR
+    assert lib.w4_quantize_pack(A + 4, 32, 64, A, A, A, None, None) == w4.W4_ERR_MISALIGNED
+    assert lib.w4_unpack(A, A, 32, 63, A, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_dequantize(A, A, None, 32, 64, A, None) == w4.W4_ERR_NULL_PTR
+    assert lib.w4_matmul(A, 1, 768, A, A, A, 767, None, A, None, 0, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.i8_quantize_head(A, 768, 100, 99, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.i8_quantize_head(A, 768, 100, 100, A + 1, A, None, None) == w4.W4_ERR_MISALIGNED
+    assert lib.i8_head_logits(A, 768, A, 50256, A, 50257, A, None, 0, None) == w4.W4_ERR_BAD_SHAPE
+    need = w4.i8_head_workspace_bytes(768, 50257)
+    assert lib.i8_head_logits(A, 768, A, 50257, A, 50257, A, None, 0, None) == w4.W4_ERR_WORKSPACE
+    assert lib.i8_head_logits(A, 768, A, 50257, A, 50257, A, A, need - 4, None) == w4.W4_ERR_WORKSPACE
+    assert lib.i8_embed(A, 4, A, 50257, A, 768, 50258, A, None, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.i8_embed(A + 4, 4, A, 50257, A, 768, 50257, A, None, None) == w4.W4_ERR_MISALIGNED
+    # empty work succeeds without a device
+    assert lib.w4_matmul(None, 0, 768, None, None, None, 768, None, None, None, 0, None) == w4.W4_OK
+    assert lib.i8_embed(None, 0, None, 10, None, 768, 10, None, None, None) == w4.W4_OK

@@ -1,0 +1,305 @@
+"""HIP path against the CPU oracle on the same seeded inputs (needs a gfx950 GPU).
+
+Bars:
+  * packing, unpacking, dequantization, the head table and its scales, and
+    the token lookup: bit-exact;
+  * every fp32 output of a matmul or the head: |y_gpu - y_ref| <= bound, the
+    oracle's per-output 1e-5 * (sum_k |x w_hat| + |bias|) + 1e-6.
+Every call goes through the C ABI (via the thin binding).  Shapes span
+several tiles and split-K workgroups with ragged tails; the full-size
+3.8B-dense shapes are checked on sampled columns that the oracle computes
+on its own (quantization is per column, so a column subset quantizes to the
+same codes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w4_block_dequant_amd as w4
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ORC = oracle.default()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def assert_bits(a, b, label):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    assert a.shape == b.shape, (label, a.shape, b.shape)
+    av = a.view(np.uint32) if a.dtype == np.float32 else a
+    bv = b.view(np.uint32) if b.dtype == np.float32 else b
+    bad = np.count_nonzero(av != bv)
+    note(f"{label}: {a.size - bad}/{a.size} bit-exact")
+    assert bad == 0
+
+
+def assert_bound(y, y_ref, bound, label):
+    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    note(f"{label}: max |err|/bound = {ratio:.3e} over {err.size} outputs")
+    assert np.all(np.isfinite(y))
+    assert np.all(err <= bound), f"{label}: {np.count_nonzero(err > bound)} outputs out of bound"
+
+
+# --------------------------------------------------------------------------
+# weights with every kind of block the format meets
+# --------------------------------------------------------------------------
+def mixed_weights(K, N, cfg):
+    W = synth.weights(K, N, cfg=cfg)
+    g = np.random.default_rng([cfg, K, N])
+    if N >= 8:
+        W[:, 0] = 0.0                                       # all-zero blocks
+        W[:, 1] = 0.5                                       # constant positive
+        W[:, 2] = -0.25                                     # constant negative
+        W[:, 3] = np.abs(W[:, 3]) + np.float32(0.3)         # same sign
+        W[:, 4] = (g.standard_normal(K) * 1e-41).astype(np.float32)  # subnormal
+        W[:, 5] = g.standard_t(2, size=K).astype(np.float32)          # heavy tail
+    return W
+
+
+PACK_SHAPES = [(32, 2), (64, 34), (96, 530), (768, 2304), (3072, 768), (160, 1024)]
+
+
+@pytest.mark.parametrize("K,N", PACK_SHAPES)
+def test_quantize_pack_bit_exact(K, N):
+    note(f"quantize_pack K={K} N={N}")
+    W = mixed_weights(K, N, cfg=200)
+    ref = ORC.quantize_pack(W)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = w4.w4_quantize_pack(dev(W), d_status=st)
+    for name, a, b in zip(("Wq", "scales", "zeros"), got, ref):
+        assert_bits(host(a), b, f"{name} {K}x{N}")
+    assert host(st)[0] == 0
+
+
+def test_quantize_pack_on_grid_and_ties():
+    from oracle_pins import _on_grid
+    W, q, z, s = _on_grid(256, 34, 4)
+    ref = ORC.quantize_pack(W)
+    got = w4.w4_quantize_pack(dev(W))
+    for name, a, b in zip(("Wq", "scales", "zeros"), got, ref):
+        assert_bits(host(a), b, f"on-grid {name}")
+    # halfway weights: (c - z + 1/2) * 2^e
+    g = np.random.default_rng(31)
+    K, N = 64, 16
+    Wt = np.zeros((K, N), np.float32)
+    for b in range(K // 32):
+        for n in range(N):
+            s_ = np.float32(2.0 ** int(g.integers(-9, -4)))
+            zz = int(g.integers(1, 15))
+            rows = g.permutation(32)
+            for i, r in enumerate(rows):
+                c = 0 if i == 0 else 15 if i == 1 else int(g.integers(0, 15))
+                off = 0.0 if i < 2 else 0.5
+                Wt[b * 32 + r, n] = np.float32(c - zz + off) * s_
+    ref = ORC.quantize_pack(Wt)
+    got = w4.w4_quantize_pack(dev(Wt))
+    for name, a, b in zip(("Wq", "scales", "zeros"), got, ref):
+        assert_bits(host(a), b, f"ties {name}")
+
+
+@pytest.mark.parametrize("K,N", [(64, 34), (768, 768), (96, 530)])
+def test_unpack_and_dequantize_bit_exact(K, N):
+    note(f"unpack/dequantize K={K} N={N}")
+    W = mixed_weights(K, N, cfg=201)
+    Wq, s, z = ORC.quantize_pack(W)
+    q_ref, z_ref = ORC.unpack(Wq, z, K, N)
+    q, zz = w4.w4_unpack(dev(Wq), dev(z), K, N)
+    assert_bits(host(q), q_ref, "q")
+    assert_bits(host(zz), z_ref, "z")
+    What = w4.w4_dequantize(dev(Wq), dev(s), dev(z))
+    assert_bits(host(What), ORC.dequantize(Wq, s, z, K, N), "W_hat")
+
+
+def test_quantize_nonfinite_sets_status():
+    W = synth.weights(64, 32, cfg=202)
+    W[40, 7] = np.nan
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    w4.w4_quantize_pack(dev(W), d_status=st)
+    assert host(st)[0] == w4.W4_ERR_NONFINITE
+    W[40, 7] = 1.0
+    W[3, 3], W[4, 3] = 3e38, -3e38
+    st.zero_()
+    w4.w4_quantize_pack(dev(W), d_status=st)
+    assert host(st)[0] == w4.W4_ERR_NONFINITE
+
+
+# --------------------------------------------------------------------------
+# matmul
+# --------------------------------------------------------------------------
+def run_matmul_case(M, K, N, cfg, bias=True, outliers=False, weights=None):
+    W = mixed_weights(K, N, cfg) if weights is None else weights
+    x = synth.activations(M, K, cfg=cfg, outliers=outliers)
+    b = synth.bias(N, cfg=cfg) if bias else None
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z, b)
+    y = w4.w4_matmul(dev(x), dev(Wq), dev(s), dev(z), None if b is None else dev(b))
+    return host(y), y_ref, bound
+
+
+GEMV_SHAPES = [
+    (32, 16), (64, 256), (96, 272), (768, 768), (768, 2304), (3072, 768), (768, 3072),
+    (1024, 1008), (8192, 512), (256, 40), (128, 2), (4096, 4112),
+]
+
+
+@pytest.mark.parametrize("K,N", GEMV_SHAPES)
+@pytest.mark.parametrize("bias", [True, False])
+def test_gemv_m1(K, N, bias):
+    note(f"gemv M=1 K={K} N={N} bias={bias}")
+    y, y_ref, bound = run_matmul_case(1, K, N, cfg=210, bias=bias, outliers=(K % 64 == 0))
+    assert_bound(y, y_ref, bound, f"gemv {K}x{N}")
+
+
+@pytest.mark.parametrize("M", [2, 3, 16, 58, 64, 65])
+@pytest.mark.parametrize("K,N", [(768, 768), (96, 272), (256, 40)])
+def test_small_m(M, K, N):
+    note(f"small-M M={M} K={K} N={N}")
+    y, y_ref, bound = run_matmul_case(M, K, N, cfg=211, outliers=True)
+    assert_bound(y, y_ref, bound, f"M={M} {K}x{N}")
+
+
+@pytest.mark.parametrize("M", [1, 58])
+@pytest.mark.parametrize("slot", range(4))
+def test_gpt2_body_shapes(M, slot):
+    K, N = synth.GPT2_SHAPES[slot]
+    note(f"gpt2 slot {slot} M={M} K={K} N={N}")
+    W = synth.weights(K, N, cfg=synth.CFG_GPT2_PREFILL, slot=slot)
+    y, y_ref, bound = run_matmul_case(M, K, N, cfg=synth.CFG_GPT2_PREFILL, weights=W)
+    assert_bound(y, y_ref, bound, f"gpt2 M={M} {K}x{N}")
+
+
+def sample_pairs(N, count, seed):
+    g = np.random.default_rng(seed)
+    pairs = np.sort(g.choice(N // 2, size=count, replace=False))
+    pairs[0], pairs[-1] = 0, N // 2 - 1
+    return np.unique(pairs)
+
+
+@pytest.mark.parametrize("slot", range(4))
+@pytest.mark.parametrize("M", [1, 16])
+def test_dense38_full_size_sampled(slot, M):
+    """Full-size 3.8B-dense shapes in the benchmark's launch configuration."""
+    K, N = synth.DENSE38_SHAPES[slot]
+    note(f"dense38 slot {slot} M={M} K={K} N={N} (sampled columns)")
+    W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=0, slot=slot)
+    x = synth.activations(M, K, cfg=synth.CFG_DENSE38, layer=0, slot=slot, outliers=True)
+    Wq_d, s_d, z_d = w4.w4_quantize_pack(dev(W))
+    y = host(w4.w4_matmul(dev(x), Wq_d, s_d, z_d))
+    pairs = sample_pairs(N, 48, seed=slot)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    Wq, s, z = ORC.quantize_pack(W[:, cols])
+    # packing of the sampled column pairs is bit-exact
+    assert_bits(host(Wq_d)[:, pairs], Wq, "sampled Wq")
+    assert_bits(host(s_d)[:, cols], s, "sampled scales")
+    assert_bits(host(z_d)[:, pairs], z, "sampled zeros")
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    assert_bound(y[:, cols], y_ref, bound, f"dense38 {K}x{N} M={M}")
+
+
+def test_matmul_empty_and_bias_only():
+    K, N = 64, 32
+    W = synth.weights(K, N, cfg=212)
+    Wq, s, z = (dev(a) for a in ORC.quantize_pack(W))
+    b = synth.bias(N, cfg=212)
+    y = w4.w4_matmul(torch.zeros((0, K), device=DEV), Wq, s, z, dev(b))
+    assert y.shape == (0, N)
+    # K == 0: the output is the bias
+    e = torch.zeros((0, N // 2), dtype=torch.uint8, device=DEV)
+    y = w4.w4_matmul(torch.zeros((3, 0), device=DEV), e,
+                     torch.zeros((0, N), device=DEV), e, dev(b))
+    assert_bits(host(y), np.stack([b, b, b]), "K=0 bias")
+    y = w4.w4_matmul(torch.zeros((1, 0), device=DEV), e, torch.zeros((0, N), device=DEV), e)
+    assert not host(y).any()
+
+
+def test_matmul_one_hot_rows_are_dequantized_rows():
+    K, N = 256, 512
+    W = synth.weights(K, N, cfg=213)
+    Wq, s, z = ORC.quantize_pack(W)
+    What = ORC.dequantize(Wq, s, z, K, N)
+    Wd = [dev(a) for a in (Wq, s, z)]
+    for k in (0, 31, 32, 200, K - 1):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        y = host(w4.w4_matmul(dev(x), *Wd))
+        assert_bits(y[0], What[k], f"one-hot row {k}")
+
+
+def test_matmul_deterministic_and_workspace_clean():
+    K, N = 3072, 9216
+    W = synth.weights(K, N, cfg=214)
+    x = dev(synth.activations(1, K, cfg=214))
+    Wd = w4.w4_quantize_pack(dev(W))
+    need = w4.w4_matmul_workspace_bytes(1, K, N)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    y1 = host(w4.w4_matmul(x, *Wd, workspace=ws))
+    y2 = host(w4.w4_matmul(x, *Wd, workspace=ws))
+    assert_bits(y1, y2, "repeat")
+    tiles = (N + 255) // 256
+    assert not host(ws[: tiles * 4]).any(), "arrival counters must return to zero"
+
+
+def test_matmul_rejects_bad_device_pointers():
+    K, N = 64, 32
+    Wq, s, z = (dev(a) for a in ORC.quantize_pack(synth.weights(K, N, cfg=215)))
+    x = torch.zeros((1, K + 4), device=DEV)[:, 1:K + 1]     # 4-byte offset view
+    lib = w4.library()
+    st = lib.w4_matmul(x.data_ptr(), 1, K, Wq.data_ptr(), s.data_ptr(), z.data_ptr(), N, None,
+                       torch.empty(N, device=DEV).data_ptr(), None, 0, None)
+    assert st == w4.W4_ERR_MISALIGNED
+
+
+# --------------------------------------------------------------------------
+# int8 head and token lookup
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("K,N,ldq", [(768, 50257, 50257), (768, 50257, 50272), (100, 37, 37),
+                                     (100, 37, 48), (64, 300, 301), (33, 1000, 1003)])
+def test_head(K, N, ldq):
+    note(f"head K={K} N={N} ldq={ldq}")
+    cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 220
+    E = synth.head_table(K, N, cfg=cfg)
+    if N > 10:
+        E[:, 5] = 0.0
+    Q_ref, hs_ref = ORC.i8_quantize_head(E, ldq=ldq)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Q, hs = w4.i8_quantize_head(dev(E), ldq=ldq, d_status=st)
+    assert_bits(host(Q), Q_ref, f"head Q {K}x{N}/{ldq}")
+    assert_bits(host(hs), hs_ref, f"head hs {K}x{N}/{ldq}")
+    assert host(st)[0] == 0
+    x = synth.activations(58, K, cfg=cfg, outliers=True)
+    x_last = dev(x)[-1]                       # the last position only
+    logits = host(w4.i8_head_logits(x_last, dev(Q_ref), dev(hs_ref)))
+    ref, bound = ORC.i8_head_logits(x[-1], Q_ref, hs_ref)
+    assert_bound(logits, ref, bound, f"head logits {K}x{N}/{ldq}")
+
+
+def test_embed():
+    K, N, ldq = 768, 50257, 50257
+    E = synth.head_table(K, N)
+    Q, hs = ORC.i8_quantize_head(E, ldq=ldq)
+    toks = synth.tokens(58, N, cfg=synth.CFG_HEAD)
+    toks[0], toks[-1] = 0, N - 1
+    out = w4.i8_embed(dev(toks), dev(Q), dev(hs))
+    assert_bits(host(out), ORC.i8_embed(toks, Q, hs), "embedding rows")
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad = np.array([3, N, -1], np.int64)
+    out = host(w4.i8_embed(dev(bad), dev(Q), dev(hs), d_status=st))
+    assert host(st)[0] == w4.W4_ERR_BAD_SHAPE
+    assert not out[1:].any()
+    assert_bits(out[0], ORC.i8_embed(bad[:1], Q, hs)[0], "valid row beside bad ids")

@@ -1,0 +1,207 @@
+// The C ABI (include/w4.h): host-side argument checks, device check, and
+// dispatch to the kernel launchers.  Every check runs before any HIP call,
+// so a rejected call enqueues nothing; the w4_check_* functions run the same
+// checks with no HIP call at all.
+#include <atomic>
+#include <string.h>
+
+#include "launch.h"
+#include "w4.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // keeps every index in int64 range
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// A pointer is required unless the buffer it names is empty.
+bool need(const void *p, int64_t count) { return count == 0 || p != nullptr; }
+
+int check_w4_shape(int64_t K, int64_t N) {
+    if (K < 0 || N < 0 || K % 32 != 0 || N % 2 != 0) return W4_ERR_BAD_SHAPE;
+    if (K > kMaxElems / (N > 0 ? N : 1)) return W4_ERR_BAD_SHAPE;
+    return W4_OK;
+}
+
+int check_packed(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
+                 int64_t N) {
+    if (!need(Wq, K * N) || !need(scales, K * N) || !need(zeros, K * N)) return W4_ERR_NULL_PTR;
+    if (!aligned(Wq, 16) || !aligned(scales, 16) || !aligned(zeros, 16)) return W4_ERR_MISALIGNED;
+    return W4_OK;
+}
+
+size_t matmul_workspace(int64_t M, int64_t K, int64_t N) {
+    if (M == 1) return w4::plan_gemv(K, N).workspace;
+    return w4::plan_small_m(M, K, N).workspace;
+}
+
+// The current device must be a gfx950; the answer is cached per device.
+int device_check() {
+    static std::atomic<int> cache[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return W4_ERR_DEVICE;
+    }
+    if (dev >= 64) return W4_ERR_DEVICE;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return W4_ERR_DEVICE;
+        }
+        c = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c == 1 ? W4_OK : W4_ERR_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? W4_OK : W4_ERR_LAUNCH; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int w4_abi_version(void) { return W4_ABI_VERSION; }
+
+const char *w4_strerror(int status) {
+    switch (status) {
+    case W4_OK: return "ok";
+    case W4_ERR_NULL_PTR: return "a required pointer is NULL";
+    case W4_ERR_BAD_SHAPE: return "bad shape (negative size, K % 32 != 0, N odd, ldq < N, or token id out of range)";
+    case W4_ERR_MISALIGNED: return "misaligned pointer";
+    case W4_ERR_WORKSPACE: return "workspace missing or too small";
+    case W4_ERR_DEVICE: return "no current HIP device, or the device is not gfx950";
+    case W4_ERR_LAUNCH: return "kernel launch failed";
+    case W4_ERR_NONFINITE: return "non-finite input value";
+    default: return "unknown status";
+    }
+}
+
+int w4_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, float *scales,
+                     uint8_t *zeros, int *d_status, void *stream) {
+    int st = check_w4_shape(K, N);
+    if (st) return st;
+    if (!need(W, K * N)) return W4_ERR_NULL_PTR;
+    if ((st = check_packed(Wq, scales, zeros, K, N))) return st;
+    if (!aligned(W, 16) || !aligned(d_status, 4)) return W4_ERR_MISALIGNED;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_quantize_pack(W, K, N, Wq, scales, zeros, d_status, as_stream(stream)));
+}
+
+int w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N, uint8_t *q,
+              uint8_t *z, void *stream) {
+    int st = check_w4_shape(K, N);
+    if (st) return st;
+    if (!need(Wq, K * N) || !need(zeros, K * N) || !need(q, K * N) || !need(z, K * N))
+        return W4_ERR_NULL_PTR;
+    if (!aligned(Wq, 16) || !aligned(zeros, 16) || !aligned(q, 2) || !aligned(z, 2))
+        return W4_ERR_MISALIGNED;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_unpack(Wq, zeros, K, N, q, z, as_stream(stream)));
+}
+
+int w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
+                  int64_t N, float *W_hat, void *stream) {
+    int st = check_w4_shape(K, N);
+    if (st) return st;
+    if ((st = check_packed(Wq, scales, zeros, K, N))) return st;
+    if (!need(W_hat, K * N)) return W4_ERR_NULL_PTR;
+    if (!aligned(W_hat, 8)) return W4_ERR_MISALIGNED;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_dequantize(Wq, scales, zeros, K, N, W_hat, as_stream(stream)));
+}
+
+size_t w4_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || check_w4_shape(K, N) != W4_OK) return 0;
+    return matmul_workspace(M, K, N);
+}
+
+int w4_check_matmul_args(const float *x, int64_t M, int64_t K, const uint8_t *Wq,
+                         const float *scales, const uint8_t *zeros, int64_t N, const float *bias,
+                         const float *y, const void *workspace, size_t workspace_bytes) {
+    if (M < 0) return W4_ERR_BAD_SHAPE;
+    int st = check_w4_shape(K, N);
+    if (st) return st;
+    if (M > kMaxElems / (K > 0 ? K : 1) || M > kMaxElems / (N > 0 ? N : 1)) return W4_ERR_BAD_SHAPE;
+    if (M == 0 || N == 0) return W4_OK;
+    if (!need(x, M * K) || !y) return W4_ERR_NULL_PTR;
+    if ((st = check_packed(Wq, scales, zeros, K, N))) return st;
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4)) return W4_ERR_MISALIGNED;
+    const size_t need_ws = matmul_workspace(M, K, N);
+    if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return W4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
+    return W4_OK;
+}
+
+int w4_matmul(const float *x, int64_t M, int64_t K, const uint8_t *Wq, const float *scales,
+              const uint8_t *zeros, int64_t N, const float *bias, float *y, void *workspace,
+              size_t workspace_bytes, void *stream) {
+    int st = w4_check_matmul_args(x, M, K, Wq, scales, zeros, N, bias, y, workspace,
+                                  workspace_bytes);
+    if (st) return st;
+    if (M == 0 || N == 0) return W4_OK;
+    if ((st = device_check())) return st;
+    if (M == 1)
+        return launched(w4::launch_gemv(w4::plan_gemv(K, N), x, K, Wq, scales, zeros, N, bias, y,
+                                        workspace, as_stream(stream)));
+    return launched(w4::launch_small_m(w4::plan_small_m(M, K, N), x, M, K, Wq, scales, zeros, N,
+                                       bias, y, workspace, as_stream(stream)));
+}
+
+int i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q, float *hs,
+                     int *d_status, void *stream) {
+    if (K < 0 || N < 0 || ldq < N) return W4_ERR_BAD_SHAPE;
+    if (K > kMaxElems / (ldq > 0 ? ldq : 1)) return W4_ERR_BAD_SHAPE;
+    if (!need(E, K * N) || !need(Q, K * ldq) || !need(hs, N)) return W4_ERR_NULL_PTR;
+    if (!aligned(E, 4) || !aligned(Q, 16) || !aligned(hs, 4) || !aligned(d_status, 4))
+        return W4_ERR_MISALIGNED;
+    if (K * ldq == 0 && N == 0) return W4_OK;
+    int st = device_check();
+    if (st) return st;
+    return launched(w4::launch_head_quantize(E, K, N, ldq, Q, hs, d_status, as_stream(stream)));
+}
+
+size_t i8_head_workspace_bytes(int64_t K, int64_t N) {
+    if (K < 0 || N < 0) return 0;
+    return w4::plan_head(K, N).workspace;
+}
+
+int i8_head_logits(const float *x_last, int64_t K, const int8_t *Q, int64_t ldq, const float *hs,
+                   int64_t N, float *logits, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (K < 0 || N < 0 || ldq < N) return W4_ERR_BAD_SHAPE;
+    if (K > kMaxElems / (ldq > 0 ? ldq : 1)) return W4_ERR_BAD_SHAPE;
+    if (N == 0) return W4_OK;
+    if (!need(x_last, K) || !need(Q, K * ldq) || !hs || !logits) return W4_ERR_NULL_PTR;
+    if (!aligned(x_last, 4) || !aligned(Q, 16) || !aligned(hs, 4) || !aligned(logits, 4))
+        return W4_ERR_MISALIGNED;
+    const w4::HeadPlan plan = w4::plan_head(K, N);
+    if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+        return W4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
+    int st = device_check();
+    if (st) return st;
+    return launched(w4::launch_head_logits(plan, x_last, K, Q, ldq, hs, N, logits, workspace,
+                                           as_stream(stream)));
+}
+
+int i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq, const float *hs,
+             int64_t K, int64_t N, float *out, int *d_status, void *stream) {
+    if (T < 0 || K < 0 || N < 0 || ldq < N) return W4_ERR_BAD_SHAPE;
+    if (K > kMaxElems / (ldq > 0 ? ldq : 1) || T > kMaxElems / (K > 0 ? K : 1))
+        return W4_ERR_BAD_SHAPE;
+    if (T * K == 0) return W4_OK;
+    if (!tokens || !Q || !hs || !out) return W4_ERR_NULL_PTR;
+    if (!aligned(tokens, 8) || !aligned(Q, 16) || !aligned(hs, 4) || !aligned(out, 4) ||
+        !aligned(d_status, 4))
+        return W4_ERR_MISALIGNED;
+    int st = device_check();
+    if (st) return st;
+    return launched(w4::launch_embed(tokens, T, Q, ldq, hs, K, N, out, d_status, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Kernel launchers (one per entry point).  Arguments are already validated;
+// each launcher only enqueues work on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace w4 {
+
+hipError_t launch_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq,
+                                float *scales, uint8_t *zeros, int *d_status, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N,
+                         uint8_t *q, uint8_t *z, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                             int64_t K, int64_t N, float *out, hipStream_t stream);
+
+hipError_t launch_gemv(const GemvPlan &plan, const float *x, int64_t K, const uint8_t *Wq,
+                       const float *scales, const uint8_t *zeros, int64_t N, const float *bias,
+                       float *y, void *workspace, hipStream_t stream);
+
+hipError_t launch_small_m(const SmallMPlan &plan, const float *x, int64_t M, int64_t K,
+                          const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                          int64_t N, const float *bias, float *y, void *workspace,
+                          hipStream_t stream);
+
+hipError_t launch_bias_fill(const float *bias, int64_t M, int64_t N, float *y,
+                            hipStream_t stream);
+
+hipError_t launch_head_quantize(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q,
+                                float *hs, int *d_status, hipStream_t stream);
+hipError_t launch_head_logits(const HeadPlan &plan, const float *x, int64_t K, const int8_t *Q,
+                              int64_t ldq, const float *hs, int64_t N, float *logits,
+                              void *workspace, hipStream_t stream);
+hipError_t launch_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
+                        const float *hs, int64_t K, int64_t N, float *out, int *d_status,
+                        hipStream_t stream);
+
+}  // namespace w4

@@ -1,0 +1,63 @@
+// Launch plans: pure host functions (no HIP calls) that fix the grid, the
+// split-K factor and the workspace size of each kernel from the problem shape.
+// The ABI layer validates arguments against them; the launchers execute them.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// Workspace layout shared by the split-K kernels: one 32-bit arrival counter
+// per column tile (padded to 256 bytes), then the fp32 partial sums.
+constexpr size_t kCounterAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- M == 1 fused dequant-GEMV ---------------------------------------------
+// A lane owns 16 consecutive columns (8 bytes of one packed row) and all 32
+// rows of one K-block; 16 lanes cover a 256-column tile, the 4 lane groups of
+// a wave take 4 different K-blocks.  A workgroup of `waves` waves covers one
+// column tile and `blocks_per_wg` K-blocks; `splits` workgroups along K
+// combine their partial sums through the workspace.
+struct GemvPlan {
+    enum Kind { kEmpty = 0, kBiasOnly = 1, kFast = 2, kGeneric = 3 } kind;
+    int64_t tiles = 0;          // column tiles (fast path)
+    int64_t splits = 1;         // workgroups along K per column tile
+    int64_t blocks_per_wg = 0;  // K-blocks per workgroup
+    int waves = 1;              // waves per workgroup
+    int64_t npad = 0;           // tiles * 256
+    size_t workspace = 0;       // bytes
+};
+
+constexpr int kGemvTileCols = 256;
+constexpr int kGemvGroups = 4;  // lane groups per wave
+
+GemvPlan plan_gemv(int64_t K, int64_t N);
+
+// ---- int8 head logits (last row) -------------------------------------------
+// Same geometry as the GEMV: a lane owns 16 columns (16 bytes of a row) and
+// 32 rows; 16 lanes make a 256-column tile; 4 lane groups per wave.
+struct HeadPlan {
+    enum Kind { kEmpty = 0, kZero = 1, kRun = 2 } kind;
+    int64_t tiles = 0, splits = 1, rows_per_wg = 0, npad = 0;
+    int waves = 1;
+    size_t workspace = 0;
+};
+
+HeadPlan plan_head(int64_t K, int64_t N);
+
+// ---- small-M matmul (M > 1) ----------------------------------------------
+struct SmallMPlan {
+    enum Kind { kEmpty = 0, kBiasOnly = 1, kMfma = 2, kGeneric = 3 } kind;
+    int64_t mtiles = 0;         // 16-row tiles of M handled per workgroup pass
+    int64_t tiles = 0;          // column tiles
+    int64_t splits = 1;
+    int64_t blocks_per_wg = 0;
+    int64_t npad = 0;
+    size_t workspace = 0;
+};
+
+SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N);
+
+}  // namespace w4
