@@ -6,7 +6,9 @@ The step is one decode body pass of the 3.8B-dense-shaped model at M = 1:
 32 layers x 4 W4 matmuls (3072x9216 QKV, 3072x3072 out, 3072x16384
 gate+up, 8192x3072 down), 2.32 GB of packed weights, i.e. 128 launches of
 the fused dequant-GEMV on one stream, captured once in a HIP graph and
-replayed.  The weights are far larger than the 256 MB Infinity Cache, so
+replayed.  The weights are quantized on the GPU into the canonical layout
+and prepacked once (K-major copy of the same bytes) before timing; the
+timed GEMV reads the prepacked copy.  The weights are far larger than the 256 MB Infinity Cache, so
 every pass streams them from HBM.  `value` is the pass's algorithmic bytes
 (packed weights, scales, zero points, x and y, each counted once) divided
 by the measured time per pass.
@@ -74,7 +76,8 @@ def main():
     pool = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
 
     class Mat:
-        __slots__ = ("layer", "slot", "K", "N", "Wq", "s", "z", "b", "x", "y", "bytes", "flops")
+        __slots__ = ("layer", "slot", "K", "N", "Wq", "s", "z", "P", "b", "x", "y", "bytes",
+                     "flops")
 
     def build_body(name, cfg, M, with_bias, outliers):
         shapes = synth.body(name)
@@ -90,6 +93,7 @@ def main():
             m = Mat()
             m.layer, m.slot, m.K, m.N = l, s, K, N
             m.Wq, m.s, m.z = w4.w4_quantize_pack(W)
+            m.P = w4.w4_prepack_kmajor(m.Wq, m.s, m.z) if K % 64 == 0 else None
             del W
             m.b = torch.from_numpy(synth.bias(N, cfg, l, s)).to(dev) if with_bias else None
             m.x = torch.from_numpy(synth.activations(M, K, cfg, l, s, outliers=outliers)).to(dev)
@@ -118,9 +122,15 @@ def main():
 
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
 
-    def run_pass(mats, head=None):
-        for m in mats:
+    def matmul(m, layout):
+        if layout == "kmajor":
+            w4.w4_matmul_kmajor(m.x, *m.P, bias=m.b, out=m.y)
+        else:
             w4.w4_matmul(m.x, m.Wq, m.s, m.z, m.b, out=m.y, workspace=ws)
+
+    def run_pass(mats, head=None, layout="kmajor"):
+        for m in mats:
+            matmul(m, layout)
         if head is not None:
             head()
 
@@ -160,7 +170,7 @@ def main():
             for _ in range(20):
                 a.fill_(1)
 
-    def per_launch_ms(mats, reps=3):
+    def per_launch_ms(mats, reps=3, layout="kmajor"):
         """Duration of each matmul launch (HIP events on the launch stream)."""
         res = np.zeros((reps, len(mats)))
         for r in range(reps):
@@ -169,7 +179,7 @@ def main():
             hold_gpu()
             for (a, b), m in zip(evs, mats):
                 a.record()
-                w4.w4_matmul(m.x, m.Wq, m.s, m.z, m.b, out=m.y, workspace=ws)
+                matmul(m, layout)
                 b.record()
             torch.cuda.synchronize()
             res[r] = [a.elapsed_time(b) for a, b in evs]
@@ -201,6 +211,17 @@ def main():
         per_shape[f"{K}x{N}"] = {"us": round(1e3 * float(np.mean(d)), 3),
                                  "GB_s": round(b / (np.mean(d) * 1e-3) / 1e9, 1)}
     log(f"GEMV per launch: {1e3 * avg_ms:.2f} us avg, {achieved:.1f} GB/s; {per_shape}")
+
+    # the same pass on the canonical layout (split-K GEMV), for comparison
+    gcan = capture(lambda: run_pass(dense, layout="canonical"))
+    ms_can, _ = time_graph(gcan, max(3, args.steps // 4), 2)
+    del gcan
+    canonical = {"ms": round(ms_can, 4),
+                 "GB_s": round(pass_bytes / (ms_can * 1e-3) / 1e9, 1),
+                 "tokens_per_s": round(1e3 / ms_can, 1)}
+    log(f"canonical-layout pass: {canonical}")
+    # restore the K-major outputs for the parity check below
+    run_pass(dense)
 
     # ------------------------------------------------ parity + CPU baseline
     import oracle
@@ -239,26 +260,31 @@ def main():
     if not args.skip_secondary:
         # 3.8B body at M = 16 (batched decode), same weights
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
-        g16 = capture(lambda: run_pass(d16))
-        ms16, _ = time_graph(g16, 3, 1)
         fl16 = sum(m.flops for m in d16)
-        secondary["dense38_m16_pass"] = {
-            "ms": round(ms16, 4), "tokens_per_s": round(16e3 / ms16, 1),
-            "TFLOP_s": round(fl16 / (ms16 * 1e-3) / 1e12, 3),
-            "frac_fp32_mfma_peak": round(fl16 / (ms16 * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
-        del d16, g16
+        for layout, name in (("canonical", "dense38_m16_pass_mfma"),
+                             ("kmajor", "dense38_m16_pass_kmajor")):
+            g16 = capture(lambda: run_pass(d16, layout=layout))
+            ms16, _ = time_graph(g16, 3, 1)
+            secondary[name] = {
+                "ms": round(ms16, 4), "tokens_per_s": round(16e3 / ms16, 1),
+                "TFLOP_s": round(fl16 / (ms16 * 1e-3) / 1e12, 3),
+                "frac_fp32_mfma_peak": round(fl16 / (ms16 * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
+            del g16
+        del d16
         del graph
         dense.clear()
         torch.cuda.empty_cache()
 
         gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)
-        gg = capture(lambda: run_pass(gpt2))
-        msg, _ = time_graph(gg, 200, 20)
         gb = sum(m.bytes for m in gpt2)
-        secondary["gpt2_decode_pass"] = {
-            "ms": round(msg, 5), "tokens_per_s": round(1e3 / msg, 1),
-            "GB_s": round(gb / (msg * 1e-3) / 1e9, 1),
-            "note": "55 MB body: resident in the 256 MB Infinity Cache across passes"}
+        for layout in ("kmajor", "canonical"):
+            gg = capture(lambda: run_pass(gpt2, layout=layout))
+            msg, _ = time_graph(gg, 200, 20)
+            secondary[f"gpt2_decode_pass_{layout}"] = {
+                "ms": round(msg, 5), "tokens_per_s": round(1e3 / msg, 1),
+                "GB_s": round(gb / (msg * 1e-3) / 1e9, 1),
+                "note": "55 MB body: resident in the 256 MB Infinity Cache across passes"}
+            del gg
 
         E = torch.from_numpy(synth.head_table()).to(dev)
         heads = {}
@@ -281,10 +307,10 @@ def main():
         lg = torch.empty(synth.GPT2_VOCAB, device=dev)
 
         def head_last():
-            # the head reads the last prompt row of the final projection's input
-            w4.i8_head_logits(last.x[-1], Qh, hsh, out=lg, workspace=ws)
+            # the head reads the last prompt row of the body's output (768 wide)
+            w4.i8_head_logits(last.y[-1], Qh, hsh, out=lg, workspace=ws)
 
-        gp = capture(lambda: run_pass(pre, head_last))
+        gp = capture(lambda: run_pass(pre, head_last, layout="canonical"))
         msp, _ = time_graph(gp, 20, 3)
         fp = sum(m.flops for m in pre) + 2 * synth.GPT2_HIDDEN * synth.GPT2_VOCAB
         secondary["gpt2_prefill_m58_pass_plus_head"] = {
@@ -317,8 +343,9 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_gemv_fast", "avg_launch_us": round(1e3 * avg_ms, 3),
+                     "kernel": "k_gemv_kmajor", "avg_launch_us": round(1e3 * avg_ms, 3),
                      "avg_bytes_per_launch": round(avg_bytes), "per_shape": per_shape},
+        "canonical_layout_pass": canonical,
         "cpu_baseline": cpu,
         "parity": parity,
         "secondary": secondary,

@@ -130,6 +130,33 @@ int w4_check_matmul_args(const float *x, int64_t M, int64_t K,
                          const void *workspace, size_t workspace_bytes);
 
 /* ---------------------------------------------------------------------------
+ * K-major ("prepacked") copy of the same format, for the decode GEMV.  The
+ * page mentions the runtime's weight prepacking; here it is a byte-exact
+ * reordering that makes each output column's data contiguous:
+ *   Pq uint8 [N, K/2]   Pq[n, i] = q[2i, n] | q[2i+1, n] << 4 (pairs along K)
+ *   Ps fp32  [N, K/32]  Ps[n, b] = scales[b, n]
+ *   Pz uint8 [N, K/64]  Pz[n, j] = z[2j, n] | z[2j+1, n] << 4
+ * Same bytes per weight as the canonical layout.  Requires K % 64 == 0.
+ * Pq, Ps, Pz are caller-allocated device buffers (16-byte aligned).        */
+int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                      int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz,
+                      void *stream);
+
+/* y = x . w_hat + bias on the K-major layout: same result contract as
+ * w4_matmul (fp32, same bound, deterministic).  Each workgroup owns whole
+ * columns, so it needs no workspace.  Built for decode (M = 1) and small
+ * batches (up to 4 rows share each weight load; larger M repeats that per
+ * 4 rows).  Indexing is 32-bit: K * N, M * K and M * N must be below 2^31
+ * (W4_ERR_BAD_SHAPE otherwise).                                            */
+int w4_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
+                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *stream);
+
+/* Argument check of w4_matmul_kmajor without any HIP call.                 */
+int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                const float *Ps, const uint8_t *Pz, int64_t N,
+                                const float *bias, const float *y);
+
+/* ---------------------------------------------------------------------------
  * int8 tied head (step 3).  E fp32 [K, N] -> Q int8 [K, ldq], hs fp32 [N]:
  * hs[n] = max_k |E[k, n]| / 127 (correctly rounded fp32 division),
  * Q[k, n] = clamp(rint(E[k, n] / hs[n]), -127, 127); a zero column gives

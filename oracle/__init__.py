@@ -66,6 +66,7 @@ _SIGS = {
     "orc_w4_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "orc_w4_unpack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "orc_w4_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "orc_w4_prepack_kmajor": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P]),
     "orc_matmul_f64": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "orc_w4_matmul": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
     "orc_i8_quantize_head": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
@@ -164,6 +165,17 @@ class Oracle:
                self._l.orc_w4_dequantize(_ptr(_c(Wq, np.uint8)), _ptr(_c(scales, np.float32)),
                                          _ptr(_c(zeros, np.uint8)), K, N, _ptr(out)))
         return out
+
+    def prepack_kmajor(self, Wq, scales, zeros, K, N):
+        """-> (Pq uint8 [N, K/2], Ps fp32 [N, K/32], Pz uint8 [N, K/64])."""
+        Pq = np.zeros((N, K // 2), np.uint8)
+        Ps = np.zeros((N, K // BLOCK), np.float32)
+        Pz = np.zeros((N, K // 64), np.uint8)
+        _check("orc_w4_prepack_kmajor",
+               self._l.orc_w4_prepack_kmajor(_ptr(_c(Wq, np.uint8)), _ptr(_c(scales, np.float32)),
+                                             _ptr(_c(zeros, np.uint8)), K, N, _ptr(Pq), _ptr(Ps),
+                                             _ptr(Pz)))
+        return Pq, Ps, Pz
 
     def matmul_f64(self, x, W, bias=None):
         """x fp32 [M, K], W fp32 [K, N] -> (y fp32 [M, N], bound fp64 [M, N])."""

@@ -129,6 +129,31 @@ int orc_w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zer
     return ORC_OK;
 }
 
+int orc_w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                          int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz)
+{
+    if (bad_w4_shape(K, N) || K % 64 != 0) return ORC_BAD_SHAPE;
+    int64_t nb = K / BLOCK;
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    uint8_t *z = (uint8_t *)malloc((size_t)(nb * N) + 1);
+    uint8_t *qt = (uint8_t *)malloc((size_t)(K * N) + 1);
+    uint8_t *zt = (uint8_t *)malloc((size_t)(nb * N) + 1);
+    if (!q || !z || !qt || !zt) { free(q); free(z); free(qt); free(zt); return ORC_NO_MEMORY; }
+    orc_w4_unpack(Wq, zeros, K, N, q, z);
+    /* transpose the unpacked codes and zero points to column-major, then pack */
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) qt[n * K + k] = q[k * N + n];
+    for (int64_t b = 0; b < nb; ++b)
+        for (int64_t n = 0; n < N; ++n) {
+            zt[n * nb + b] = z[b * N + n];
+            Ps[n * nb + b] = scales[b * N + n];
+        }
+    orc_pack_u4(qt, K * N, Pq);
+    orc_pack_u4(zt, nb * N, Pz);
+    free(q); free(z); free(qt); free(zt);
+    return ORC_OK;
+}
+
 int orc_matmul_f64(const float *x, int64_t M, int64_t K, const float *W, int64_t N,
                    const float *bias, float *y, double *bound)
 {

@@ -69,6 +69,15 @@ int orc_w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N,
 int orc_w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
                       int64_t K, int64_t N, float *W_hat);
 
+/* K-major relayout of the 4-bit format (the same bytes, reordered; the page
+ * calls such a load-time weight reordering "prepacking"):
+ *   Pq uint8 [N, K/2]:   Pq[n, i] = q[2i, n] | q[2i+1, n] << 4  (pairs along K)
+ *   Ps fp32  [N, K/32]:  Ps[n, b] = scales[b, n]
+ *   Pz uint8 [N, K/64]:  Pz[n, j] = z[2j, n] | z[2j+1, n] << 4  (K % 64 == 0)
+ * Status ORC_BAD_SHAPE unless K % 64 == 0 and N even.                      */
+int orc_w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                          int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz);
+
 /* Plain matmul with fp64 accumulation:
  * y[m, n] = fl32(sum_k x[m, k] * W[k, n] + bias[n])  (bias may be NULL),
  * bound[m, n] = 1e-5 * (sum_k |x[m, k] * W[k, n]| + |bias[n]|) + 1e-6,

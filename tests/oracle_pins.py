@@ -321,6 +321,30 @@ def pin_dequant_all_pairs(orc):
     assert len(seen) == 256
 
 
+def pin_prepack_kmajor(orc):
+    """The K-major relayout is the transpose of the unpacked codes, packed
+    low-nibble-first along K; scales and zero points transpose the same way."""
+    for K, N in ((64, 2), (128, 6), (192, 34)):
+        W = synth.weights(K, N, cfg=108, slot=K)
+        Wq, s, z = orc.quantize_pack(W)
+        q, zz = orc.unpack(Wq, z, K, N)
+        Pq, Ps, Pz = orc.prepack_kmajor(Wq, s, z, K, N)
+        assert Pq.shape == (N, K // 2) and Ps.shape == (N, K // 32) and Pz.shape == (N, K // 64)
+        assert np.array_equal(orc.unpack_u4(Pq).reshape(N, K), np.ascontiguousarray(q.T))
+        assert np.array_equal(orc.unpack_u4(Pz).reshape(N, K // 32), np.ascontiguousarray(zz.T))
+        assert np.array_equal(Ps, np.ascontiguousarray(s.T))
+        # spot check of the low-nibble-first pairing along K on one element
+        k, n = K - 3, N - 1
+        byte = int(Pq[n, k // 2])
+        assert (byte >> (4 * (k % 2))) & 15 == int(q[k, n])
+    try:
+        orc.prepack_kmajor(*orc.quantize_pack(synth.weights(32, 4, cfg=108)), 32, 4)
+    except oracle_mod.OracleError as e:
+        assert e.status == oracle_mod.BAD_SHAPE
+    else:
+        raise AssertionError("K % 64 != 0 accepted")
+
+
 # --------------------------------------------------------------------------
 # matmul
 # --------------------------------------------------------------------------
@@ -497,6 +521,7 @@ ALL_PINS = [
     pin_degenerate_blocks,
     pin_shape_and_value_errors,
     pin_dequant_all_pairs,
+    pin_prepack_kmajor,
     pin_matmul_exact_small,
     pin_matmul_special_cases,
     pin_head_quantizer,

@@ -30,6 +30,7 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for must in ("w4_quantize_pack", "w4_matmul", "i8_head_logits", "w4_unpack", "w4_dequantize",
+                 "w4_prepack_kmajor", "w4_matmul_kmajor", "w4_check_matmul_kmajor_args",
                  "i8_quantize_head", "i8_embed", "w4_matmul_workspace_bytes",
                  "i8_head_workspace_bytes", "w4_check_matmul_args", "w4_strerror",
                  "w4_abi_version"):
@@ -126,6 +127,11 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.i8_head_logits(A, 768, A, 50257, A, 50257, A, A, need - 4, None) == w4.W4_ERR_WORKSPACE
     assert lib.i8_embed(A, 4, A, 50257, A, 768, 50258, A, None, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.i8_embed(A + 4, 4, A, 50257, A, 768, 50257, A, None, None) == w4.W4_ERR_MISALIGNED
+    assert lib.w4_check_matmul_kmajor_args(A, 1, 96, A, A, A, 16, None, A) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_check_matmul_kmajor_args(A, 1, 128, A, A, A, 16, None, A) == w4.W4_OK
+    assert lib.w4_check_matmul_kmajor_args(A, 1, 128, A + 8, A, A, 16, None, A) == w4.W4_ERR_MISALIGNED
+    assert lib.w4_check_matmul_kmajor_args(None, 1, 128, A, A, A, 16, None, A) == w4.W4_ERR_NULL_PTR
+    assert lib.w4_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE
     # empty work succeeds without a device
     assert lib.w4_matmul(None, 0, 768, None, None, None, 768, None, None, None, 0, None) == w4.W4_OK
     assert lib.i8_embed(None, 0, None, 10, None, 768, 10, None, None, None) == w4.W4_OK

@@ -303,3 +303,59 @@ def test_embed():
     assert host(st)[0] == w4.W4_ERR_BAD_SHAPE
     assert not out[1:].any()
     assert_bits(out[0], ORC.i8_embed(bad[:1], Q, hs)[0], "valid row beside bad ids")
+
+
+# --------------------------------------------------------------------------
+# K-major (prepacked) layout and its GEMV
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("K,N", [(64, 34), (768, 2304), (3072, 768), (192, 530)])
+def test_prepack_kmajor_bit_exact(K, N):
+    note(f"prepack_kmajor K={K} N={N}")
+    W = mixed_weights(K, N, cfg=230)
+    Wq, s, z = ORC.quantize_pack(W)
+    ref = ORC.prepack_kmajor(Wq, s, z, K, N)
+    got = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    for name, a, b in zip(("Pq", "Ps", "Pz"), got, ref):
+        assert_bits(host(a), b, f"{name} {K}x{N}")
+
+
+KMAJOR_SHAPES = [(64, 16), (768, 768), (768, 2304), (3072, 768), (1024, 1008), (192, 530),
+                 (8192, 512), (128, 2), (4096, 4112), (320, 96)]
+
+
+@pytest.mark.parametrize("K,N", KMAJOR_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16])
+def test_kmajor_matmul(M, K, N):
+    note(f"kmajor M={M} K={K} N={N}")
+    W = mixed_weights(K, N, cfg=231)
+    x = synth.activations(M, K, cfg=231, slot=M, outliers=True)
+    b = synth.bias(N, cfg=231)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z, b)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y, y_ref, bound, f"kmajor M={M} {K}x{N}")
+
+
+@pytest.mark.parametrize("slot", range(4))
+@pytest.mark.parametrize("M", [1, 4])
+def test_dense38_kmajor_full_size_sampled(slot, M):
+    """Full-size 3.8B-dense shapes on the K-major path the benchmark times."""
+    K, N = synth.DENSE38_SHAPES[slot]
+    note(f"dense38 kmajor slot {slot} M={M} K={K} N={N} (sampled columns)")
+    W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=0, slot=slot)
+    x = synth.activations(M, K, cfg=synth.CFG_DENSE38, layer=0, slot=slot, outliers=True)
+    P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P))
+    pairs = sample_pairs(N, 48, seed=10 + slot)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    Wq, s, z = ORC.quantize_pack(W[:, cols])
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    assert_bound(y[:, cols], y_ref, bound, f"dense38 kmajor {K}x{N} M={M}")
+
+
+def test_kmajor_rejects_bad_shapes():
+    lib = w4.library()
+    A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
+    assert lib.w4_matmul_kmajor(A, 1, 96, A, A, A, 16, None, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE

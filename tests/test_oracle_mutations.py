@@ -68,6 +68,12 @@ MUTATIONS = {
     "head_truncates": (
         "if (s != 0.0f) qv = clamp_int(rintf(E[k * N + n] / s), -127, 127);",
         "if (s != 0.0f) qv = clamp_int(truncf(E[k * N + n] / s), -127, 127);"),
+    "prepack_scales_not_transposed": (
+        "            Ps[n * nb + b] = scales[b * N + n];",
+        "            Ps[b * N + n] = scales[b * N + n];"),
+    "prepack_codes_not_transposed": (
+        "        for (int64_t n = 0; n < N; ++n) qt[n * K + k] = q[k * N + n];",
+        "        for (int64_t n = 0; n < N; ++n) qt[k * N + n] = q[k * N + n];"),
     "embed_wrong_scale": (
         "out[t * K + k] = (float)((double)Q[k * ldq + tok] * (double)hs[tok]);",
         "out[t * K + k] = (float)((double)Q[k * ldq + tok] * (double)hs[k]);"),

@@ -9,6 +9,8 @@ functions carry the C names:
     w4_unpack(Wq, zeros, K, N)             -> (q, z)
     w4_dequantize(Wq, scales, zeros)       -> W_hat
     w4_matmul(x, Wq, scales, zeros, bias)  -> y
+    w4_prepack_kmajor(Wq, scales, zeros)   -> (Pq, Ps, Pz)  K-major copy
+    w4_matmul_kmajor(x, Pq, Ps, Pz, bias)  -> y             decode GEMV on it
     i8_quantize_head(E, ldq)               -> (Q, hs)
     i8_head_logits(x_last, Q, hs)          -> logits
     i8_embed(tokens, Q, hs)                -> rows of the dequantized table
@@ -28,7 +30,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m w4_block_dequant_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python w4_block_dequant_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -42,6 +44,9 @@ _SIGS = {
     "w4_matmul_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w4_matmul": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "w4_check_matmul_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
+    "w4_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "w4_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
+    "w4_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "i8_quantize_head": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "i8_head_workspace_bytes": (_SZ, [_I64, _I64]),
     "i8_head_logits": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
@@ -194,6 +199,44 @@ def w4_matmul(x: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, zeros: to
     _check("w4_matmul", _lib.w4_matmul(_ptr(x), M, K, _ptr(Wq), _ptr(scales), _ptr(zeros), N,
                                        _ptr(bias), _ptr(out), _ptr(ws), wsb,
                                        _stream(x.device)))
+    return out
+
+
+def w4_prepack_kmajor(Wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+    """Canonical layout -> K-major copy (Pq uint8 [N, K/2], Ps fp32 [N, K/32], Pz uint8 [N, K/64])."""
+    _dev(Wq, torch.uint8, "Wq")
+    _dev(scales, torch.float32, "scales")
+    _dev(zeros, torch.uint8, "zeros")
+    K, N = Wq.shape[0], scales.shape[1]
+    Pq = torch.empty((N, K // 2), dtype=torch.uint8, device=Wq.device)
+    Ps = torch.empty((N, K // BLOCK), dtype=torch.float32, device=Wq.device)
+    Pz = torch.empty((N, K // 64), dtype=torch.uint8, device=Wq.device)
+    _check("w4_prepack_kmajor", _lib.w4_prepack_kmajor(
+        _ptr(Wq), _ptr(scales), _ptr(zeros), K, N, _ptr(Pq), _ptr(Ps), _ptr(Pz),
+        _stream(Wq.device)))
+    return Pq, Ps, Pz
+
+
+def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: torch.Tensor,
+                     bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """y fp32 [M, N] = x [M, K] . dequantize(K-major weights) (+ bias)."""
+    _dev(x, torch.float32, "x")
+    _dev(Pq, torch.uint8, "Pq")
+    _dev(Ps, torch.float32, "Ps")
+    _dev(Pz, torch.uint8, "Pz")
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+    M, K = x.shape
+    N = Pq.shape[0]
+    if Pq.shape != (N, K // 2) or Ps.shape != (N, K // BLOCK):
+        raise ValueError("K-major weights do not match x")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, torch.float32, "out")
+    _check("w4_matmul_kmajor", _lib.w4_matmul_kmajor(
+        _ptr(x), M, K, _ptr(Pq), _ptr(Ps), _ptr(Pz), N, _ptr(bias), _ptr(out),
+        _stream(x.device)))
     return out
 
 

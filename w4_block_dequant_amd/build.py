@@ -1,6 +1,8 @@
 """Build libw4.so (the C-ABI library of include/w4.h) for gfx950 with hipcc.
 
-    python -m w4_block_dequant_amd.build
+    python w4_block_dequant_amd/build.py
+
+(run as a script: importing the package would load the library being rebuilt)
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instructions
 disabled, then linked into w4_block_dequant_amd/libw4.so (in-tree).

@@ -152,6 +152,46 @@ int w4_matmul(const float *x, int64_t M, int64_t K, const uint8_t *Wq, const flo
                                        bias, y, workspace, as_stream(stream)));
 }
 
+int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
+                      int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz, void *stream) {
+    int st = check_w4_shape(K, N);
+    if (st) return st;
+    if (K % 64 != 0) return W4_ERR_BAD_SHAPE;
+    if ((st = check_packed(Wq, scales, zeros, K, N))) return st;
+    if ((st = check_packed(Pq, Ps, Pz, K, N))) return st;
+    if (K * N == 0) return W4_OK;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_prepack_kmajor(Wq, scales, zeros, K, N, Pq, Ps, Pz, as_stream(stream)));
+}
+
+int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                const float *Ps, const uint8_t *Pz, int64_t N, const float *bias,
+                                const float *y) {
+    if (M < 0) return W4_ERR_BAD_SHAPE;
+    int st = check_w4_shape(K, N);
+    if (st) return st;
+    if (K % 64 != 0) return W4_ERR_BAD_SHAPE;
+    if (M > kMaxElems / (K > 0 ? K : 1) || M > kMaxElems / (N > 0 ? N : 1)) return W4_ERR_BAD_SHAPE;
+    if (M == 0 || N == 0) return W4_OK;
+    // the K-major kernel indexes with 32-bit offsets
+    if (K * N >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) || M * N >= ((int64_t)1 << 31))
+        return W4_ERR_BAD_SHAPE;
+    if (!need(x, M * K) || !y) return W4_ERR_NULL_PTR;
+    if ((st = check_packed(Pq, Ps, Pz, K, N))) return st;
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4)) return W4_ERR_MISALIGNED;
+    return W4_OK;
+}
+
+int w4_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
+                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *stream) {
+    int st = w4_check_matmul_kmajor_args(x, M, K, Pq, Ps, Pz, N, bias, y);
+    if (st) return st;
+    if (M == 0 || N == 0) return W4_OK;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, Pz, N, bias,
+                                           y, as_stream(stream)));
+}
+
 int i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q, float *hs,
                      int *d_status, void *stream) {
     if (K < 0 || N < 0 || ldq < N) return W4_ERR_BAD_SHAPE;

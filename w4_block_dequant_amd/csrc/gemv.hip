@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_fast(
         if (splits == 1) {
             if (n < N) y[n] = bias ? v + bias[n] : v;
         } else {
-            part[split * npad + n] = v;
+            store_partial(part + split * npad + n, v);
         }
     }
     if (splits == 1) return;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_fast(
     for (int c = tid; c < kTN; c += 64 * WAVES) {
         const int64_t n = tile * kTN + c;
         float v = 0.0f;
-        for (int64_t s = 0; s < splits; ++s) v += part[s * npad + n];
+        for (int64_t s = 0; s < splits; ++s) v += load_partial(part + s * npad + n);
         if (n < N) y[n] = bias ? v + bias[n] : v;
     }
     splitk_reset(counters + tile);

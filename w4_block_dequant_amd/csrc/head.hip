@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits(
         if (splits == 1) {
             if (n < N) logits[n] = (v * 16777216.0f) * hs[n];
         } else {
-            part[split * npad + n] = v;
+            store_partial(part + split * npad + n, v);
         }
     }
     if (splits == 1) return;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits(
     for (int c = tid; c < kTN; c += 64 * WAVES) {
         const int64_t n = tile * kTN + c;
         float v = 0.0f;
-        for (int64_t s = 0; s < splits; ++s) v += part[s * npad + n];
+        for (int64_t s = 0; s < splits; ++s) v += load_partial(part + s * npad + n);
         if (n < N) logits[n] = (v * 16777216.0f) * hs[n];
     }
     splitk_reset(counters + tile);

@@ -1,0 +1,258 @@
+// K-major ("prepacked") layout of the 4-bit format, and the decode GEMV on it.
+//
+// The page ("ONNX export, quantization and the browser runtime", section
+// "Quantization") stores each weight as a plain [K, N] UINT4 constant with a
+// blocked DequantizeLinear, and mentions the runtime's weight "prepacking".
+// Here prepacking is a byte-exact reordering of the same format so that the
+// data of one output column is contiguous:
+//   Pq uint8 [N, K/2]   codes of column n, pairs along K (low nibble = even k)
+//   Ps fp32  [N, K/32]  the column's block scales
+//   Pz uint8 [N, K/64]  the column's zero points, pairs of blocks per byte
+// The bytes per weight are unchanged (0.640625 B).
+//
+// GEMV on this layout: a workgroup owns a few whole columns, so no partial
+// sums leave it (no split-K across workgroups, no atomics, no workspace).
+// A lane owns one 32-row block of a column: one 16-byte load of codes, one
+// scale, one zero point, and the 32 activations of that block (held in
+// registers across all the workgroup's columns).  64 lanes read 1 KB of one
+// column contiguously.  Per packed word: 1 shift, 4 masks, 4 packed-fp16
+// subtractions (q - z as exact fp16 subnormals) and 8 v_fma_mix_f32.  The
+// per-lane block sums are scaled, then summed over the column's lanes in a
+// fixed order through LDS, so results are deterministic.
+#include "common.h"
+#include "launch.h"
+
+namespace w4 {
+namespace {
+
+// Relayout, one thread per (column pair j, k pair i): reads the two packed
+// bytes Wq[2i, j], Wq[2i+1, j] (columns 2j, 2j+1) and writes Pq[2j, i] and
+// Pq[2j+1, i].  Consecutive threads take consecutive i (coalesced writes).
+__global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t *__restrict__ Wq, int64_t K,
+                                                       int64_t N, uint8_t *__restrict__ Pq) {
+    const int64_t hk = K / 2, half = N / 2;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= hk * half) return;
+    const int64_t j = t / hk, i = t - j * hk;
+    const uint8_t a = Wq[(2 * i) * half + j];      // row 2i: columns 2j (low), 2j+1 (high)
+    const uint8_t b = Wq[(2 * i + 1) * half + j];  // row 2i+1
+    Pq[(2 * j) * hk + i] = (uint8_t)((a & 15) | ((b & 15) << 4));
+    Pq[(2 * j + 1) * hk + i] = (uint8_t)((a >> 4) | (b & 0xF0));
+}
+
+// Scales and zero points, one thread per (column pair j, block pair c).
+__global__ __launch_bounds__(256) void k_prepack_blocks(const float *__restrict__ scales,
+                                                        const uint8_t *__restrict__ zeros,
+                                                        int64_t K, int64_t N,
+                                                        float *__restrict__ Ps,
+                                                        uint8_t *__restrict__ Pz) {
+    const int64_t NB = K / kBlock, half = N / 2, hb = NB / 2;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= hb * half) return;
+    const int64_t j = t / hb, c = t - j * hb;
+    const int64_t b0 = 2 * c, b1 = 2 * c + 1;
+    const uint8_t z0 = zeros[b0 * half + j], z1 = zeros[b1 * half + j];
+    Pz[(2 * j) * hb + c] = (uint8_t)((z0 & 15) | ((z1 & 15) << 4));
+    Pz[(2 * j + 1) * hb + c] = (uint8_t)((z0 >> 4) | (z1 & 0xF0));
+    Ps[(2 * j) * NB + b0] = scales[b0 * N + 2 * j];
+    Ps[(2 * j) * NB + b1] = scales[b1 * N + 2 * j];
+    Ps[(2 * j + 1) * NB + b0] = scales[b0 * N + 2 * j + 1];
+    Ps[(2 * j + 1) * NB + b1] = scales[b1 * N + 2 * j + 1];
+}
+
+// acc[r] += x_r[k] * (q[k] - z) over the 8 codes k = 8d .. 8d+7 of one word,
+// for MR activation rows.  Even k land in accE (units 2^-24), odd k in accO
+// (units 2^-20); see common.h for the subnormal encoding.
+template <int MR>
+__device__ __forceinline__ void fma_kword(uint32_t v, half2_t zE, half2_t zO,
+                                          const float (*xr)[kBlock], int d, float (*accE)[2],
+                                          float (*accO)[2]) {
+    const uint32_t hi = v >> 8;
+    const half2_t e0 = as_half2(v & 0x000F000Fu) - zE;   // k = 8d+0, 8d+4
+    const half2_t o0 = as_half2(v & 0x00F000F0u) - zO;   // k = 8d+1, 8d+5
+    const half2_t e1 = as_half2(hi & 0x000F000Fu) - zE;  // k = 8d+2, 8d+6
+    const half2_t o1 = as_half2(hi & 0x00F000F0u) - zO;  // k = 8d+3, 8d+7
+    const int k = 8 * d;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        accE[r][0] = __builtin_fmaf(xr[r][k + 0], (float)e0.x, accE[r][0]);
+        accE[r][1] = __builtin_fmaf(xr[r][k + 4], (float)e0.y, accE[r][1]);
+        accO[r][0] = __builtin_fmaf(xr[r][k + 1], (float)o0.x, accO[r][0]);
+        accO[r][1] = __builtin_fmaf(xr[r][k + 5], (float)o0.y, accO[r][1]);
+        accE[r][0] = __builtin_fmaf(xr[r][k + 2], (float)e1.x, accE[r][0]);
+        accE[r][1] = __builtin_fmaf(xr[r][k + 6], (float)e1.y, accE[r][1]);
+        accO[r][0] = __builtin_fmaf(xr[r][k + 3], (float)o1.x, accO[r][0]);
+        accO[r][1] = __builtin_fmaf(xr[r][k + 7], (float)o1.y, accO[r][1]);
+    }
+}
+
+// One workgroup: columns n0 .. n0 + CC - 1 (CC = G * P), MR rows of x
+// starting at row m0 = blockIdx.y * MR.  Lane L = (g, bl): column slot
+// g = L / NBL and block bl, then bl + NBL, ... while < NB.  Pass p covers
+// column n0 + p * G + g.  Offsets are 32-bit (the host keeps every array
+// below 2^31 bytes).  CHECK clamps columns past N (ragged last workgroup);
+// without it every load is unconditional, so the compiler can start on
+// pass 0 while later passes are still in flight.
+template <int MR, int P, bool CHECK>
+__global__ __launch_bounds__(256) void k_gemv_kmajor(
+    const float *__restrict__ x, int M, int K, const uint8_t *__restrict__ Pq,
+    const float *__restrict__ Ps, const uint8_t *__restrict__ Pz, int N,
+    const float *__restrict__ bias, float *__restrict__ y, int G, int NBL, int ch) {
+    extern __shared__ float red[];  // [MR][CC][NBL], then [MR][CC][NBL / ch]
+    const int L = threadIdx.x;
+    const int g = L / NBL, bl = L - g * NBL;
+    const int NB = K / kBlock, hk = K / 2;
+    const int CC = G * P;
+    const int n0 = blockIdx.x * CC;
+    const int m0 = blockIdx.y * MR;
+
+    float part[MR][P];
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int p = 0; p < P; ++p) part[r][p] = 0.0f;
+
+    if (g < G) {
+        for (int b = bl; b < NB; b += NBL) {
+            // activations of this block, for each of the MR rows
+            float xr[MR][kBlock];
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const int m = min(m0 + r, M - 1);
+                const f32x4_t *xp = reinterpret_cast<const f32x4_t *>(x + (size_t)m * K + b * kBlock);
+#pragma unroll
+                for (int i = 0; i < kBlock / 4; ++i) {
+                    const f32x4_t v = xp[i];
+                    xr[r][4 * i + 0] = v.x;
+                    xr[r][4 * i + 1] = v.y;
+                    xr[r][4 * i + 2] = v.z;
+                    xr[r][4 * i + 3] = v.w;
+                }
+            }
+            // codes, scale and zero point of this block, for each pass's column
+            u32x4_t w[P];
+            float s[P];
+            uint32_t zb[P];
+            const int nf = n0 + g;  // this lane's column in pass 0
+            uint32_t oq = (uint32_t)(nf * hk + 16 * b);
+            uint32_t os = (uint32_t)(nf * NB + b);
+            uint32_t oz = (uint32_t)(nf * (NB / 2) + (b >> 1));
+            const uint32_t sq = (uint32_t)(G * hk), ss = (uint32_t)(G * NB),
+                           sz = (uint32_t)(G * (NB / 2));
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                uint32_t q_off = oq, s_off = os, z_off = oz;
+                if (CHECK && n0 + p * G + g >= N) {  // past the last column: re-read it
+                    const int nl = N - 1;
+                    q_off = (uint32_t)(nl * hk + 16 * b);
+                    s_off = (uint32_t)(nl * NB + b);
+                    z_off = (uint32_t)(nl * (NB / 2) + (b >> 1));
+                }
+                w[p] = load_stream<u32x4_t>(Pq + q_off);
+                s[p] = Ps[s_off];
+                zb[p] = Pz[z_off];
+                oq += sq;
+                os += ss;
+                oz += sz;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // every load in flight before the arithmetic
+            const int zsh = (b & 1) * 4;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const uint32_t z = (zb[p] >> zsh) & 15;
+                const half2_t zE = as_half2(z * 0x00010001u);
+                const half2_t zO = as_half2((z << 4) * 0x00010001u);
+                float accE[MR][2], accO[MR][2];
+#pragma unroll
+                for (int r = 0; r < MR; ++r) accE[r][0] = accE[r][1] = accO[r][0] = accO[r][1] = 0.0f;
+                fma_kword<MR>(w[p].x, zE, zO, xr, 0, accE, accO);
+                fma_kword<MR>(w[p].y, zE, zO, xr, 1, accE, accO);
+                fma_kword<MR>(w[p].z, zE, zO, xr, 2, accE, accO);
+                fma_kword<MR>(w[p].w, zE, zO, xr, 3, accE, accO);
+#pragma unroll
+                for (int r = 0; r < MR; ++r) {
+                    const float t = __builtin_fmaf(accO[r][0] + accO[r][1], 1048576.0f,
+                                                   (accE[r][0] + accE[r][1]) * 16777216.0f);
+                    part[r][p] = __builtin_fmaf(s[p], t, part[r][p]);
+                }
+            }
+        }
+    }
+
+    // lane partials -> LDS as [MR][CC][NBL]; column c = p * G + g
+    if (g < G) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int p = 0; p < P; ++p) red[(r * CC + p * G + g) * NBL + bl] = part[r][p];
+    }
+    __syncthreads();
+    // stage 1: chunks of `ch` consecutive partials (ch divides NBL), in order
+    const int total = MR * CC * NBL;
+    float *red2 = red + total;
+    for (int i = L; i * ch < total; i += blockDim.x) {
+        float v = 0.0f;
+        for (int j = 0; j < ch; ++j) v += red[i * ch + j];
+        red2[i] = v;
+    }
+    __syncthreads();
+    // stage 2: one thread per column, rows in turn; chunk sums in order
+    const int npc = NBL / ch;
+    if (L < CC) {
+        const int n = n0 + L;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            float v = 0.0f;
+            for (int j = 0; j < npc; ++j) v += red2[(r * CC + L) * npc + j];
+            const int m = m0 + r;
+            if (n < N && m < M) y[(size_t)m * N + n] = bias ? v + bias[n] : v;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                                 int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz,
+                                 hipStream_t stream) {
+    const int64_t t1 = (K / 2) * (N / 2), t2 = (K / 64) * (N / 2);
+    if (t1 > 0)
+        hipLaunchKernelGGL(k_prepack_codes, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
+                           Wq, K, N, Pq);
+    if (t2 > 0)
+        hipLaunchKernelGGL(k_prepack_blocks, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0,
+                           stream, scales, zeros, K, N, Ps, Pz);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, int64_t K,
+                              const uint8_t *Pq, const float *Ps, const uint8_t *Pz, int64_t N,
+                              const float *bias, float *y, hipStream_t stream) {
+    if (p.kind == KmajorPlan::kEmpty) return hipSuccess;
+    if (p.kind == KmajorPlan::kBiasOnly) return launch_bias_fill(bias, M, N, y, stream);
+    const int64_t C = (int64_t)p.groups * p.passes;
+    const dim3 grid((unsigned)((N + C - 1) / C), (unsigned)((M + p.rows - 1) / p.rows));
+    const int64_t cells = (int64_t)p.rows * C * p.lanes_per_col;
+    const size_t shm = (size_t)(cells + cells / p.chunk) * sizeof(float);
+    const bool check = (N % C) != 0;
+#define W4_KM_CASE(MRV, PV)                                                                     \
+    if (p.rows == MRV && p.passes == PV) {                                                      \
+        if (check)                                                                              \
+            hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, true>), grid, dim3(p.threads), shm, stream, \
+                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups,         \
+                               p.lanes_per_col, p.chunk);                                       \
+        else                                                                                    \
+            hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, false>), grid, dim3(p.threads), shm,      \
+                               stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups, \
+                               p.lanes_per_col, p.chunk);                                       \
+        return hipGetLastError();                                                               \
+    }
+    W4_KM_CASE(1, 1) W4_KM_CASE(1, 2) W4_KM_CASE(1, 3) W4_KM_CASE(1, 4)
+    W4_KM_CASE(1, 6) W4_KM_CASE(1, 8)
+    W4_KM_CASE(2, 1) W4_KM_CASE(2, 2) W4_KM_CASE(2, 4)
+    W4_KM_CASE(4, 1) W4_KM_CASE(4, 2)
+#undef W4_KM_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace w4

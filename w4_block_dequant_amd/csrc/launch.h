@@ -25,6 +25,13 @@ hipError_t launch_small_m(const SmallMPlan &plan, const float *x, int64_t M, int
                           int64_t N, const float *bias, float *y, void *workspace,
                           hipStream_t stream);
 
+hipError_t launch_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
+                                 int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz,
+                                 hipStream_t stream);
+hipError_t launch_gemv_kmajor(const KmajorPlan &plan, const float *x, int64_t M, int64_t K,
+                              const uint8_t *Pq, const float *Ps, const uint8_t *Pz, int64_t N,
+                              const float *bias, float *y, hipStream_t stream);
+
 hipError_t launch_bias_fill(const float *bias, int64_t M, int64_t N, float *y,
                             hipStream_t stream);
 

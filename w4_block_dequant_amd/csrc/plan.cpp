@@ -93,7 +93,83 @@ SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N) {
         p.kind = SmallMPlan::kBiasOnly;
         return p;
     }
-    p.kind = SmallMPlan::kGeneric;
+    if (N % 8 != 0) {
+        p.kind = SmallMPlan::kGeneric;
+        return p;
+    }
+    static const int64_t env_wgs = env_int("W4_MFMA_TARGET_WGS");
+    const int64_t target = env_wgs > 0 ? env_wgs : 512;
+    p.kind = SmallMPlan::kMfma;
+    p.mgroups = cdiv(M, 64);
+    p.mtiles = cdiv(M < 64 ? M : 64, 16);
+    p.tiles = cdiv(N, 256);
+    p.npad = p.tiles * 256;
+    const int64_t NB = K / 32;
+    int64_t splits = cdiv(target, p.tiles * p.mgroups);
+    if (splits > NB) splits = NB;
+    if (splits < 1) splits = 1;
+    p.blocks_per_wg = cdiv(NB, splits);
+    p.splits = cdiv(NB, p.blocks_per_wg);
+    p.workspace = p.splits > 1 ? align_up((size_t)p.tiles * p.mgroups * 4, kCounterAlign) +
+                                     (size_t)p.splits * M * p.npad * 4
+                               : 0;
+    return p;
+}
+
+KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N) {
+    KmajorPlan p{};
+    if (N == 0 || M == 0) {
+        p.kind = KmajorPlan::kEmpty;
+        return p;
+    }
+    if (K == 0) {
+        p.kind = KmajorPlan::kBiasOnly;
+        return p;
+    }
+    p.kind = KmajorPlan::kRun;
+    p.rows = M >= 4 ? 4 : (M >= 2 ? (M == 2 ? 2 : 4) : 1);
+    const int64_t NB = K / 32;
+    // the smallest workgroup whose lanes split evenly into whole columns of blocks
+    int threads = 0;
+    for (int w = 1; w <= 4; ++w)
+        if ((64 * w) % NB == 0) {
+            threads = 64 * w;
+            break;
+        }
+    if (threads) {
+        p.threads = threads;
+        // a column needs at least `rows` lanes for the final per-output sums;
+        // for very short K the extra lanes idle (NB < 4 only)
+        int lanes = (int)NB;
+        while (lanes < p.rows) lanes *= 2;
+        p.lanes_per_col = lanes;
+        p.groups = threads / lanes;
+    } else {  // no exact fit within 256 lanes: one column slot, lanes loop over blocks
+        const int64_t lanes = NB < 256 ? NB : 256;
+        p.threads = (int)(cdiv(lanes, 64) * 64);
+        p.lanes_per_col = p.threads;
+        p.groups = 1;
+    }
+    static const int64_t env_p = env_int("W4_KMAJOR_PASSES");
+    static const int allowed1[] = {8, 6, 4, 3, 2, 1};
+    static const int allowed2[] = {4, 2, 1};
+    static const int allowed4[] = {2, 1};
+    const int *allowed = p.rows == 1 ? allowed1 : p.rows == 2 ? allowed2 : allowed4;
+    const int nallowed = p.rows == 1 ? 6 : p.rows == 2 ? 3 : 2;
+    // enough workgroups to fill the chip: about 512 column groups
+    const int64_t want = env_p > 0 ? env_p : N / ((int64_t)p.groups * 512);
+    p.passes = 1;
+    for (int i = 0; i < nallowed; ++i)
+        if (allowed[i] <= want && p.rows * allowed[i] <= p.lanes_per_col) {
+            p.passes = allowed[i];
+            break;
+        }
+    p.chunk = 1;
+    for (int c : {8, 4, 2})
+        if (p.lanes_per_col % c == 0) {
+            p.chunk = c;
+            break;
+        }
     return p;
 }
 

@@ -48,9 +48,12 @@ struct HeadPlan {
 HeadPlan plan_head(int64_t K, int64_t N);
 
 // ---- small-M matmul (M > 1) ----------------------------------------------
+// A workgroup (4 waves) owns a 256-column tile, up to 64 rows of M (1..4
+// MFMA m-tiles) and `blocks_per_wg` K-blocks; `mgroups` = ceil(M / 64).
 struct SmallMPlan {
     enum Kind { kEmpty = 0, kBiasOnly = 1, kMfma = 2, kGeneric = 3 } kind;
-    int64_t mtiles = 0;         // 16-row tiles of M handled per workgroup pass
+    int64_t mtiles = 0;         // 16-row MFMA tiles per workgroup (1..4)
+    int64_t mgroups = 1;        // 64-row groups of M
     int64_t tiles = 0;          // column tiles
     int64_t splits = 1;
     int64_t blocks_per_wg = 0;
@@ -59,5 +62,18 @@ struct SmallMPlan {
 };
 
 SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N);
+
+// ---- matmul on the K-major (prepacked) layout -------------------------------
+// A workgroup of `threads` lanes holds `groups` column slots of
+// `lanes_per_col` lanes; lane (slot, b) owns K-block b of its column.  The
+// workgroup runs `passes` columns per slot (groups * passes columns in all)
+// for `rows` rows of x; grid = ceil(N / columns) x ceil(M / rows).
+struct KmajorPlan {
+    enum Kind { kEmpty = 0, kBiasOnly = 1, kRun = 2 } kind;
+    int rows = 1, passes = 1, groups = 1, lanes_per_col = 64, threads = 64;
+    int chunk = 1;  // partials summed per thread in the first reduction stage
+};
+
+KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N);
 
 }  // namespace w4

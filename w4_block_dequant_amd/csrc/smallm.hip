@@ -1,6 +1,23 @@
-// M > 1: the small-M path (prefill rows, batched decode).
+// M > 1 (prefill rows, batched decode): dequantize to LDS, then fp32 MFMA.
+//
+// The method (page "ONNX export, quantization and the browser runtime",
+// section "Quantization", steps 1-2, and the runtime paragraph after them)
+// computes Y = X . W_hat + bias in fp32 with W_hat = (q - z) * scale.  With
+// M >= 16 rows the product is a dense contraction, so it runs on
+// v_mfma_f32_16x16x4_f32 (true fp32: no reduced-precision inputs).
+//
+// A workgroup (4 waves) owns a 256-column tile and a range of K-blocks.  Per
+// 32-row block every thread loads 4 rows x 8 columns of packed codes (rows of
+// 128 contiguous bytes across 32 threads), dequantizes them exactly --
+// (q - z) as an fp16-subnormal pair, times scale * 2^24 in one v_fma_mix,
+// i.e. fl32((q - z) * scale), the same value the oracle forms -- and stores
+// the fp32 tile in one of two LDS buffers.  After one barrier each wave runs
+// its 64 columns (4 MFMA n-tiles) against up to 4 MFMA m-tiles of X, reading
+// its B operands with ds_read_b128, while the next block's loads are in
+// flight.  Split-K partials combine as in the GEMV (splitk.h).
 #include "common.h"
 #include "launch.h"
+#include "splitk.h"
 
 namespace w4 {
 
@@ -8,19 +25,217 @@ hipError_t launch_matmul_generic(const float *x, int64_t M, int64_t K, const uin
                                  const float *scales, const uint8_t *zeros, int64_t N,
                                  const float *bias, float *y, hipStream_t stream);
 
+namespace {
+
+constexpr int kTN = 256;     // columns per workgroup tile
+constexpr int kRowsPad = 256;  // LDS row stride (floats)
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Operand layout of v_mfma_f32_16x16x4_f32 (one 16x16 block):
+//   A (16 x 4): lane l holds A[l % 16][l / 16]
+//   B (4 x 16): lane l holds B[l / 16][l % 16]
+//   D (16 x 16): lane l, register v holds D[4 * (l / 16) + v][l % 16]
+// The k index of A and B only has to agree per lane group, so lane group kq
+// at step t stands for block row 8 * kq + t.
+template <int MT>
+__global__ __launch_bounds__(256) void k_mm_mfma(
+    const float *__restrict__ x, int64_t M, int64_t K, const uint8_t *__restrict__ Wq,
+    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int64_t N,
+    const float *__restrict__ bias, float *__restrict__ y, int64_t tiles, int64_t splits,
+    int64_t bpw, int64_t npad, float *__restrict__ part, unsigned *__restrict__ counters) {
+    __shared__ float Ws[2][kBlock * kRowsPad];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int kq = lane >> 4, c = lane & 15;
+    const int64_t mgroups = (M + 63) / 64;
+    const int64_t wg = blockIdx.x;
+    const int64_t tile = wg % tiles;
+    const int64_t split = (wg / tiles) % splits;
+    const int64_t mg = wg / (tiles * splits);
+    const int64_t n0 = tile * kTN;
+    const int64_t m0 = mg * 64;
+    const int64_t NB = K / kBlock;
+    const int64_t b_begin = split * bpw;
+    const int64_t b_end = min(b_begin + bpw, NB);
+    const int64_t half = N / 2;
+
+    // loader role: 8 columns (4 packed bytes) x 4 rows
+    const int li = tid & 31, lg = tid >> 5;
+    const int64_t lcol = n0 + 8 * li;
+    const bool lok = lcol < N;
+
+    uint32_t wreg[4];
+    f32x4_t sreg[2];
+    uint32_t zreg;
+    auto load_block = [&](int64_t b) {
+        if (lok) {
+            const uint8_t *wp = Wq + (b * kBlock + 4 * lg) * half + lcol / 2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wreg[r] = load_stream<uint32_t>(wp + r * half);
+            const float *sp = scales + b * N + lcol;
+            sreg[0] = *reinterpret_cast<const f32x4_t *>(sp);
+            sreg[1] = *reinterpret_cast<const f32x4_t *>(sp + 4);
+            zreg = *reinterpret_cast<const uint32_t *>(zeros + b * half + lcol / 2);
+        }
+    };
+    auto store_block = [&](float *buf) {
+        f32x4_t o[4][2];
+        if (lok) {
+            const NibblePairs zp = nibble_pairs(zreg);
+            float su[8];  // scale * 2^24 or 2^20, matching each column's subnormal unit
+#pragma unroll
+            for (int j = 0; j < 8; ++j) su[j] = sreg[j >> 2][j & 3] * nibble_unscale(j);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const NibblePairs qp = nibble_pairs(wreg[r]);
+                float w[8];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const half2_t d = qp.p[m] - zp.p[m];
+                    w[m] = (float)d.x * su[m];
+                    w[m + 4] = (float)d.y * su[m + 4];
+                }
+                o[r][0] = f32x4_t{w[0], w[1], w[2], w[3]};
+                o[r][1] = f32x4_t{w[4], w[5], w[6], w[7]};
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r][0] = o[r][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float *dst = buf + (4 * lg + r) * kRowsPad + 8 * li;
+            *reinterpret_cast<f32x4_t *>(dst) = o[r][0];
+            *reinterpret_cast<f32x4_t *>(dst + 4) = o[r][1];
+        }
+    };
+
+    f32x4v acc[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+    if (b_begin < b_end) load_block(b_begin);
+    int buf = 0;
+    for (int64_t b = b_begin; b < b_end; ++b) {
+        store_block(Ws[buf]);
+        __syncthreads();
+        if (b + 1 < b_end) load_block(b + 1);
+
+        // A operands: X[m0 + 16 mt + c][32 b + 8 kq + t], t = 0..7
+        f32x4_t xa[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int64_t m = m0 + 16 * mt + c;
+            if (m < M) {
+                const float *xp = x + m * K + b * kBlock + 8 * kq;
+                xa[mt][0] = *reinterpret_cast<const f32x4_t *>(xp);
+                xa[mt][1] = *reinterpret_cast<const f32x4_t *>(xp + 4);
+            } else {
+                xa[mt][0] = xa[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        const float *bs = Ws[buf] + 64 * wave + 4 * c;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t *>(bs + (8 * kq + t) * kRowsPad);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float a = xa[mt][t >> 2][t & 3];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv[nt], acc[mt][nt], 0, 0, 0);
+            }
+        }
+        buf ^= 1;
+    }
+
+    // lane holds D[4 kq + v][c] of each (mt, nt): row m0 + 16 mt + 4 kq + v,
+    // column n0 + 64 wave + 4 c + nt
+    const int64_t rows = min((int64_t)64, M - m0);
+    if (splits == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int64_t n = n0 + 64 * wave + 4 * c + nt;
+                if (n >= N) continue;
+                const float bn = bias ? bias[n] : 0.0f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t mr = 16 * mt + 4 * kq + v;
+                    if (mr < rows) y[(m0 + mr) * N + n] = acc[mt][nt][v] + bn;
+                }
+            }
+        return;
+    }
+    // partials: part[split][m0 + mr][n] with row stride npad
+    float *pp = part + split * (M * npad);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int64_t n = n0 + 64 * wave + 4 * c + nt;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t mr = 16 * mt + 4 * kq + v;
+                if (mr < rows) store_partial(pp + (m0 + mr) * npad + n, acc[mt][nt][v]);
+            }
+        }
+    unsigned *cnt = counters + mg * tiles + tile;
+    if (!splitk_arrive(cnt, splits)) return;
+    for (int64_t e = tid; e < rows * kTN; e += 256) {
+        const int64_t mr = e / kTN, n = n0 + (e % kTN);
+        if (n >= N) continue;
+        float v = 0.0f;
+        for (int64_t s = 0; s < splits; ++s)
+            v += load_partial(part + s * (M * npad) + (m0 + mr) * npad + n);
+        y[(m0 + mr) * N + n] = bias ? v + bias[n] : v;
+    }
+    splitk_reset(cnt);
+}
+
+}  // namespace
+
 hipError_t launch_small_m(const SmallMPlan &p, const float *x, int64_t M, int64_t K,
                           const uint8_t *Wq, const float *scales, const uint8_t *zeros,
                           int64_t N, const float *bias, float *y, void *workspace,
                           hipStream_t stream) {
-    (void)workspace;
     switch (p.kind) {
     case SmallMPlan::kEmpty:
         return hipSuccess;
     case SmallMPlan::kBiasOnly:
         return launch_bias_fill(bias, M, N, y, stream);
-    default:
+    case SmallMPlan::kGeneric:
         return launch_matmul_generic(x, M, K, Wq, scales, zeros, N, bias, y, stream);
+    case SmallMPlan::kMfma:
+        break;
     }
+    unsigned *counters = static_cast<unsigned *>(workspace);
+    float *part = p.splits > 1 ? reinterpret_cast<float *>(
+                                     static_cast<char *>(workspace) +
+                                     align_up((size_t)p.tiles * p.mgroups * 4, kCounterAlign))
+                               : nullptr;
+    const dim3 grid((unsigned)(p.tiles * p.splits * p.mgroups));
+#define W4_MFMA_CASE(MTV)                                                                       \
+    case MTV:                                                                                   \
+        hipLaunchKernelGGL(k_mm_mfma<MTV>, grid, dim3(256), 0, stream, x, M, K, Wq, scales,      \
+                           zeros, N, bias, y, p.tiles, p.splits, p.blocks_per_wg, p.npad, part,  \
+                           counters);                                                           \
+        break;
+    switch (p.mtiles) {
+        W4_MFMA_CASE(1)
+        W4_MFMA_CASE(2)
+        W4_MFMA_CASE(3)
+        W4_MFMA_CASE(4)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef W4_MFMA_CASE
+    return hipGetLastError();
 }
 
 }  // namespace w4
