@@ -110,10 +110,10 @@ int w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
  * 1e-5 * (sum_k |x[m, k] * w_hat[k, n]| + |bias[n]|) + 1e-6 of the exact
  * value.  M == 1 runs the fused dequant-GEMV; M > 1 runs the dequant-to-LDS
  * fp32-MFMA kernel.  Results are deterministic (no floating-point atomics).
- * bias may be NULL.  The workspace holds split-K partial sums and per-tile
- * arrival counters: it must be at least w4_matmul_workspace_bytes(M, K, N)
- * bytes, zero-filled once when first allocated; every call leaves its
- * counters at zero again, so the same workspace serves any later call.
+ * bias may be NULL.  Where K is split across workgroups, their partial sums
+ * go to the caller's workspace (at least w4_matmul_workspace_bytes(M, K, N)
+ * bytes, 256-byte aligned, any contents) and a second kernel on the same
+ * stream adds them in a fixed order; a size of 0 means no workspace is used.
  * ------------------------------------------------------------------------- */
 size_t w4_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
 

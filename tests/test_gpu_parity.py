@@ -241,18 +241,21 @@ def test_matmul_one_hot_rows_are_dequantized_rows():
         assert_bits(y[0], What[k], f"one-hot row {k}")
 
 
-def test_matmul_deterministic_and_workspace_clean():
+def test_matmul_deterministic_with_dirty_workspace():
+    """Repeated calls give identical bits; the workspace needs no initial contents."""
     K, N = 3072, 9216
     W = synth.weights(K, N, cfg=214)
     x = dev(synth.activations(1, K, cfg=214))
     Wd = w4.w4_quantize_pack(dev(W))
     need = w4.w4_matmul_workspace_bytes(1, K, N)
-    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    assert need > 0
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)   # garbage: NaN-ish floats
     y1 = host(w4.w4_matmul(x, *Wd, workspace=ws))
     y2 = host(w4.w4_matmul(x, *Wd, workspace=ws))
     assert_bits(y1, y2, "repeat")
-    tiles = (N + 255) // 256
-    assert not host(ws[: tiles * 4]).any(), "arrival counters must return to zero"
+    Wq, s, z = (host(t) for t in Wd)
+    y_ref, bound = ORC.w4_matmul(host(x), Wq, s, z)
+    assert_bound(y1, y_ref, bound, "dirty workspace")
 
 
 def test_matmul_rejects_bad_device_pointers():

@@ -105,10 +105,9 @@ def _stream(device) -> int:
 
 
 class Workspace:
-    """Zero-filled device scratch for the split-K kernels, grown on demand.
+    """Device scratch for the split-K partial sums, grown on demand.
 
-    The kernels leave their arrival counters at zero, so one buffer serves
-    every later call ordered on the same stream.
+    One buffer per device serves every call ordered on the same stream.
     """
 
     def __init__(self):
@@ -123,7 +122,7 @@ class Workspace:
             buf = self._buf.get(key)
             if buf is None or buf.numel() < nbytes:
                 size = max(nbytes, 1 << 20)
-                buf = torch.zeros(size, dtype=torch.uint8, device=device)
+                buf = torch.empty(size, dtype=torch.uint8, device=device)
                 self._buf[key] = buf
         return buf, buf.numel()
 

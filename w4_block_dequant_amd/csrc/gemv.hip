@@ -10,8 +10,8 @@
 // (see common.h): each x * (q - z) product is exact and rounded once into
 // fp32.  At the end of a block each column's sum is multiplied by its scale.
 // Lane groups and waves that worked on other K-blocks of the same columns
-// are summed through LDS, and workgroups along K through the workspace
-// (splitk.h), both in a fixed order.
+// are summed through LDS; workgroups along K write partial sums to the
+// workspace, which a second kernel adds in split order (splitk.h).
 #include "common.h"
 #include "launch.h"
 #include "splitk.h"
@@ -28,7 +28,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_fast(
     const float *__restrict__ x, const uint8_t *__restrict__ Wq, const float *__restrict__ scales,
     const uint8_t *__restrict__ zeros, const float *__restrict__ bias, float *__restrict__ y,
     int64_t NB, int64_t N, int64_t tiles, int64_t splits, int64_t bpw, int64_t npad,
-    float *__restrict__ part, unsigned *__restrict__ counters) {
+    float *__restrict__ part) {
     constexpr int SLOTS = WAVES * kGemvGroups;
     __shared__ float red[SLOTS * kTN];
 
@@ -94,18 +94,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_fast(
         if (splits == 1) {
             if (n < N) y[n] = bias ? v + bias[n] : v;
         } else {
-            store_partial(part + split * npad + n, v);
+            part[split * npad + n] = v;
         }
     }
-    if (splits == 1) return;
-    if (!splitk_arrive(counters + tile, splits)) return;
-    for (int c = tid; c < kTN; c += 64 * WAVES) {
-        const int64_t n = tile * kTN + c;
-        float v = 0.0f;
-        for (int64_t s = 0; s < splits; ++s) v += load_partial(part + s * npad + n);
-        if (n < N) y[n] = bias ? v + bias[n] : v;
-    }
-    splitk_reset(counters + tile);
 }
 
 // Any even N and any M: one thread per (row m, column pair j), sequential
@@ -187,16 +178,14 @@ hipError_t launch_gemv(const GemvPlan &p, const float *x, int64_t K, const uint8
     case GemvPlan::kFast:
         break;
     }
-    unsigned *counters = static_cast<unsigned *>(workspace);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                            align_up((size_t)p.tiles * 4, kCounterAlign));
+    float *part = static_cast<float *>(workspace);
     const dim3 grid((unsigned)(p.tiles * p.splits));
     const int64_t NB = K / kBlock;
 #define W4_GEMV_CASE(WV)                                                                        \
     case WV:                                                                                    \
         hipLaunchKernelGGL(k_gemv_fast<WV>, grid, dim3(64 * WV), 0, stream, x, Wq, scales,       \
                            zeros, bias, y, NB, N, p.tiles, p.splits, p.blocks_per_wg, p.npad,    \
-                           part, counters);                                                     \
+                           part);                                                               \
         break;
     switch (p.waves) {
         W4_GEMV_CASE(1)
@@ -206,7 +195,9 @@ hipError_t launch_gemv(const GemvPlan &p, const float *x, int64_t K, const uint8
         return hipErrorInvalidValue;
     }
 #undef W4_GEMV_CASE
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_reduce(part, p.splits, 1, N, p.npad, bias, nullptr, 1.0f, y, stream);
 }
 
 }  // namespace w4

@@ -139,8 +139,7 @@ template <int WAVES, bool ALIGNED>
 __global__ __launch_bounds__(64 * WAVES) void k_head_logits(
     const float *__restrict__ x, int64_t K, const int8_t *__restrict__ Q, int64_t ldq,
     const float *__restrict__ hs, int64_t N, float *__restrict__ logits, int64_t tiles,
-    int64_t splits, int64_t rows_per_wg, int64_t npad, float *__restrict__ part,
-    unsigned *__restrict__ counters) {
+    int64_t splits, int64_t rows_per_wg, int64_t npad, float *__restrict__ part) {
     constexpr int SLOTS = WAVES * kGemvGroups;
     extern __shared__ float smem[];
     float *red = smem;                    // [SLOTS * kTN]
@@ -206,18 +205,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits(
         if (splits == 1) {
             if (n < N) logits[n] = (v * 16777216.0f) * hs[n];
         } else {
-            store_partial(part + split * npad + n, v);
+            part[split * npad + n] = v;
         }
     }
-    if (splits == 1) return;
-    if (!splitk_arrive(counters + tile, splits)) return;
-    for (int c = tid; c < kTN; c += 64 * WAVES) {
-        const int64_t n = tile * kTN + c;
-        float v = 0.0f;
-        for (int64_t s = 0; s < splits; ++s) v += load_partial(part + s * npad + n);
-        if (n < N) logits[n] = (v * 16777216.0f) * hs[n];
-    }
-    splitk_reset(counters + tile);
 }
 
 }  // namespace
@@ -245,11 +235,7 @@ hipError_t launch_head_logits(const HeadPlan &p, const float *x, int64_t K, cons
                               void *workspace, hipStream_t stream) {
     if (p.kind == HeadPlan::kEmpty) return hipSuccess;
     if (p.kind == HeadPlan::kZero) return launch_bias_fill(nullptr, 1, N, logits, stream);
-    unsigned *counters = static_cast<unsigned *>(workspace);
-    float *part = p.splits > 1 ? reinterpret_cast<float *>(
-                                     static_cast<char *>(workspace) +
-                                     align_up((size_t)p.tiles * 4, kCounterAlign))
-                               : nullptr;
+    float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const dim3 grid((unsigned)(p.tiles * p.splits));
     const bool aligned = (ldq % 16) == 0;
     const size_t shm = (size_t)(p.waves * kGemvGroups * kTN + p.rows_per_wg) * sizeof(float);
@@ -258,11 +244,11 @@ hipError_t launch_head_logits(const HeadPlan &p, const float *x, int64_t K, cons
         if (aligned)                                                                            \
             hipLaunchKernelGGL((k_head_logits<WV, true>), grid, dim3(64 * WV), shm, stream, x, K,  \
                                Q, ldq, hs, N, logits, p.tiles, p.splits, p.rows_per_wg, p.npad,  \
-                               part, counters);                                                 \
+                               part);                                                           \
         else                                                                                    \
             hipLaunchKernelGGL((k_head_logits<WV, false>), grid, dim3(64 * WV), shm, stream, x, K, \
                                Q, ldq, hs, N, logits, p.tiles, p.splits, p.rows_per_wg, p.npad,  \
-                               part, counters);                                                 \
+                               part);                                                           \
         break;
     switch (p.waves) {
         W4_HEAD_CASE(1)
@@ -272,7 +258,10 @@ hipError_t launch_head_logits(const HeadPlan &p, const float *x, int64_t K, cons
         return hipErrorInvalidValue;
     }
 #undef W4_HEAD_CASE
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_reduce(part, p.splits, 1, N, p.npad, nullptr, hs, 16777216.0f, logits,
+                                stream);
 }
 
 }  // namespace w4

@@ -60,29 +60,37 @@ __global__ __launch_bounds__(256) void k_prepack_blocks(const float *__restrict_
     Ps[(2 * j + 1) * NB + b1] = scales[b1 * N + 2 * j + 1];
 }
 
-// acc[r] += x_r[k] * (q[k] - z) over the 8 codes k = 8d .. 8d+7 of one word,
-// for MR activation rows.  Even k land in accE (units 2^-24), odd k in accO
-// (units 2^-20); see common.h for the subnormal encoding.
+// acc[r] += x_r[k] * (q[k] - z) over the 16 codes k = 16h .. 16h+15 of two
+// consecutive words (v0: k = 16h .. 16h+7, v1: the next 8), for MR
+// activation rows.  One 64-bit shift serves both words: the masks below only
+// read bits 0-7 and 16-23 of each 32-bit half, which the shift fills from
+// the right word.  Even k land in accE (units 2^-24), odd k in accO (units
+// 2^-20); see common.h for the subnormal encoding.
 template <int MR>
-__device__ __forceinline__ void fma_kword(uint32_t v, half2_t zE, half2_t zO,
-                                          const float (*xr)[kBlock], int d, float (*accE)[2],
-                                          float (*accO)[2]) {
-    const uint32_t hi = v >> 8;
-    const half2_t e0 = as_half2(v & 0x000F000Fu) - zE;   // k = 8d+0, 8d+4
-    const half2_t o0 = as_half2(v & 0x00F000F0u) - zO;   // k = 8d+1, 8d+5
-    const half2_t e1 = as_half2(hi & 0x000F000Fu) - zE;  // k = 8d+2, 8d+6
-    const half2_t o1 = as_half2(hi & 0x00F000F0u) - zO;  // k = 8d+3, 8d+7
-    const int k = 8 * d;
+__device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, half2_t zO,
+                                          const float (*xr)[kBlock], int h, float *accE,
+                                          float *accO) {
+    const uint64_t sh = (((uint64_t)v1 << 32) | v0) >> 8;
+    const uint32_t hv[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
+    const uint32_t lv[2] = {v0, v1};
 #pragma unroll
-    for (int r = 0; r < MR; ++r) {
-        accE[r][0] = __builtin_fmaf(xr[r][k + 0], (float)e0.x, accE[r][0]);
-        accE[r][1] = __builtin_fmaf(xr[r][k + 4], (float)e0.y, accE[r][1]);
-        accO[r][0] = __builtin_fmaf(xr[r][k + 1], (float)o0.x, accO[r][0]);
-        accO[r][1] = __builtin_fmaf(xr[r][k + 5], (float)o0.y, accO[r][1]);
-        accE[r][0] = __builtin_fmaf(xr[r][k + 2], (float)e1.x, accE[r][0]);
-        accE[r][1] = __builtin_fmaf(xr[r][k + 6], (float)e1.y, accE[r][1]);
-        accO[r][0] = __builtin_fmaf(xr[r][k + 3], (float)o1.x, accO[r][0]);
-        accO[r][1] = __builtin_fmaf(xr[r][k + 7], (float)o1.y, accO[r][1]);
+    for (int d = 0; d < 2; ++d) {
+        const half2_t e0 = as_half2(lv[d] & 0x000F000Fu) - zE;  // k = +0, +4
+        const half2_t o0 = as_half2(lv[d] & 0x00F000F0u) - zO;  // k = +1, +5
+        const half2_t e1 = as_half2(hv[d] & 0x000F000Fu) - zE;  // k = +2, +6
+        const half2_t o1 = as_half2(hv[d] & 0x00F000F0u) - zO;  // k = +3, +7
+        const int k = 16 * h + 8 * d;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            accE[r] = __builtin_fmaf(xr[r][k + 0], (float)e0.x, accE[r]);
+            accO[r] = __builtin_fmaf(xr[r][k + 1], (float)o0.x, accO[r]);
+            accE[r] = __builtin_fmaf(xr[r][k + 2], (float)e1.x, accE[r]);
+            accO[r] = __builtin_fmaf(xr[r][k + 3], (float)o1.x, accO[r]);
+            accE[r] = __builtin_fmaf(xr[r][k + 4], (float)e0.y, accE[r]);
+            accO[r] = __builtin_fmaf(xr[r][k + 5], (float)o0.y, accO[r]);
+            accE[r] = __builtin_fmaf(xr[r][k + 6], (float)e1.y, accE[r]);
+            accO[r] = __builtin_fmaf(xr[r][k + 7], (float)o1.y, accO[r]);
+        }
     }
 }
 
@@ -162,17 +170,14 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                 const uint32_t z = (zb[p] >> zsh) & 15;
                 const half2_t zE = as_half2(z * 0x00010001u);
                 const half2_t zO = as_half2((z << 4) * 0x00010001u);
-                float accE[MR][2], accO[MR][2];
+                float accE[MR], accO[MR];
 #pragma unroll
-                for (int r = 0; r < MR; ++r) accE[r][0] = accE[r][1] = accO[r][0] = accO[r][1] = 0.0f;
-                fma_kword<MR>(w[p].x, zE, zO, xr, 0, accE, accO);
-                fma_kword<MR>(w[p].y, zE, zO, xr, 1, accE, accO);
-                fma_kword<MR>(w[p].z, zE, zO, xr, 2, accE, accO);
-                fma_kword<MR>(w[p].w, zE, zO, xr, 3, accE, accO);
+                for (int r = 0; r < MR; ++r) accE[r] = accO[r] = 0.0f;
+                fma_kpair<MR>(w[p].x, w[p].y, zE, zO, xr, 0, accE, accO);
+                fma_kpair<MR>(w[p].z, w[p].w, zE, zO, xr, 1, accE, accO);
 #pragma unroll
                 for (int r = 0; r < MR; ++r) {
-                    const float t = __builtin_fmaf(accO[r][0] + accO[r][1], 1048576.0f,
-                                                   (accE[r][0] + accE[r][1]) * 16777216.0f);
+                    const float t = __builtin_fmaf(accO[r], 1048576.0f, accE[r] * 16777216.0f);
                     part[r][p] = __builtin_fmaf(s[p], t, part[r][p]);
                 }
             }
@@ -248,7 +253,7 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
         return hipGetLastError();                                                               \
     }
     W4_KM_CASE(1, 1) W4_KM_CASE(1, 2) W4_KM_CASE(1, 3) W4_KM_CASE(1, 4)
-    W4_KM_CASE(1, 6) W4_KM_CASE(1, 8)
+    W4_KM_CASE(1, 6) W4_KM_CASE(1, 8) W4_KM_CASE(1, 12) W4_KM_CASE(1, 16)
     W4_KM_CASE(2, 1) W4_KM_CASE(2, 2) W4_KM_CASE(2, 4)
     W4_KM_CASE(4, 1) W4_KM_CASE(4, 2)
 #undef W4_KM_CASE

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "plan.h"
+#include "splitk.h"
 
 namespace w4 {
 

@@ -14,9 +14,10 @@ int64_t env_int(const char *name) {
     return v ? atoll(v) : 0;
 }
 
-size_t splitk_bytes(int64_t tiles, int64_t splits, int64_t npad, int64_t rows) {
+// partial planes part[splits][rows][npad] (fp32)
+size_t splitk_bytes(int64_t splits, int64_t npad, int64_t rows) {
     if (splits <= 1) return 0;
-    return align_up((size_t)tiles * 4, kCounterAlign) + (size_t)splits * rows * npad * 4;
+    return (size_t)splits * rows * npad * 4;
 }
 
 // Pick the number of K-blocks each lane group takes: one, unless that makes
@@ -47,7 +48,7 @@ GemvPlan plan_gemv(int64_t K, int64_t N) {
     static const int64_t env_waves = env_int("W4_GEMV_WAVES");
     static const int64_t env_t = env_int("W4_GEMV_BLOCKS_PER_GROUP");
     p.kind = GemvPlan::kFast;
-    p.waves = (env_waves == 1 || env_waves == 2 || env_waves == 4) ? (int)env_waves : 1;
+    p.waves = (env_waves == 1 || env_waves == 2 || env_waves == 4) ? (int)env_waves : 4;
     const int slots = p.waves * kGemvGroups;
     const int64_t NB = K / 32;
     p.tiles = cdiv(N, kGemvTileCols);
@@ -55,7 +56,7 @@ GemvPlan plan_gemv(int64_t K, int64_t N) {
     const int64_t t = env_t > 0 ? env_t : blocks_per_group(p.tiles, NB, slots);
     p.blocks_per_wg = (int64_t)slots * t;
     p.splits = cdiv(NB, p.blocks_per_wg);
-    p.workspace = splitk_bytes(p.tiles, p.splits, p.npad, 1);
+    p.workspace = splitk_bytes(p.splits, p.npad, 1);
     return p;
 }
 
@@ -79,7 +80,7 @@ HeadPlan plan_head(int64_t K, int64_t N) {
     const int64_t t = blocks_per_group(p.tiles, RB, slots);
     p.rows_per_wg = (int64_t)slots * t * 32;
     p.splits = cdiv(K, p.rows_per_wg);
-    p.workspace = splitk_bytes(p.tiles, p.splits, p.npad, 1);
+    p.workspace = splitk_bytes(p.splits, p.npad, 1);
     return p;
 }
 
@@ -110,9 +111,7 @@ SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N) {
     if (splits < 1) splits = 1;
     p.blocks_per_wg = cdiv(NB, splits);
     p.splits = cdiv(NB, p.blocks_per_wg);
-    p.workspace = p.splits > 1 ? align_up((size_t)p.tiles * p.mgroups * 4, kCounterAlign) +
-                                     (size_t)p.splits * M * p.npad * 4
-                               : 0;
+    p.workspace = splitk_bytes(p.splits, p.npad, M);
     return p;
 }
 
@@ -151,11 +150,11 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N) {
         p.groups = 1;
     }
     static const int64_t env_p = env_int("W4_KMAJOR_PASSES");
-    static const int allowed1[] = {8, 6, 4, 3, 2, 1};
+    static const int allowed1[] = {16, 12, 8, 6, 4, 3, 2, 1};
     static const int allowed2[] = {4, 2, 1};
     static const int allowed4[] = {2, 1};
     const int *allowed = p.rows == 1 ? allowed1 : p.rows == 2 ? allowed2 : allowed4;
-    const int nallowed = p.rows == 1 ? 6 : p.rows == 2 ? 3 : 2;
+    const int nallowed = p.rows == 1 ? 8 : p.rows == 2 ? 3 : 2;
     // enough workgroups to fill the chip: about 512 column groups
     const int64_t want = env_p > 0 ? env_p : N / ((int64_t)p.groups * 512);
     p.passes = 1;

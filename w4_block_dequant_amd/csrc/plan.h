@@ -8,10 +8,6 @@
 
 namespace w4 {
 
-// Workspace layout shared by the split-K kernels: one 32-bit arrival counter
-// per column tile (padded to 256 bytes), then the fp32 partial sums.
-constexpr size_t kCounterAlign = 256;
-
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- M == 1 fused dequant-GEMV ---------------------------------------------
@@ -19,7 +15,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // rows of one K-block; 16 lanes cover a 256-column tile, the 4 lane groups of
 // a wave take 4 different K-blocks.  A workgroup of `waves` waves covers one
 // column tile and `blocks_per_wg` K-blocks; `splits` workgroups along K
-// combine their partial sums through the workspace.
+// write partial sums to the workspace, summed by a second kernel.
 struct GemvPlan {
     enum Kind { kEmpty = 0, kBiasOnly = 1, kFast = 2, kGeneric = 3 } kind;
     int64_t tiles = 0;          // column tiles (fast path)

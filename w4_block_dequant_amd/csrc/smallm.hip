@@ -14,7 +14,8 @@
 // the fp32 tile in one of two LDS buffers.  After one barrier each wave runs
 // its 64 columns (4 MFMA n-tiles) against up to 4 MFMA m-tiles of X, reading
 // its B operands with ds_read_b128, while the next block's loads are in
-// flight.  Split-K partials combine as in the GEMV (splitk.h).
+// flight.  Workgroups along K write partial sums that a second kernel adds
+// in split order (splitk.h).
 #include "common.h"
 #include "launch.h"
 #include "splitk.h"
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void k_mm_mfma(
     const float *__restrict__ x, int64_t M, int64_t K, const uint8_t *__restrict__ Wq,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int64_t N,
     const float *__restrict__ bias, float *__restrict__ y, int64_t tiles, int64_t splits,
-    int64_t bpw, int64_t npad, float *__restrict__ part, unsigned *__restrict__ counters) {
+    int64_t bpw, int64_t npad, float *__restrict__ part) {
     __shared__ float Ws[2][kBlock * kRowsPad];
 
     const int tid = threadIdx.x;
@@ -182,20 +183,9 @@ __global__ __launch_bounds__(256) void k_mm_mfma(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t mr = 16 * mt + 4 * kq + v;
-                if (mr < rows) store_partial(pp + (m0 + mr) * npad + n, acc[mt][nt][v]);
+                if (mr < rows) pp[(m0 + mr) * npad + n] = acc[mt][nt][v];
             }
         }
-    unsigned *cnt = counters + mg * tiles + tile;
-    if (!splitk_arrive(cnt, splits)) return;
-    for (int64_t e = tid; e < rows * kTN; e += 256) {
-        const int64_t mr = e / kTN, n = n0 + (e % kTN);
-        if (n >= N) continue;
-        float v = 0.0f;
-        for (int64_t s = 0; s < splits; ++s)
-            v += load_partial(part + s * (M * npad) + (m0 + mr) * npad + n);
-        y[(m0 + mr) * N + n] = bias ? v + bias[n] : v;
-    }
-    splitk_reset(cnt);
 }
 
 }  // namespace
@@ -214,17 +204,12 @@ hipError_t launch_small_m(const SmallMPlan &p, const float *x, int64_t M, int64_
     case SmallMPlan::kMfma:
         break;
     }
-    unsigned *counters = static_cast<unsigned *>(workspace);
-    float *part = p.splits > 1 ? reinterpret_cast<float *>(
-                                     static_cast<char *>(workspace) +
-                                     align_up((size_t)p.tiles * p.mgroups * 4, kCounterAlign))
-                               : nullptr;
+    float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const dim3 grid((unsigned)(p.tiles * p.splits * p.mgroups));
 #define W4_MFMA_CASE(MTV)                                                                       \
     case MTV:                                                                                   \
         hipLaunchKernelGGL(k_mm_mfma<MTV>, grid, dim3(256), 0, stream, x, M, K, Wq, scales,      \
-                           zeros, N, bias, y, p.tiles, p.splits, p.blocks_per_wg, p.npad, part,  \
-                           counters);                                                           \
+                           zeros, N, bias, y, p.tiles, p.splits, p.blocks_per_wg, p.npad, part); \
         break;
     switch (p.mtiles) {
         W4_MFMA_CASE(1)
@@ -235,7 +220,9 @@ hipError_t launch_small_m(const SmallMPlan &p, const float *x, int64_t M, int64_
         return hipErrorInvalidValue;
     }
 #undef W4_MFMA_CASE
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_reduce(part, p.splits, M, N, p.npad, bias, nullptr, 1.0f, y, stream);
 }
 
 }  // namespace w4

@@ -1,50 +1,22 @@
-// Deterministic split-K combination across workgroups.
+// Deterministic split-K combination.
 //
-// Each of the `splits` workgroups of a column tile stores its fp32 partial
-// sums, then increments the tile's arrival counter.  The workgroup that
-// arrives last reads every split's partials in split order (so the result
-// does not depend on arrival order), writes the output and resets the
-// counter to zero for the next launch.  No floating-point atomics.
-//
-// Visibility across the XCDs (each has its own L2) is obtained without a
-// device-scope fence, which on gfx950 writes back and invalidates the whole
-// L2 of the calling XCD: the partials are written with device-scope stores
-// (sc1, coherent at the device level) and read with device-scope loads, and
-// every thread waits for its stores to complete (s_waitcnt) before the
-// workgroup barrier that precedes the counter increment.  The last
-// workgroup issues its loads only after its counter RMW has returned.
+// A split-K kernel writes its fp32 partial sums to the workspace as
+// part[s][m][n] (row stride npad, split stride rows * npad) with plain stores;
+// a second kernel on the same stream then forms every output
+// y[m, n] = sum_s part[s][m][n] (+ bias[n]) in split order, one thread per
+// output.  No atomics, no counters and no ordering between workgroups of the
+// first kernel; stream order makes the partials visible to the second.
 #pragma once
 
 #include "common.h"
 
 namespace w4 {
 
-__device__ __forceinline__ void store_partial(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float load_partial(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// All threads of the workgroup call this after storing their partials with
-// store_partial.  Returns true (in every thread) for the workgroup that must
-// finish the tile.
-__device__ __forceinline__ bool splitk_arrive(unsigned *counter, int64_t splits) {
-    __shared__ int s_last;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)(splits - 1));
-    }
-    __syncthreads();
-    return s_last != 0;
-}
-
-__device__ __forceinline__ void splitk_reset(unsigned *counter) {
-    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// y[m, n] (row stride N) from `splits` partial planes of `rows` x npad floats;
+// `scale` multiplies the sum before the bias is added (used by the int8 head
+// to apply its fp16-subnormal unit and per-token scale: pass col_scale).
+hipError_t launch_splitk_reduce(const float *part, int64_t splits, int64_t rows, int64_t N,
+                                int64_t npad, const float *bias, const float *col_scale,
+                                float unit, float *y, hipStream_t stream);
 
 }  // namespace w4
