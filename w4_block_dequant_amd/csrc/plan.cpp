@@ -112,6 +112,17 @@ SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N) {
     p.blocks_per_wg = cdiv(NB, splits);
     p.splits = cdiv(NB, p.blocks_per_wg);
     p.workspace = splitk_bytes(p.splits, p.npad, M);
+    // prefetch depth: enough MFMA work in flight to cover memory latency (one
+    // block of MFMAs is 8 * mtiles per wave), without idle ring steps
+    static const int64_t env_d = env_int("W4_MFMA_DEPTH");
+    const int max_d = p.mtiles <= 2 ? 3 : 2;
+    p.depth = 1;
+    for (int d = max_d; d >= 2; --d)
+        if (p.blocks_per_wg % d == 0 || p.blocks_per_wg > 4 * d) {
+            p.depth = d;
+            break;
+        }
+    if (env_d >= 1 && env_d <= max_d) p.depth = (int)env_d;
     return p;
 }
 

@@ -50,6 +50,7 @@ struct SmallMPlan {
     enum Kind { kEmpty = 0, kBiasOnly = 1, kMfma = 2, kGeneric = 3 } kind;
     int64_t mtiles = 0;         // 16-row MFMA tiles per workgroup (1..4)
     int64_t mgroups = 1;        // 64-row groups of M
+    int depth = 1;              // blocks of loads in flight ahead of the MFMAs
     int64_t tiles = 0;          // column tiles
     int64_t splits = 1;
     int64_t blocks_per_wg = 0;
