@@ -15,8 +15,9 @@ by the measured time per pass.
 
 Also reported on the same JSON line:
   * roofline: the GEMV kernel's algorithmic bytes per launch over its
-    average launch duration (HIP events around each launch on the launch
-    stream), against the 8 TB/s HBM peak;
+    average launch duration (the timed pass over its 128 launches, all of
+    them this kernel), against the 8 TB/s HBM peak, plus per-shape times
+    from graphs of one shape's 32 launches;
   * cpu_baseline: the CPU oracle (dequantize, then fp64 matmul, one thread)
     on the first layers of the same body, in the same unit;
   * parity: GPU outputs of those layers against the oracle's, per output;
@@ -40,6 +41,68 @@ import numpy as np
 METRIC = "W4 decode GEMV achieved HBM GB/s (% of peak) + body-pass tokens/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+# The dominant kernel of the timed pass, the sources that define it, and the
+# committed counter summary that bench.py reads `roofline.traffic` from.  The
+# summary records a digest of these sources; once they change, traffic is
+# reported as null until the counters are taken again.
+GEMV_KERNEL = "k_gemv_kmajor"
+GEMV_SOURCES = ("w4_block_dequant_amd/csrc/kmajor.hip", "w4_block_dequant_amd/csrc/common.h")
+PROFILE_DIR = "profiles"
+TRACE_SUMMARY = "k_gemv_kmajor_dense38_m1_kernel_trace.md"
+TRAFFIC_SUMMARY = "k_gemv_kmajor_dense38_m1_traffic.md"
+COPY_FLOATS = 1 << 26          # calibration copy: 256 MiB read, 256 MiB written
+PROFILE_COMMANDS = (
+    "cd <repo root>; export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/w4prof/trace -o run "
+    "-- python bench.py --steps 10 --warmup 2 --skip-secondary --skip-cpu "
+    "--json-out /tmp/w4prof/trace_bench.json",
+    "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/w4prof/fetch "
+    "-o run -- python bench.py --profile-run --steps 2",
+    "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/w4prof/write "
+    "-o run -- python bench.py --profile-run --steps 2",
+    "python bench.py --summarize-profiles /tmp/w4prof --out profiles",
+)
+
+
+def gemv_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMV_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_summary_fields(path: str) -> dict:
+    """`key: value` lines of a committed profile summary (one per line, after a dash)."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                out[k.strip("`")] = v.strip().strip("`")
+    return out
+
+
+def committed_traffic():
+    """HBM bytes per GEMV launch from the committed counter summary, if still current."""
+    f = read_summary_fields(os.path.join(ROOT, PROFILE_DIR, TRAFFIC_SUMMARY))
+    if not f or f.get("gemv_source_sha256") != gemv_digest():
+        return None, None
+    try:
+        fetch = float(f["fetch_bytes_per_launch"])
+        write = float(f["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None, None
+    return fetch + write, {"fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+                           "fetch_factor": float(f.get("fetch_factor", "nan")),
+                           "write_factor": float(f.get("write_factor", "nan")),
+                           "source": f"{PROFILE_DIR}/{TRAFFIC_SUMMARY}"}
 
 
 def parse():
@@ -51,11 +114,21 @@ def parse():
     p.add_argument("--skip-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-oracle time budget for the baseline sample")
+    p.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--profile-run", action="store_true",
+                   help="short eager run for hardware counters: `--steps` M=1 passes, then "
+                        "a plain copy of known size for calibration")
+    p.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                   help="turn rocprofv3 CSV output under DIR into the profile summaries")
+    p.add_argument("--out", default=PROFILE_DIR, help="where --summarize-profiles writes")
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.out)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding or collectives).", file=sys.stderr)
@@ -85,6 +158,8 @@ def main():
         futs = {}
         mats = []
         for i, (l, s, K, N) in enumerate(shapes):
+            if i % 32 == 0:
+                log(f"  {name}: matrix {i} of {len(shapes)}")
             for j in range(i, min(i + ahead, len(shapes))):
                 if j not in futs:
                     lj, sj, Kj, Nj = shapes[j]
@@ -161,34 +236,29 @@ def main():
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
-    def hold_gpu():
-        """Queue a long GPU job so the launches that follow are timed back to back."""
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(50_000_000)
-        else:
-            a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
-            for _ in range(20):
-                a.fill_(1)
-
-    def per_launch_ms(mats, reps=3, layout="kmajor"):
-        """Duration of each matmul launch (HIP events on the launch stream)."""
-        res = np.zeros((reps, len(mats)))
-        for r in range(reps):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in mats]
-            hold_gpu()
-            for (a, b), m in zip(evs, mats):
-                a.record()
-                matmul(m, layout)
-                b.record()
-            torch.cuda.synchronize()
-            res[r] = [a.elapsed_time(b) for a, b in evs]
-        return res.mean(axis=0)
-
     log("building the 3.8B-dense-shaped body (2.32 GB packed) ...")
     t = time.perf_counter()
     dense = build_body("dense38", synth.CFG_DENSE38, 1, with_bias=False, outliers=False)
     log(f"  built in {time.perf_counter() - t:.1f} s")
+
+    if args.profile_run:
+        # eager passes (one dispatch per matmul), then the calibration copy
+        for _ in range(args.warmup):
+            run_pass(dense)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            run_pass(dense)
+            torch.cuda.synchronize()
+            log(f"profile pass {i + 1} of {args.steps} done")
+        src = torch.randn(COPY_FLOATS, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)      # reads and writes COPY_FLOATS * 4 bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": True, "passes": args.steps, "launches_per_pass": len(dense),
+                          "copy_bytes": COPY_FLOATS * 4}), flush=True)
+        return
 
     # ------------------------------------------------------------ timed steps
     graph = capture(lambda: run_pass(dense))
@@ -199,18 +269,25 @@ def main():
     log(f"dense38 M=1 pass: {ms:.4f} ms, {value:.1f} GB/s, {1e3 / ms:.1f} tok/s")
 
     # ------------------------------------------------------ per-kernel roofline
-    dur = per_launch_ms(dense)
+    # Every launch of the timed pass is the K-major GEMV kernel, so its average
+    # launch duration is the timed pass time (HIP events on the launch stream
+    # around the graph replays) over the launches; the small gaps between graph
+    # nodes are included, which makes it a slight overestimate.
     launches = len(dense)
     avg_bytes = pass_bytes / launches
-    avg_ms = float(dur.mean())
+    avg_ms = ms / launches
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
     per_shape = {}
     for slot, (K, N) in enumerate(synth.DENSE38_SHAPES):
-        d = [dur[i] for i, m in enumerate(dense) if m.slot == slot]
-        b = dense[slot].bytes
-        per_shape[f"{K}x{N}"] = {"us": round(1e3 * float(np.mean(d)), 3),
-                                 "GB_s": round(b / (np.mean(d) * 1e-3) / 1e9, 1)}
+        sub = [m for m in dense if m.slot == slot]
+        gs = capture(lambda: run_pass(sub))
+        mss, _ = time_graph(gs, max(5, args.steps // 2), 2)
+        del gs
+        us = 1e3 * mss / len(sub)
+        per_shape[f"{K}x{N}"] = {"us": round(us, 3),
+                                 "GB_s": round(sub[0].bytes / (us * 1e-6) / 1e9, 1)}
     log(f"GEMV per launch: {1e3 * avg_ms:.2f} us avg, {achieved:.1f} GB/s; {per_shape}")
+    traffic, traffic_detail = committed_traffic()
 
     # the same pass on the canonical layout (split-K GEMV), for comparison
     gcan = capture(lambda: run_pass(dense, layout="canonical"))
@@ -342,15 +419,136 @@ def main():
         "body_pass_tokens_per_s": round(1e3 / ms, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_gemv_kmajor", "avg_launch_us": round(1e3 * avg_ms, 3),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "traffic_detail": traffic_detail,
+                     "kernel": GEMV_KERNEL, "avg_launch_us": round(1e3 * avg_ms, 3),
                      "avg_bytes_per_launch": round(avg_bytes), "per_shape": per_shape},
         "canonical_layout_pass": canonical,
         "cpu_baseline": cpu,
         "parity": parity,
         "secondary": secondary,
     }
-    print(json.dumps(line), flush=True)
+    text = json.dumps(line)
+    print(text, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(text + "\n")
+
+
+def _csvs(root: str, suffix: str):
+    out = []
+    for d, _, files in os.walk(root):
+        out += [os.path.join(d, f) for f in files if f.endswith(suffix)]
+    return sorted(out)
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    name = name.split("(")[0]
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def summarize_profiles(src: str, out_dir: str):
+    """Write the kernel-trace and traffic summaries from rocprofv3 CSV output.
+
+    src/trace: `--kernel-trace --stats` of the timed bench command (plus the
+    bench's own JSON line in src/trace_bench.json); src/fetch and src/write:
+    `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` of `--profile-run`.  The counters
+    are scaled by what they read for the calibration copy (COPY_FLOATS * 4
+    bytes each way), so the traffic figures are in bytes.
+    """
+    import csv
+    import statistics
+
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = "\n".join(f"    {c}" for c in PROFILE_COMMANDS)
+
+    # ---- kernel trace
+    rows = []
+    for f in _csvs(os.path.join(src, "trace"), "kernel_trace.csv"):
+        rows += list(csv.DictReader(open(f)))
+    durs = {}
+    for r in rows:
+        durs.setdefault(r["Kernel_Name"], []).append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    gemv = [d for k, v in durs.items() if GEMV_KERNEL in k for d in v]
+    bench = {}
+    bj = os.path.join(src, "trace_bench.json")
+    if os.path.exists(bj):
+        bench = json.loads(open(bj).read().strip().splitlines()[-1])
+    lines = [f"# {GEMV_KERNEL}: kernel trace of the M=1 3.8B-dense-shaped body pass", "",
+             "Made by:", "", cmds, "",
+             "Every dispatch of the run (graph replays, the per-launch event timing and "
+             "the canonical-layout comparison pass).", ""]
+    lines += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:12]:
+        lines.append(f"| `{_short(k)}` | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                     f"{min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} |")
+    avg_gemv_us = statistics.mean(gemv) / 1e3 if gemv else float("nan")
+    lines += ["", f"- gemv_dispatches: {len(gemv)}",
+              f"- gemv_avg_us_rocprof: {avg_gemv_us:.3f}"]
+    if bench:
+        rl = bench.get("roofline", {})
+        lines += [f"- gemv_avg_us_bench_events: {rl.get('avg_launch_us')}",
+                  f"- bench_value_GB_s: {bench.get('value')}",
+                  f"- bench_ms_per_step: {bench.get('ms_per_step')}",
+                  f"- roofline_achieved_GB_s: {rl.get('achieved')}",
+                  f"- roofline_frac: {rl.get('frac')}"]
+    lines.append(f"- gemv_source_sha256: {gemv_digest()}")
+    with open(os.path.join(out_dir, TRACE_SUMMARY), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # ---- counters
+    def per_dispatch(sub, counter):
+        vals = {}
+        for f in _csvs(os.path.join(src, sub), "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (f, r["Dispatch_Id"])
+                name, v = r["Kernel_Name"], float(r["Counter_Value"])
+                vals[key] = (name, vals.get(key, (name, 0.0))[1] + v)
+        return list(vals.values())
+
+    copy_bytes = COPY_FLOATS * 4
+    res = {}
+    for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        d = per_dispatch(sub, counter)
+        copy = [v for k, v in d if "neg_kernel" in k]
+        g = [v for k, v in d if GEMV_KERNEL in k]
+        if not copy or not g:
+            raise SystemExit(f"no {counter} rows for the copy or the GEMV under {src}/{sub}")
+        factor = statistics.median(copy) * 1024.0 / copy_bytes
+        res[sub] = {"factor": factor, "per_launch": statistics.mean(g) * 1024.0 / factor,
+                    "n": len(g), "copy_kib": statistics.median(copy), "gemv_kib": statistics.mean(g)}
+    alg = None
+    if bench:
+        alg = bench.get("roofline", {}).get("avg_bytes_per_launch")
+    lines = [f"# {GEMV_KERNEL}: HBM traffic per launch, M=1 3.8B-dense-shaped body pass", "",
+             "Made by:", "", cmds, "",
+             "FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by "
+             "what it reads for a plain copy kernel (`torch.neg`, "
+             f"{copy_bytes} bytes read and {copy_bytes} bytes written) so that the figures "
+             "below are bytes.", "",
+             f"- fetch_copy_kib: {res['fetch']['copy_kib']:.1f}",
+             f"- write_copy_kib: {res['write']['copy_kib']:.1f}",
+             f"- fetch_factor: {res['fetch']['factor']:.5f}",
+             f"- write_factor: {res['write']['factor']:.5f}",
+             f"- gemv_dispatches_counted: {res['fetch']['n']}",
+             f"- fetch_kib_per_launch_raw: {res['fetch']['gemv_kib']:.1f}",
+             f"- write_kib_per_launch_raw: {res['write']['gemv_kib']:.1f}",
+             f"- fetch_bytes_per_launch: {res['fetch']['per_launch']:.0f}",
+             f"- write_bytes_per_launch: {res['write']['per_launch']:.0f}"]
+    if alg:
+        tot = res["fetch"]["per_launch"] + res["write"]["per_launch"]
+        lines += [f"- algorithmic_bytes_per_launch: {alg}",
+                  f"- traffic_over_algorithmic: {tot / alg:.4f}"]
+    lines.append(f"- gemv_source_sha256: {gemv_digest()}")
+    with open(os.path.join(out_dir, TRAFFIC_SUMMARY), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(os.path.join(out_dir, TRACE_SUMMARY)).read())
+    print(open(os.path.join(out_dir, TRAFFIC_SUMMARY)).read())
 
 
 if __name__ == "__main__":

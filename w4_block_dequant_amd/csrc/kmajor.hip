@@ -18,7 +18,8 @@
 // column contiguously.  Per packed word: 1 shift, 4 masks, 4 packed-fp16
 // subtractions (q - z as exact fp16 subnormals) and 8 v_fma_mix_f32.  The
 // per-lane block sums are scaled, then summed over the column's lanes in a
-// fixed order through LDS, so results are deterministic.
+// fixed order: through LDS, a few lanes per output each adding a contiguous
+// run, then two lane exchanges.  Results are deterministic.
 #include "common.h"
 #include "launch.h"
 
@@ -101,12 +102,12 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // below 2^31 bytes).  CHECK clamps columns past N (ragged last workgroup);
 // without it every load is unconditional, so the compiler can start on
 // pass 0 while later passes are still in flight.
-template <int MR, int P, bool CHECK>
+template <int MR, int P, bool CHECK, bool LOOP>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, int M, int K, const uint8_t *__restrict__ Pq,
     const float *__restrict__ Ps, const uint8_t *__restrict__ Pz, int N,
-    const float *__restrict__ bias, float *__restrict__ y, int G, int NBL, int ch) {
-    extern __shared__ float red[];  // [MR][CC][NBL], then [MR][CC][NBL / ch]
+    const float *__restrict__ bias, float *__restrict__ y, int G, int NBL) {
+    extern __shared__ float red[];  // [MR][CC][NBL]
     const int L = threadIdx.x;
     const int g = L / NBL, bl = L - g * NBL;
     const int NB = K / kBlock, hk = K / 2;
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         for (int p = 0; p < P; ++p) part[r][p] = 0.0f;
 
     if (g < G) {
-        for (int b = bl; b < NB; b += NBL) {
+        // LOOP = false: NBL >= NB, each lane owns at most one block (no loop)
+        for (int b = bl; LOOP ? b < NB : (b == bl && b < NB); b += NBL) {
             // activations of this block, for each of the MR rows
             float xr[MR][kBlock];
 #pragma unroll
@@ -192,26 +194,28 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
             for (int p = 0; p < P; ++p) red[(r * CC + p * G + g) * NBL + bl] = part[r][p];
     }
     __syncthreads();
-    // stage 1: chunks of `ch` consecutive partials (ch divides NBL), in order
-    const int total = MR * CC * NBL;
-    float *red2 = red + total;
-    for (int i = L; i * ch < total; i += blockDim.x) {
+    // `parts` adjacent lanes per output each add one contiguous run of NBL /
+    // parts partials in order, then the runs are added by two lane exchanges:
+    // a fixed order, so the result does not depend on timing.
+    const int parts = (NBL % 4 == 0) ? 4 : ((NBL % 2 == 0) ? 2 : 1);
+    const int per = NBL / parts;
+    const int q = L % parts;
+    for (int o = L / parts; o < MR * CC; o += blockDim.x / parts) {
+        const float *rp = red + o * NBL + q * per;
         float v = 0.0f;
-        for (int j = 0; j < ch; ++j) v += red[i * ch + j];
-        red2[i] = v;
-    }
-    __syncthreads();
-    // stage 2: one thread per column, rows in turn; chunk sums in order
-    const int npc = NBL / ch;
-    if (L < CC) {
-        const int n = n0 + L;
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            float v = 0.0f;
-            for (int j = 0; j < npc; ++j) v += red2[(r * CC + L) * npc + j];
-            const int m = m0 + r;
-            if (n < N && m < M) y[(size_t)m * N + n] = bias ? v + bias[n] : v;
+        if ((per & 3) == 0) {  // 16-byte aligned runs: vector reads, pairwise adds
+            for (int j = 0; j < per; j += 4) {
+                const f32x4_t t = *reinterpret_cast<const f32x4_t *>(rp + j);
+                v += (t.x + t.y) + (t.z + t.w);
+            }
+        } else {
+            for (int j = 0; j < per; ++j) v += rp[j];
         }
+        if (parts >= 2) v += __shfl_xor(v, 1);
+        if (parts == 4) v += __shfl_xor(v, 2);
+        const int r = o / CC, c = o - r * CC;
+        const int n = n0 + c, m = m0 + r;
+        if (q == 0 && n < N && m < M) y[(size_t)m * N + n] = bias ? v + bias[n] : v;
     }
 }
 
@@ -237,25 +241,28 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     if (p.kind == KmajorPlan::kBiasOnly) return launch_bias_fill(bias, M, N, y, stream);
     const int64_t C = (int64_t)p.groups * p.passes;
     const dim3 grid((unsigned)((N + C - 1) / C), (unsigned)((M + p.rows - 1) / p.rows));
-    const int64_t cells = (int64_t)p.rows * C * p.lanes_per_col;
-    const size_t shm = (size_t)(cells + cells / p.chunk) * sizeof(float);
+    const size_t shm = (size_t)p.rows * C * p.lanes_per_col * sizeof(float);
     const bool check = (N % C) != 0;
+    const bool loop = p.lanes_per_col < K / kBlock;
+#define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
+    hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV>), grid, dim3(p.threads), shm, stream, x,   \
+                       (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups, p.lanes_per_col)
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
-        if (check)                                                                              \
-            hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, true>), grid, dim3(p.threads), shm, stream, \
-                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups,         \
-                               p.lanes_per_col, p.chunk);                                       \
-        else                                                                                    \
-            hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, false>), grid, dim3(p.threads), shm,      \
-                               stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups, \
-                               p.lanes_per_col, p.chunk);                                       \
+        if (check) {                                                                            \
+            if (loop) W4_KM_LAUNCH(MRV, PV, true, true);                                        \
+            else W4_KM_LAUNCH(MRV, PV, true, false);                                            \
+        } else {                                                                                \
+            if (loop) W4_KM_LAUNCH(MRV, PV, false, true);                                       \
+            else W4_KM_LAUNCH(MRV, PV, false, false);                                           \
+        }                                                                                       \
         return hipGetLastError();                                                               \
     }
     W4_KM_CASE(1, 1) W4_KM_CASE(1, 2) W4_KM_CASE(1, 3) W4_KM_CASE(1, 4)
     W4_KM_CASE(1, 6) W4_KM_CASE(1, 8) W4_KM_CASE(1, 12) W4_KM_CASE(1, 16)
     W4_KM_CASE(2, 1) W4_KM_CASE(2, 2) W4_KM_CASE(2, 4)
     W4_KM_CASE(4, 1) W4_KM_CASE(4, 2)
+#undef W4_KM_LAUNCH
 #undef W4_KM_CASE
     return hipErrorInvalidValue;
 }

@@ -166,19 +166,27 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N) {
     static const int allowed4[] = {2, 1};
     const int *allowed = p.rows == 1 ? allowed1 : p.rows == 2 ? allowed2 : allowed4;
     const int nallowed = p.rows == 1 ? 8 : p.rows == 2 ? 3 : 2;
-    // enough workgroups to fill the chip: about 512 column groups
+    // Workgroup count: whole multiples of the 256 compute units keep every CU
+    // equally loaded (all workgroups are resident at once), which measures
+    // better than any other choice; among those, up to 8 passes per lane.
+    // Otherwise: enough workgroups to fill the chip, about 512 column groups.
     const int64_t want = env_p > 0 ? env_p : N / ((int64_t)p.groups * 512);
     p.passes = 1;
-    for (int i = 0; i < nallowed; ++i)
-        if (allowed[i] <= want && p.rows * allowed[i] <= p.lanes_per_col) {
-            p.passes = allowed[i];
-            break;
+    bool found = false;
+    if (env_p <= 0) {
+        for (int i = 0; i < nallowed && !found; ++i) {
+            const int P = allowed[i];
+            const int64_t wgs = cdiv(N, (int64_t)p.groups * P) * cdiv(M, p.rows);
+            if (P <= 8 && wgs >= 256 && wgs % 256 == 0) {
+                p.passes = P;
+                found = true;
+            }
         }
-    p.chunk = 1;
-    for (int c : {8, 4, 2})
-        if (p.lanes_per_col % c == 0) {
-            p.chunk = c;
-            break;
+    }
+    for (int i = 0; i < nallowed && !found; ++i)
+        if (allowed[i] <= want) {
+            p.passes = allowed[i];
+            found = true;
         }
     return p;
 }

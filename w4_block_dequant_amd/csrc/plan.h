@@ -68,7 +68,6 @@ SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N);
 struct KmajorPlan {
     enum Kind { kEmpty = 0, kBiasOnly = 1, kRun = 2 } kind;
     int rows = 1, passes = 1, groups = 1, lanes_per_col = 64, threads = 64;
-    int chunk = 1;  // partials summed per thread in the first reduction stage
 };
 
 KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N);
