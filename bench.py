@@ -375,17 +375,25 @@ def main():
             heads[str(ldq)] = {"us": round(1e3 * msh, 3), "GB_s": round(hb / (msh * 1e-3) / 1e9, 1)}
             heads[str(ldq)]["Q"] = Q
             heads[str(ldq)]["hs"] = hs
+        # the same head on the token-major copy of the table (integer MFMA, one launch)
+        Qk = w4.i8_prepack_head(heads["50272"]["Q"], synth.GPT2_VOCAB)
+        hsk = heads["50272"]["hs"]
+        xl = torch.from_numpy(synth.activations(1, synth.GPT2_HIDDEN, synth.CFG_HEAD)).to(dev)[0]
+        outk = torch.empty(synth.GPT2_VOCAB, device=dev)
+        gk = capture(lambda: w4.i8_head_logits_kmajor(xl, Qk, hsk, synth.GPT2_HIDDEN, out=outk))
+        msk, _ = time_graph(gk, 200, 20)
+        hbk = synth.GPT2_HIDDEN * synth.GPT2_VOCAB + 4 * synth.GPT2_VOCAB * 2 + 4 * synth.GPT2_HIDDEN
+        heads["token_major"] = {"us": round(1e3 * msk, 3), "GB_s": round(hbk / (msk * 1e-3) / 1e9, 1)}
         secondary["i8_head_768x50257"] = {k: {a: b for a, b in v.items() if a in ("us", "GB_s")}
                                          for k, v in heads.items()}
 
         pre = with_x(gpt2, synth.CFG_GPT2_PREFILL, synth.GPT2_PROMPT, outliers=False)
-        Qh, hsh = heads["50272"]["Q"], heads["50272"]["hs"]
         last = pre[-1]
         lg = torch.empty(synth.GPT2_VOCAB, device=dev)
 
         def head_last():
             # the head reads the last prompt row of the body's output (768 wide)
-            w4.i8_head_logits(last.y[-1], Qh, hsh, out=lg, workspace=ws)
+            w4.i8_head_logits_kmajor(last.y[-1], Qk, hsk, synth.GPT2_HIDDEN, out=lg)
 
         gp = capture(lambda: run_pass(pre, head_last, layout="canonical"))
         msp, _ = time_graph(gp, 20, 3)

@@ -143,18 +143,28 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
                       void *stream);
 
 /* y = x . w_hat + bias on the K-major layout: same result contract as
- * w4_matmul (fp32, same bound, deterministic).  Each workgroup owns whole
- * columns, so it needs no workspace.  Built for decode (M = 1) and small
- * batches (up to 4 rows share each weight load; larger M repeats that per
- * 4 rows).  Indexing is 32-bit: K * N, M * K and M * N must be below 2^31
- * (W4_ERR_BAD_SHAPE otherwise).                                            */
+ * w4_matmul (fp32, same bound, deterministic).  Up to M = 4 rows (decode, small
+ * batches) every workgroup owns whole columns and no workspace is used.  For
+ * M > 4 with K % 128 == 0 the product runs on the bf16 matrix cores at fp32
+ * accuracy: (q - z) is exact in bf16 and each activation is split exactly
+ * into three bf16 terms, so every product is exact and sums are fp32; each
+ * block's scale is applied once per block.  That path may split K across
+ * workgroups and then needs a workspace of
+ * w4_matmul_kmajor_workspace_bytes(M, K, N) bytes (0 when it does not):
+ * device memory, 256-byte aligned, any contents, not shared with a call in
+ * flight on another stream.  Indexing is 32-bit: K * N, M * K and M * N must
+ * be below 2^31 (W4_ERR_BAD_SHAPE otherwise).                              */
+size_t w4_matmul_kmajor_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
 int w4_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
-                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *stream);
+                     const uint8_t *Pz, int64_t N, const float *bias, float *y,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Argument check of w4_matmul_kmajor without any HIP call.                 */
 int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                                 const float *Ps, const uint8_t *Pz, int64_t N,
-                                const float *bias, const float *y);
+                                const float *bias, const float *y,
+                                const void *workspace, size_t workspace_bytes);
 
 /* ---------------------------------------------------------------------------
  * int8 tied head (step 3).  E fp32 [K, N] -> Q int8 [K, ldq], hs fp32 [N]:
@@ -183,6 +193,38 @@ int i8_head_logits(const float *x_last, int64_t K, const int8_t *Q, int64_t ldq,
 int i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
              const float *hs, int64_t K, int64_t N, float *out,
              int *d_status, void *stream);
+
+/* ---- int8 head on a K-major copy of the table -------------------------------
+ * Same method (steps 3-4), table stored token-major: Qt int8 [N, ldt] with
+ * Qt[n, k] = Q[k, n], each row zero-padded to ldt >= K, ldt % 16 == 0, and
+ * N * ldt < 2^31.  Row n is token n's embedding vector, contiguous.        */
+
+/* Byte-exact relayout of Q [K, ldq] into Qt [N, ldt] (columns K..ldt-1 of Qt
+ * set to 0).  Q and Qt are 16-byte aligned.                                 */
+int i8_prepack_head(const int8_t *Q, int64_t K, int64_t N, int64_t ldq,
+                    int8_t *Qt, int64_t ldt, void *stream);
+
+/* Host-only validation of i8_head_logits_kmajor's arguments.               */
+int i8_check_head_logits_kmajor_args(const float *x_last, int64_t K, const int8_t *Qt,
+                                     int64_t ldt, const float *hs, int64_t N,
+                                     const float *logits);
+
+/* Last-token logits on the integer matrix cores, one launch, no workspace:
+ * logits[n] = hs[n] * sum_k x_last[k] * Qt[n, k].  K % 64 == 0, K <= 8192.
+ * The table products are exact; x_last enters as a 31-bit fixed-point value
+ * relative to 2^e, e the exponent of max|x_last|, so each activation carries
+ * an absolute error of at most 2^-30 max|x_last| and the result is within the
+ * bound of w4_matmul for activations whose largest entry is not more than
+ * about 10^4 times their |Q|-weighted average.  Non-finite x_last gives NaN
+ * logits.  x_last, Qt 16-byte aligned; hs, logits 4-byte aligned.           */
+int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int64_t ldt,
+                          const float *hs, int64_t N, float *logits, void *stream);
+
+/* Token lookup from Qt (step 3): out[t, k] = fl32(Qt[tokens[t], k] * hs[tokens[t]]),
+ * fp32 [T, K], bit-exact; ids outside [0, N) as in i8_embed.               */
+int i8_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t ldt,
+                    const float *hs, int64_t K, int64_t N, float *out,
+                    int *d_status, void *stream);
 
 #ifdef __cplusplus
 }

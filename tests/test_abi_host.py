@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                  "w4_prepack_kmajor", "w4_matmul_kmajor", "w4_check_matmul_kmajor_args",
                  "i8_quantize_head", "i8_embed", "w4_matmul_workspace_bytes",
                  "i8_head_workspace_bytes", "w4_check_matmul_args", "w4_strerror",
-                 "w4_abi_version"):
+                 "w4_abi_version", "i8_prepack_head", "i8_head_logits_kmajor",
+                 "i8_check_head_logits_kmajor_args", "i8_embed_kmajor"):
         assert must in names
 
 
@@ -127,11 +128,51 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.i8_head_logits(A, 768, A, 50257, A, 50257, A, A, need - 4, None) == w4.W4_ERR_WORKSPACE
     assert lib.i8_embed(A, 4, A, 50257, A, 768, 50258, A, None, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.i8_embed(A + 4, 4, A, 50257, A, 768, 50257, A, None, None) == w4.W4_ERR_MISALIGNED
-    assert lib.w4_check_matmul_kmajor_args(A, 1, 96, A, A, A, 16, None, A) == w4.W4_ERR_BAD_SHAPE
-    assert lib.w4_check_matmul_kmajor_args(A, 1, 128, A, A, A, 16, None, A) == w4.W4_OK
-    assert lib.w4_check_matmul_kmajor_args(A, 1, 128, A + 8, A, A, 16, None, A) == w4.W4_ERR_MISALIGNED
-    assert lib.w4_check_matmul_kmajor_args(None, 1, 128, A, A, A, 16, None, A) == w4.W4_ERR_NULL_PTR
+    km = lib.w4_check_matmul_kmajor_args
+    assert km(A, 1, 96, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_BAD_SHAPE
+    assert km(A, 1, 128, A, A, A, 16, None, A, None, 0) == w4.W4_OK
+    assert km(A, 1, 128, A + 8, A, A, 16, None, A, None, 0) == w4.W4_ERR_MISALIGNED
+    assert km(None, 1, 128, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_NULL_PTR
+    # M > 4 on the matrix-core path: split-K needs a workspace for narrow N
+    need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072)
+    assert need > 0
+    assert w4.w4_matmul_kmajor_workspace_bytes(1, 3072, 3072) == 0
+    assert w4.w4_matmul_kmajor_workspace_bytes(16, 3008, 3072) == 0   # K % 128 != 0: GEMV path
+    assert km(A, 16, 3072, A, A, A, 3072, None, A, None, 0) == w4.W4_ERR_WORKSPACE
+    assert km(A, 16, 3072, A, A, A, 3072, None, A, A, need - 1) == w4.W4_ERR_WORKSPACE
+    assert km(A, 16, 3072, A, A, A, 3072, None, A, A + 64, need) == w4.W4_ERR_MISALIGNED
+    assert km(A, 16, 3072, A, A, A, 3072, None, A, A, need) == w4.W4_OK
     assert lib.w4_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE
     # empty work succeeds without a device
     assert lib.w4_matmul(None, 0, 768, None, None, None, 768, None, None, None, 0, None) == w4.W4_OK
     assert lib.i8_embed(None, 0, None, 10, None, 768, 10, None, None, None) == w4.W4_OK
+
+
+def check_headk(K, N, ldt=None, x=A, Qt=A, hs=A, out=A):
+    if ldt is None:
+        ldt = K
+    return w4.library().i8_check_head_logits_kmajor_args(x, K, Qt, ldt, hs, N, out)
+
+
+def test_head_kmajor_checks():
+    assert check_headk(768, 50257) == w4.W4_OK
+    assert check_headk(768, 50257, ldt=784) == w4.W4_OK
+    assert check_headk(8192, 1000) == w4.W4_OK
+    assert check_headk(800, 10) == w4.W4_ERR_BAD_SHAPE          # K % 64 != 0
+    assert check_headk(8256, 10) == w4.W4_ERR_BAD_SHAPE         # K > 8192
+    assert check_headk(768, 10, ldt=776) == w4.W4_ERR_BAD_SHAPE  # ldt % 16 != 0
+    assert check_headk(768, 10, ldt=704) == w4.W4_ERR_BAD_SHAPE  # ldt < K
+    assert check_headk(768, 1 << 22) == w4.W4_ERR_BAD_SHAPE     # N * ldt >= 2^31
+    assert check_headk(768, 0, x=None, Qt=None, hs=None, out=None) == w4.W4_OK
+    assert check_headk(768, 10, Qt=None) == w4.W4_ERR_NULL_PTR
+    assert check_headk(768, 10, x=A + 4) == w4.W4_ERR_MISALIGNED
+    assert check_headk(768, 10, Qt=A + 8) == w4.W4_ERR_MISALIGNED
+    assert check_headk(768, 10, out=A + 2) == w4.W4_ERR_MISALIGNED
+    lib = w4.library()
+    assert lib.i8_prepack_head(A, 768, 10, 10, A, 776, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.i8_prepack_head(A, 768, 10, 9, A, 768, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.i8_prepack_head(A + 4, 768, 10, 10, A, 768, None) == w4.W4_ERR_MISALIGNED
+    assert lib.i8_embed_kmajor(A, 4, A, 776, A, 768, 10, A, None, None) == w4.W4_ERR_BAD_SHAPE
+    if NO_GPU:
+        assert lib.i8_head_logits_kmajor(A, 768, A, 768, A, 10, A, None) == w4.W4_ERR_DEVICE
+        assert lib.i8_prepack_head(A, 768, 10, 16, A, 768, None) == w4.W4_ERR_DEVICE

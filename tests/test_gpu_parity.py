@@ -309,6 +309,92 @@ def test_embed():
 
 
 # --------------------------------------------------------------------------
+# int8 head on the token-major table (integer MFMA)
+# --------------------------------------------------------------------------
+def token_major(Q, N, ldt):
+    """The oracle's table [K, ldq] as rows per token, zero-padded to ldt."""
+    K = Q.shape[0]
+    Qt = np.zeros((N, ldt), np.int8)
+    Qt[:, :K] = Q[:, :N].T
+    return Qt
+
+
+@pytest.mark.parametrize("K,N,ldq,ldt", [(768, 50257, 50272, 768), (64, 300, 301, 64),
+                                         (100, 37, 48, 112), (33, 1000, 1003, 48)])
+def test_head_prepack_bit_exact(K, N, ldq, ldt):
+    note(f"head prepack K={K} N={N} ldq={ldq} ldt={ldt}")
+    cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 221
+    Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=cfg), ldq=ldq)
+    Qt = w4.i8_prepack_head(dev(Q), N, ldt=ldt)
+    assert_bits(host(Qt), token_major(Q, N, ldt), f"head token-major {K}x{N}")
+
+
+def head_kmajor_case(K, N, ldt, x, label):
+    cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 222
+    E = synth.head_table(K, N, cfg=cfg)
+    if N > 10:
+        E[:, 5] = 0.0
+    Q, hs = ORC.i8_quantize_head(E, ldq=N)
+    Qt = dev(token_major(Q, N, ldt))
+    logits = host(w4.i8_head_logits_kmajor(dev(x), Qt, dev(hs), K))
+    ref, bound = ORC.i8_head_logits(x, Q, hs)
+    assert_bound(logits, ref, bound, label)
+
+
+@pytest.mark.parametrize("K,N,ldt", [(768, 50257, 768), (768, 50257, 784), (64, 300, 64),
+                                     (128, 37, 144), (256, 1000, 256), (512, 77, 512),
+                                     (1024, 515, 1024), (2048, 130, 2048), (8192, 70, 8192)])
+def test_head_kmajor(K, N, ldt):
+    note(f"head kmajor K={K} N={N} ldt={ldt}")
+    cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 223
+    x = synth.activations(58, K, cfg=cfg, outliers=True)[-1]
+    head_kmajor_case(K, N, ldt, x, f"head kmajor {K}x{N}/{ldt}")
+
+
+def test_head_kmajor_special_inputs():
+    K, N = 768, 3000
+    cases = {
+        "one-hot": np.eye(1, K, 17, dtype=np.float32)[0],
+        "zeros": np.zeros(K, np.float32),
+        "tiny": synth.activations(1, K, cfg=224)[0] * np.float32(1e-30),
+        "huge": synth.activations(1, K, cfg=225)[0] * np.float32(1e30),
+        "negative max": -np.abs(synth.activations(1, K, cfg=226)[0]),
+    }
+    spread = synth.activations(1, K, cfg=227)[0]
+    spread[::7] *= np.float32(1000.0)          # three decades between entries
+    spread[3::7] *= np.float32(1e-3)
+    cases["spread"] = spread
+    for name, x in cases.items():
+        note(f"head kmajor x={name}")
+        head_kmajor_case(K, N, K, x.astype(np.float32), f"head kmajor x={name}")
+
+
+def test_head_kmajor_nonfinite_gives_nan():
+    K, N = 128, 50
+    Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=228), ldq=N)
+    x = synth.activations(1, K, cfg=228)[0]
+    x[9] = np.inf
+    logits = host(w4.i8_head_logits_kmajor(dev(x), dev(token_major(Q, N, K)), dev(hs), K))
+    assert np.isnan(logits).all()
+
+
+def test_embed_kmajor():
+    K, N = 768, 50257
+    E = synth.head_table(K, N)
+    Q, hs = ORC.i8_quantize_head(E, ldq=N)
+    Qt = dev(token_major(Q, N, 768))
+    toks = synth.tokens(58, N, cfg=synth.CFG_HEAD)
+    toks[0], toks[-1] = 0, N - 1
+    out = w4.i8_embed_kmajor(dev(toks), Qt, dev(hs), K)
+    assert_bits(host(out), ORC.i8_embed(toks, Q, hs), "token-major embedding rows")
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad = np.array([3, N, -1], np.int64)
+    out = host(w4.i8_embed_kmajor(dev(bad), Qt, dev(hs), K, d_status=st))
+    assert host(st)[0] == w4.W4_ERR_BAD_SHAPE
+    assert not out[1:].any()
+
+
+# --------------------------------------------------------------------------
 # K-major (prepacked) layout and its GEMV
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("K,N", [(64, 34), (768, 2304), (3072, 768), (192, 530)])
@@ -340,8 +426,58 @@ def test_kmajor_matmul(M, K, N):
     assert_bound(y, y_ref, bound, f"kmajor M={M} {K}x{N}")
 
 
+X3_SHAPES = [(128, 16), (768, 768), (768, 2304), (3072, 768), (1024, 1008), (256, 530),
+             (8192, 512), (128, 2), (640, 4112), (384, 96), (3072, 3072)]
+
+
+@pytest.mark.parametrize("K,N", X3_SHAPES)
+@pytest.mark.parametrize("M", [5, 16, 17, 58, 64, 65, 130])
+def test_kmajor_matrix_cores(M, K, N):
+    """M > 4 on the bf16 matrix cores (split-K, ragged N, partial m-tiles)."""
+    note(f"kmajor x3 M={M} K={K} N={N} ws={w4.w4_matmul_kmajor_workspace_bytes(M, K, N)}")
+    W = mixed_weights(K, N, cfg=232)
+    x = synth.activations(M, K, cfg=232, slot=M, outliers=True)
+    b = synth.bias(N, cfg=232)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z, b)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y, y_ref, bound, f"kmajor x3 M={M} {K}x{N}")
+
+
+def test_kmajor_matrix_cores_special_inputs():
+    K, N, M = 768, 2304, 16
+    W = mixed_weights(K, N, cfg=233)
+    Wq, s, z = ORC.quantize_pack(W)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    base = synth.activations(M, K, cfg=233)
+    cases = {"zeros": np.zeros((M, K), np.float32),
+             "one-hot rows": np.eye(M, K, 5, dtype=np.float32),
+             "tiny": base * np.float32(1e-30),
+             "huge": base * np.float32(1e30),
+             "spread": base * np.where(np.arange(K) % 3 == 0, 1e3, 1e-3).astype(np.float32)}
+    for name, x in cases.items():
+        y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+        y = host(w4.w4_matmul_kmajor(dev(x), *P))
+        assert_bound(y, y_ref, bound, f"kmajor x3 x={name}")
+
+
+def test_kmajor_matrix_cores_deterministic_with_dirty_workspace():
+    K, N, M = 3072, 768, 16
+    W = mixed_weights(K, N, cfg=234)
+    P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
+    x = dev(synth.activations(M, K, cfg=234))
+    need = w4.w4_matmul_kmajor_workspace_bytes(M, K, N)
+    assert need > 0
+    ws = torch.full((need + 256,), 0x7F, dtype=torch.uint8, device=DEV)
+    y1 = host(w4.w4_matmul_kmajor(x, *P, workspace=ws))
+    ws.fill_(0xFF)
+    y2 = host(w4.w4_matmul_kmajor(x, *P, workspace=ws))
+    assert_bits(y1, y2, "x3 repeat")
+
+
 @pytest.mark.parametrize("slot", range(4))
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 4, 16])
 def test_dense38_kmajor_full_size_sampled(slot, M):
     """Full-size 3.8B-dense shapes on the K-major path the benchmark times."""
     K, N = synth.DENSE38_SHAPES[slot]
@@ -360,5 +496,5 @@ def test_dense38_kmajor_full_size_sampled(slot, M):
 def test_kmajor_rejects_bad_shapes():
     lib = w4.library()
     A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
-    assert lib.w4_matmul_kmajor(A, 1, 96, A, A, A, 16, None, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_matmul_kmajor(A, 1, 96, A, A, A, 16, None, A, None, 0, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.w4_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE

@@ -45,12 +45,17 @@ _SIGS = {
     "w4_matmul": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "w4_check_matmul_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
     "w4_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
-    "w4_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
-    "w4_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "w4_matmul_kmajor_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "w4_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
+    "w4_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
     "i8_quantize_head": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "i8_head_workspace_bytes": (_SZ, [_I64, _I64]),
     "i8_head_logits": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "i8_embed": (_INT, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _P, _P]),
+    "i8_prepack_head": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _P]),
+    "i8_check_head_logits_kmajor_args": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P]),
+    "i8_head_logits_kmajor": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P]),
+    "i8_embed_kmajor": (_INT, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -216,8 +221,13 @@ def w4_prepack_kmajor(Wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tenso
     return Pq, Ps, Pz
 
 
+def w4_matmul_kmajor_workspace_bytes(M: int, K: int, N: int) -> int:
+    return _lib.w4_matmul_kmajor_workspace_bytes(M, K, N)
+
+
 def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: torch.Tensor,
-                     bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+                     bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
     """y fp32 [M, N] = x [M, K] . dequantize(K-major weights) (+ bias)."""
     _dev(x, torch.float32, "x")
     _dev(Pq, torch.uint8, "Pq")
@@ -233,9 +243,15 @@ def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: to
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     else:
         _dev(out, torch.float32, "out")
+    need = _lib.w4_matmul_kmajor_workspace_bytes(M, K, N)
+    if workspace is None:
+        ws, wsb = _workspace.get(x.device, need) if need else (None, 0)
+    else:
+        _dev(workspace, torch.uint8, "workspace")
+        ws, wsb = workspace, workspace.numel()
     _check("w4_matmul_kmajor", _lib.w4_matmul_kmajor(
         _ptr(x), M, K, _ptr(Pq), _ptr(Ps), _ptr(Pz), N, _ptr(bias), _ptr(out),
-        _stream(x.device)))
+        _ptr(ws), wsb, _stream(x.device)))
     return out
 
 
@@ -295,4 +311,49 @@ def i8_embed(tokens: torch.Tensor, Q: torch.Tensor, hs: torch.Tensor,
         _dev(d_status, torch.int32, "d_status")
     _check("i8_embed", _lib.i8_embed(_ptr(tokens), T, _ptr(Q), ldq, _ptr(hs), K, N, _ptr(out),
                                      _ptr(d_status), _stream(Q.device)))
+    return out
+
+
+def i8_prepack_head(Q: torch.Tensor, N: int, ldt: int | None = None) -> torch.Tensor:
+    """Q int8 [K, ldq] (N used columns) -> token-major copy Qt int8 [N, ldt]."""
+    _dev(Q, torch.int8, "Q")
+    K, ldq = Q.shape
+    if ldt is None:
+        ldt = (K + 15) // 16 * 16
+    Qt = torch.empty((N, ldt), dtype=torch.int8, device=Q.device)
+    _check("i8_prepack_head", _lib.i8_prepack_head(_ptr(Q), K, N, ldq, _ptr(Qt), ldt,
+                                                   _stream(Q.device)))
+    return Qt
+
+
+def i8_head_logits_kmajor(x_last: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor, K: int,
+                          out: torch.Tensor | None = None):
+    """x_last fp32 [K] -> logits fp32 [N] from the token-major table Qt [N, ldt]."""
+    _dev(x_last, torch.float32, "x_last")
+    _dev(Qt, torch.int8, "Qt")
+    _dev(hs, torch.float32, "hs")
+    N, ldt = Qt.shape
+    if x_last.numel() != K or hs.numel() != N:
+        raise ValueError("x_last must have K elements and hs N")
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=Qt.device)
+    _check("i8_head_logits_kmajor",
+           _lib.i8_head_logits_kmajor(_ptr(x_last), K, _ptr(Qt), ldt, _ptr(hs), N, _ptr(out),
+                                      _stream(Qt.device)))
+    return out
+
+
+def i8_embed_kmajor(tokens: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor, K: int,
+                    d_status: torch.Tensor | None = None):
+    """tokens int64 [T] -> fp32 [T, K] (rows of the dequantized token-major table)."""
+    _dev(tokens, torch.int64, "tokens")
+    _dev(Qt, torch.int8, "Qt")
+    _dev(hs, torch.float32, "hs")
+    N, ldt = Qt.shape
+    T = tokens.numel()
+    out = torch.empty((T, K), dtype=torch.float32, device=Qt.device)
+    if d_status is not None:
+        _dev(d_status, torch.int32, "d_status")
+    _check("i8_embed_kmajor", _lib.i8_embed_kmajor(_ptr(tokens), T, _ptr(Qt), ldt, _ptr(hs), K, N,
+                                                   _ptr(out), _ptr(d_status), _stream(Qt.device)))
     return out

@@ -164,30 +164,47 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
     return launched(w4::launch_prepack_kmajor(Wq, scales, zeros, K, N, Pq, Ps, Pz, as_stream(stream)));
 }
 
+size_t w4_matmul_kmajor_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || K < 0 || N < 0) return 0;
+    return w4::plan_x3(M, K, N).workspace;
+}
+
 int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                                 const float *Ps, const uint8_t *Pz, int64_t N, const float *bias,
-                                const float *y) {
+                                const float *y, const void *workspace, size_t workspace_bytes) {
     if (M < 0) return W4_ERR_BAD_SHAPE;
     int st = check_w4_shape(K, N);
     if (st) return st;
     if (K % 64 != 0) return W4_ERR_BAD_SHAPE;
     if (M > kMaxElems / (K > 0 ? K : 1) || M > kMaxElems / (N > 0 ? N : 1)) return W4_ERR_BAD_SHAPE;
     if (M == 0 || N == 0) return W4_OK;
-    // the K-major kernel indexes with 32-bit offsets
+    // the K-major kernels index with 32-bit offsets
     if (K * N >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) || M * N >= ((int64_t)1 << 31))
         return W4_ERR_BAD_SHAPE;
     if (!need(x, M * K) || !y) return W4_ERR_NULL_PTR;
     if ((st = check_packed(Pq, Ps, Pz, K, N))) return st;
     if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4)) return W4_ERR_MISALIGNED;
+    const size_t need_ws = w4::plan_x3(M, K, N).workspace;
+    if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return W4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
     return W4_OK;
 }
 
 int w4_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
-                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *stream) {
-    int st = w4_check_matmul_kmajor_args(x, M, K, Pq, Ps, Pz, N, bias, y);
+                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    int st = w4_check_matmul_kmajor_args(x, M, K, Pq, Ps, Pz, N, bias, y, workspace,
+                                         workspace_bytes);
     if (st) return st;
     if (M == 0 || N == 0) return W4_OK;
     if ((st = device_check())) return st;
+    if (K == 0)
+        return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, Pz, N,
+                                               bias, y, as_stream(stream)));
+    const w4::X3Plan px = w4::plan_x3(M, K, N);
+    if (px.kind == w4::X3Plan::kRun)
+        return launched(w4::launch_mm_x3(px, x, M, K, Pq, Ps, Pz, N, bias, y, workspace,
+                                         as_stream(stream)));
     return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, Pz, N, bias,
                                            y, as_stream(stream)));
 }
@@ -242,6 +259,60 @@ int i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq, con
     int st = device_check();
     if (st) return st;
     return launched(w4::launch_embed(tokens, T, Q, ldq, hs, K, N, out, d_status, as_stream(stream)));
+}
+
+int i8_prepack_head(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *Qt,
+                    int64_t ldt, void *stream) {
+    if (K < 0 || N < 0 || ldq < N || ldt < K || ldt % 16 != 0) return W4_ERR_BAD_SHAPE;
+    if (K > kMaxElems / (ldq > 0 ? ldq : 1) || N > kMaxElems / (ldt > 0 ? ldt : 1) ||
+        (ldt + 63) / 64 > 65535)
+        return W4_ERR_BAD_SHAPE;
+    if (N == 0 || ldt == 0) return W4_OK;
+    if (!need(Q, K * ldq) || !Qt) return W4_ERR_NULL_PTR;
+    if (!aligned(Q, 16) || !aligned(Qt, 16)) return W4_ERR_MISALIGNED;
+    int st = device_check();
+    if (st) return st;
+    return launched(w4::launch_head_prepack(Q, K, N, ldq, Qt, ldt, as_stream(stream)));
+}
+
+int i8_check_head_logits_kmajor_args(const float *x_last, int64_t K, const int8_t *Qt,
+                                     int64_t ldt, const float *hs, int64_t N,
+                                     const float *logits) {
+    if (K < 64 || K % 64 != 0 || K > 8192 || N < 0 || ldt < K || ldt % 16 != 0)
+        return W4_ERR_BAD_SHAPE;
+    if (N > 0 && N > ((int64_t)1 << 31) / ldt - 1) return W4_ERR_BAD_SHAPE;
+    if (N == 0) return W4_OK;
+    if (!x_last || !Qt || !hs || !logits) return W4_ERR_NULL_PTR;
+    if (!aligned(x_last, 16) || !aligned(Qt, 16) || !aligned(hs, 4) || !aligned(logits, 4))
+        return W4_ERR_MISALIGNED;
+    return W4_OK;
+}
+
+int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int64_t ldt,
+                          const float *hs, int64_t N, float *logits, void *stream) {
+    int st = i8_check_head_logits_kmajor_args(x_last, K, Qt, ldt, hs, N, logits);
+    if (st) return st;
+    if (N == 0) return W4_OK;
+    if ((st = device_check())) return st;
+    return launched(
+        w4::launch_head_logits_kmajor(x_last, K, Qt, ldt, hs, N, logits, as_stream(stream)));
+}
+
+int i8_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t ldt,
+                    const float *hs, int64_t K, int64_t N, float *out, int *d_status,
+                    void *stream) {
+    if (T < 0 || K < 0 || N < 0 || ldt < K || ldt % 16 != 0) return W4_ERR_BAD_SHAPE;
+    if (N > kMaxElems / (ldt > 0 ? ldt : 1) || T > kMaxElems / (K > 0 ? K : 1))
+        return W4_ERR_BAD_SHAPE;
+    if (T * K == 0) return W4_OK;
+    if (!tokens || !Qt || !hs || !out) return W4_ERR_NULL_PTR;
+    if (!aligned(tokens, 8) || !aligned(Qt, 16) || !aligned(hs, 4) || !aligned(out, 4) ||
+        !aligned(d_status, 4))
+        return W4_ERR_MISALIGNED;
+    int st = device_check();
+    if (st) return st;
+    return launched(
+        w4::launch_embed_kmajor(tokens, T, Qt, ldt, hs, K, N, out, d_status, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -44,5 +44,16 @@ hipError_t launch_head_logits(const HeadPlan &plan, const float *x, int64_t K, c
 hipError_t launch_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
                         const float *hs, int64_t K, int64_t N, float *out, int *d_status,
                         hipStream_t stream);
+hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                        const float *Ps, const uint8_t *Pz, int64_t N, const float *bias, float *y,
+                        void *workspace, hipStream_t stream);
+hipError_t launch_head_prepack(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *Qt,
+                               int64_t ldt, hipStream_t stream);
+hipError_t launch_head_logits_kmajor(const float *x, int64_t K, const int8_t *Qt, int64_t ldt,
+                                     const float *hs, int64_t N, float *logits,
+                                     hipStream_t stream);
+hipError_t launch_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t ldt,
+                               const float *hs, int64_t K, int64_t N, float *out, int *d_status,
+                               hipStream_t stream);
 
 }  // namespace w4

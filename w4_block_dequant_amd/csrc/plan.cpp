@@ -191,4 +191,46 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N) {
     return p;
 }
 
+X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
+    X3Plan p;
+    if (M <= 4 || K <= 0 || N <= 0 || K % 128 != 0) return p;
+    p.kind = X3Plan::kRun;
+    const int64_t rows = M < 64 ? M : 64;
+    p.mt = (int)cdiv(rows, 16);
+    static const int64_t env_nt = env_int("W4_X3_NT");
+    p.nt = (env_nt == 2 && p.mt <= 2) ? 2 : 1;
+    p.dq = p.mt <= 2 ? 3 : 2;
+    if (p.mt == 2 && p.nt == 2) p.dq = 2;
+    p.col_wgs = cdiv(N, 64 * p.nt);
+    p.mgroups = cdiv(M, 64);
+    p.npad = p.col_wgs * 64 * p.nt;
+    const int64_t NQ = K / 128;
+    // enough workgroups to fill the chip; larger row tiles carry more matrix
+    // work per weight byte, so fewer (and less split-K partial traffic)
+    static const int64_t env_wgs = env_int("W4_X3_TARGET_WGS");
+    const int64_t target = env_wgs > 0 ? env_wgs : (p.mt <= 2 ? 512 : 256);
+    int64_t splits = cdiv(target, p.col_wgs * p.mgroups);
+    if (splits > NQ) splits = NQ;
+    if (splits < 1) splits = 1;
+    const int64_t want = cdiv(NQ, splits);  // quads per workgroup, then the largest
+    static const int allowed[] = {12, 8, 6, 4, 3, 2, 1};  // instantiated count <= want
+    p.quads_per_wg = 1;
+    for (int a : allowed)
+        if (a <= want) {
+            p.quads_per_wg = a;
+            break;
+        }
+    p.splits = cdiv(NQ, p.quads_per_wg);
+    p.workspace = splitk_bytes(p.splits, p.npad, M);
+    return p;
+}
+
+int plan_head_kmajor_waves(int64_t K, int64_t N) {
+    (void)N;
+    static const int64_t env_w = env_int("W4_HEAD_MFMA_WAVES");
+    if (K > 1024) return 4;
+    if (env_w == 1 || env_w == 2 || env_w == 4) return (int)env_w;
+    return 4;
+}
+
 }  // namespace w4

@@ -72,4 +72,22 @@ struct KmajorPlan {
 
 KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N);
 
+// ---- M > 4 rows on the K-major layout: bf16 matrix cores, fp32 accuracy ------
+// Workgroup: 4 waves x nt tiles of 16 columns, all rows of one 64-row group
+// (mt tiles of 16), quads_per_wg quads of 4 K-blocks; grid = col_wgs x
+// splits x mgroups.  dq quads of loads in flight.  Needs K % 128 == 0.
+struct X3Plan {
+    enum Kind { kNone = 0, kRun = 1 } kind = kNone;
+    int mt = 1, nt = 1, dq = 2;
+    int64_t col_wgs = 0, mgroups = 0, splits = 1, quads_per_wg = 0, npad = 0;
+    size_t workspace = 0;
+};
+
+X3Plan plan_x3(int64_t M, int64_t K, int64_t N);
+
+// ---- int8 head on the token-major table ---------------------------------------
+// Waves per workgroup (1, 2 or 4) of the integer-MFMA head; each wave owns a
+// 16-token tile over all of K.  K > 1024 always takes 4.
+int plan_head_kmajor_waves(int64_t K, int64_t N);
+
 }  // namespace w4
