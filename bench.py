@@ -398,6 +398,24 @@ def main():
                                 "GB_s": round((tbytes + hb_lane) / (us * 1e-6) / 1e9, 1)}
         secondary["i8_head_768x50257"] = head_times
 
+        # full-sequence logits [58 x 50257] (the export before the last-position
+        # slice): one launch over the token-major table, 8 table copies in turn
+        xs = torch.from_numpy(synth.activations(synth.GPT2_PROMPT, synth.GPT2_HIDDEN,
+                                                synth.CFG_HEAD)).to(dev)
+        outs = torch.empty((synth.GPT2_PROMPT, synth.GPT2_VOCAB), device=dev)
+        tabs = [Qk.clone() for _ in range(8)]
+        gs = capture(lambda: [w4.i8_head_logits_rows(xs, tabs[i % 8], hsk, out=outs)
+                              for i in range(16)])
+        mss, _ = time_graph(gs, 10, 2)
+        del gs, tabs
+        us = 1e3 * mss / 16
+        fb = (synth.GPT2_HIDDEN * synth.GPT2_VOCAB + 4 * synth.GPT2_VOCAB
+              + 4 * synth.GPT2_PROMPT * (synth.GPT2_HIDDEN + synth.GPT2_VOCAB))
+        ff = 2 * synth.GPT2_PROMPT * synth.GPT2_HIDDEN * synth.GPT2_VOCAB
+        secondary["i8_head_full_sequence_58x768x50257"] = {
+            "us": round(us, 3), "GB_s": round(fb / (us * 1e-6) / 1e9, 1),
+            "TOP_s_equiv": round(ff / (us * 1e-6) / 1e12, 2)}
+
         pre = with_x(gpt2, synth.CFG_GPT2_PREFILL, synth.GPT2_PROMPT, outliers=False)
         last = pre[-1]
         lg = torch.empty(synth.GPT2_VOCAB, device=dev)

@@ -220,6 +220,19 @@ int i8_check_head_logits_kmajor_args(const float *x_last, int64_t K, const int8_
 int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int64_t ldt,
                           const float *hs, int64_t N, float *logits, void *stream);
 
+/* Full-sequence logits (the page's export before the last-position slice of
+ * step 4): logits[m, n] = hs[n] * sum_k x[m, k] * Qt[n, k] for every row m of
+ * x [M, K] (fp32, row-major, 4-byte aligned), logits [M, N] fp32.  Same
+ * arithmetic and precision condition as i8_head_logits_kmajor, with one
+ * exponent per row.  K % 64 == 0, K <= 2048; N * ldt < 2^31; one launch,
+ * no workspace.                                                             */
+int i8_check_head_logits_rows_args(const float *x, int64_t M, int64_t K, const int8_t *Qt,
+                                   int64_t ldt, const float *hs, int64_t N,
+                                   const float *logits);
+
+int i8_head_logits_rows(const float *x, int64_t M, int64_t K, const int8_t *Qt, int64_t ldt,
+                        const float *hs, int64_t N, float *logits, void *stream);
+
 /* Token lookup from Qt (step 3): out[t, k] = fl32(Qt[tokens[t], k] * hs[tokens[t]]),
  * fp32 [T, K], bit-exact; ids outside [0, N) as in i8_embed.               */
 int i8_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t ldt,

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                  "i8_quantize_head", "i8_embed", "w4_matmul_workspace_bytes",
                  "i8_head_workspace_bytes", "w4_check_matmul_args", "w4_strerror",
                  "w4_abi_version", "i8_prepack_head", "i8_head_logits_kmajor",
-                 "i8_check_head_logits_kmajor_args", "i8_embed_kmajor"):
+                 "i8_check_head_logits_kmajor_args", "i8_embed_kmajor",
+                 "i8_head_logits_rows", "i8_check_head_logits_rows_args"):
         assert must in names
 
 
@@ -176,3 +177,18 @@ def test_head_kmajor_checks():
     if NO_GPU:
         assert lib.i8_head_logits_kmajor(A, 768, A, 768, A, 10, A, None) == w4.W4_ERR_DEVICE
         assert lib.i8_prepack_head(A, 768, 10, 16, A, 768, None) == w4.W4_ERR_DEVICE
+
+
+def test_head_rows_checks():
+    chk = w4.library().i8_check_head_logits_rows_args
+    assert chk(A, 58, 768, A, 768, A, 50257, A) == w4.W4_OK
+    assert chk(A, 58, 4096, A, 4096, A, 100, A) == w4.W4_ERR_BAD_SHAPE   # K > 2048
+    assert chk(A, 58, 800, A, 800, A, 100, A) == w4.W4_ERR_BAD_SHAPE     # K % 64 != 0
+    assert chk(A, -1, 768, A, 768, A, 100, A) == w4.W4_ERR_BAD_SHAPE
+    assert chk(None, 0, 768, None, 768, None, 100, None) == w4.W4_OK
+    assert chk(A, 2, 768, None, 768, A, 100, A) == w4.W4_ERR_NULL_PTR
+    assert chk(A + 2, 2, 768, A, 768, A, 100, A) == w4.W4_ERR_MISALIGNED
+    assert chk(A, 2, 768, A + 8, 768, A, 100, A) == w4.W4_ERR_MISALIGNED
+    if NO_GPU:
+        assert w4.library().i8_head_logits_rows(A, 2, 768, A, 768, A, 100, A, None) == \
+            w4.W4_ERR_DEVICE

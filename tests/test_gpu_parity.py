@@ -378,6 +378,40 @@ def test_head_kmajor_nonfinite_gives_nan():
     assert np.isnan(logits).all()
 
 
+@pytest.mark.parametrize("M,K,N,ldt", [(58, 768, 50257, 768), (1, 768, 50257, 784), (3, 768, 4099, 768),
+                                       (5, 64, 300, 64), (9, 128, 37, 144), (6, 2048, 130, 2048),
+                                       (17, 512, 1000, 512), (4, 1024, 515, 1024)])
+def test_head_rows(M, K, N, ldt):
+    """Full-sequence logits: every row of x against the oracle's head."""
+    note(f"head rows M={M} K={K} N={N} ldt={ldt}")
+    cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 229
+    E = synth.head_table(K, N, cfg=cfg)
+    if N > 10:
+        E[:, 5] = 0.0
+    Q, hs = ORC.i8_quantize_head(E, ldq=N)
+    x = synth.activations(M, K, cfg=cfg, outliers=True)
+    got = host(w4.i8_head_logits_rows(dev(x), dev(token_major(Q, N, ldt)), dev(hs)))
+    refs = [ORC.i8_head_logits(x[m], Q, hs) for m in range(M)]
+    ref = np.stack([r[0] for r in refs])
+    bound = np.stack([r[1] for r in refs])
+    assert_bound(got, ref, bound, f"head rows {M}x{K}x{N}")
+
+
+def test_head_rows_special_rows():
+    K, N, M = 768, 2000, 6
+    Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=230), ldq=N)
+    x = synth.activations(M, K, cfg=230)
+    x[1] = 0.0                                   # all-zero row
+    x[2] *= np.float32(1e-30)                    # tiny row beside normal ones
+    x[3, 11] = np.inf                            # non-finite row: NaN logits, others unaffected
+    x[4] *= np.float32(1e30)
+    got = host(w4.i8_head_logits_rows(dev(x), dev(token_major(Q, N, K)), dev(hs)))
+    assert np.isnan(got[3]).all()
+    for m in (0, 1, 2, 4, 5):
+        ref, bound = ORC.i8_head_logits(x[m], Q, hs)
+        assert_bound(got[m], ref, bound, f"head rows special row {m}")
+
+
 def test_embed_kmajor():
     K, N = 768, 50257
     E = synth.head_table(K, N)

@@ -56,6 +56,8 @@ _SIGS = {
     "i8_check_head_logits_kmajor_args": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P]),
     "i8_head_logits_kmajor": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P]),
     "i8_embed_kmajor": (_INT, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _P, _P]),
+    "i8_check_head_logits_rows_args": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "i8_head_logits_rows": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -356,4 +358,21 @@ def i8_embed_kmajor(tokens: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor, K:
         _dev(d_status, torch.int32, "d_status")
     _check("i8_embed_kmajor", _lib.i8_embed_kmajor(_ptr(tokens), T, _ptr(Qt), ldt, _ptr(hs), K, N,
                                                    _ptr(out), _ptr(d_status), _stream(Qt.device)))
+    return out
+
+
+def i8_head_logits_rows(x: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor,
+                        out: torch.Tensor | None = None):
+    """x fp32 [M, K] -> logits fp32 [M, N] for every row (token-major table Qt [N, ldt])."""
+    _dev(x, torch.float32, "x")
+    _dev(Qt, torch.int8, "Qt")
+    _dev(hs, torch.float32, "hs")
+    M, K = x.shape
+    N, ldt = Qt.shape
+    if hs.numel() != N:
+        raise ValueError("hs must have N elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=Qt.device)
+    _check("i8_head_logits_rows", _lib.i8_head_logits_rows(
+        _ptr(x), M, K, _ptr(Qt), ldt, _ptr(hs), N, _ptr(out), _stream(Qt.device)))
     return out

@@ -177,6 +177,146 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits_mfma(const float *__
     }
 }
 
+// Full-sequence logits: 4 rows of x per workgroup.  A-operand row 4 r + l is
+// digit l of row r (each row has its own exponent e_r), so all 16 rows of the
+// MFMA carry data and lane (g, c) ends with the four digit sums of row g,
+// column c.  The table is the same B operand as above.  Workgroups that share
+// a 64-token tile (one per group of 4 rows) are given ids that map to the same
+// XCD (ids are dealt to the 8 XCDs in turn), so the tile's table rows come
+// from HBM about once and from that XCD's L2 for the other row groups.
+template <int CH, int XPT>
+__global__ __launch_bounds__(256) void k_head_rows_mfma(const float *__restrict__ x, int M, int K,
+                                                        const int8_t *__restrict__ Qt, int ldt,
+                                                        const float *__restrict__ hs, int N,
+                                                        float *__restrict__ logits, int ntiles,
+                                                        int nrg) {
+    extern __shared__ i32x4_t limbs_v[];  // [16][K] bytes: row 4 r + l = digit l of row r
+    int8_t *limbs = reinterpret_cast<int8_t *>(limbs_v);
+    __shared__ float wmax[4][4];
+    const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+    const int tile = (local / nrg) * 8 + xcd, rg = local % nrg;
+    if (tile >= ntiles) return;  // whole workgroup, before any barrier
+    const int m0 = 4 * rg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int nbase = tile * 64 + wave * 16;
+    const int n = min(nbase + c, N - 1);
+    const int NJ = K / 64, RK = 4 * K;
+
+    // x of the 4 rows first, then the table rows (as in the 1-row kernel)
+    float xv[XPT];  // element e = tid + 256 i of the 4 x K block
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int e = min(tid + 256 * i, RK - 1);
+        const int r = e / K;
+        xv[i] = x[(size_t)min(m0 + r, M - 1) * K + (e - r * K)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t rowoff = (uint32_t)n * (uint32_t)ldt + 16u * g;
+    u32x4_t b[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+        b[j] = load_stream<u32x4_t>(Qt + rowoff + 64u * (uint32_t)min(j, NJ - 1));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // per-row max |x| (a non-finite entry makes its row's max infinite)
+    float mr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int e = tid + 256 * i;
+        const int r = e / K;
+        const bool valid = e < RK && m0 + r < M;
+        if (!valid) xv[i] = 0.0f;
+        const float a = __builtin_isfinite(xv[i]) ? __builtin_fabsf(xv[i]) : __builtin_inff();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mr[q] = (r == q) ? __builtin_fmaxf(mr[q], a) : mr[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mr[q] = __builtin_fmaxf(mr[q], __shfl_xor(mr[q], o));
+        if (lane == 0) wmax[wave][q] = mr[q];
+    }
+    __syncthreads();
+    int er[4];
+    bool okr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float am = __builtin_fmaxf(__builtin_fmaxf(wmax[0][q], wmax[1][q]),
+                                         __builtin_fmaxf(wmax[2][q], wmax[3][q]));
+        okr[q] = __builtin_isfinite(am);
+        er[q] = 0;
+        if (okr[q] && am > 0.0f) (void)__builtin_frexpf(am, &er[q]);
+    }
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int e = tid + 256 * i;
+        if (e < RK) {
+            const int r = e / K, k = e - r * K;
+            int eq = er[0];
+            bool oq = okr[0];
+#pragma unroll
+            for (int q = 1; q < 4; ++q)
+                if (r == q) {
+                    eq = er[q];
+                    oq = okr[q];
+                }
+            const int v = oq ? (int)__builtin_rintf(__builtin_ldexpf(xv[i], 30 - eq)) : 0;
+            const int l0 = (int)(int8_t)(v & 0xFF);
+            const int v1 = (v - l0) >> 8;
+            const int l1 = (int)(int8_t)(v1 & 0xFF);
+            const int v2 = (v1 - l1) >> 8;
+            const int l2 = (int)(int8_t)(v2 & 0xFF);
+            const int l3 = (v2 - l2) >> 8;
+            int8_t *lr = limbs + (4 * r) * K + k;
+            lr[0] = (int8_t)l0;
+            lr[K] = (int8_t)l1;
+            lr[2 * K] = (int8_t)l2;
+            lr[3 * K] = (int8_t)l3;
+        }
+    }
+    __syncthreads();
+
+    i32x4_t acc = {0, 0, 0, 0};
+    for (int j0 = 0; j0 < NJ; j0 += CH) {
+        if (j0 > 0) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                b[j] = load_stream<u32x4_t>(Qt + rowoff + 64u * (uint32_t)min(j0 + j, NJ - 1));
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int jj = j0 + j;
+            if (jj < NJ) {
+                const i32x4_t a =
+                    *reinterpret_cast<const i32x4_t *>(limbs + c * K + 64 * jj + 16 * g);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    a, __builtin_bit_cast(i32x4_t, b[j]), acc, 0, 0, 0);
+            }
+        }
+    }
+
+    // lane (g, c) holds the four digit sums of row m0 + g, column nbase + c
+    const int m = m0 + g;
+    if (m < M && nbase + c < N) {
+        int eg = er[0];
+        bool og = okr[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (g == q) {
+                eg = er[q];
+                og = okr[q];
+            }
+        float out = __builtin_nanf("");
+        if (og) {
+            const double t = ((double)acc[3] * 16777216.0 + (double)acc[2] * 65536.0) +
+                             ((double)acc[1] * 256.0 + (double)acc[0]);
+            out = (float)(__builtin_ldexp(t, eg - 30) * (double)hs[n]);
+        }
+        logits[(size_t)m * N + nbase + c] = out;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_head_prepack(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *Qt,
@@ -215,6 +355,24 @@ hipError_t launch_head_logits_kmajor(const float *x, int64_t K, const int8_t *Qt
     else W4_HK(16, 32, 4);
 #undef W4_HK3
 #undef W4_HK
+    return hipGetLastError();
+}
+
+hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const int8_t *Qt,
+                                  int64_t ldt, const float *hs, int64_t N, float *logits,
+                                  hipStream_t stream) {
+    const int ntiles = (int)((N + 63) / 64), nrg = (int)((M + 3) / 4);
+    const int64_t wgs = (int64_t)((ntiles + 7) / 8) * 8 * nrg;
+    const size_t shm = (size_t)16 * K;
+#define W4_HR(CHV, XV)                                                                            \
+    hipLaunchKernelGGL((k_head_rows_mfma<CHV, XV>), dim3((unsigned)wgs), dim3(256), shm, stream, x, \
+                       (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits, ntiles, nrg)
+    if (K <= 256) W4_HR(4, 4);
+    else if (K <= 512) W4_HR(8, 8);
+    else if (K <= 768) W4_HR(12, 12);
+    else if (K <= 1024) W4_HR(16, 16);
+    else W4_HR(16, 32);
+#undef W4_HR
     return hipGetLastError();
 }
 
