@@ -73,6 +73,10 @@ _SIGS = {
     "orc_i8_dequantize_head": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "orc_i8_head_logits": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_i8_embed": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _P]),
+    "orc_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
+    "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+    "orc_f16_array_to_f32": (None, [_P, _I64, _P]),
+    "orc_w4h_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
 }
 
 
@@ -204,6 +208,43 @@ class Oracle:
                                      _ptr(_c(scales, np.float32)), _ptr(_c(zeros, np.uint8)),
                                      N, _ptr(b), _ptr(y), _ptr(bound)))
         return y, bound
+
+    # -- fp16-scale variant ------------------------------------------------------
+    def f32_to_f16(self, v):
+        """fp32 array -> binary16 bit patterns (uint16), one oracle call per element."""
+        v = _c(v, np.float32).reshape(-1)
+        out = np.empty(v.size, np.uint16)
+        for i in range(v.size):
+            out[i] = self._l.orc_f32_to_f16(float(v[i]))
+        return out
+
+    def f16_to_f32(self, h):
+        """binary16 bit patterns -> fp32."""
+        h = _c(h, np.uint16)
+        out = np.empty(h.shape, np.float32)
+        self._l.orc_f16_array_to_f32(_ptr(h), h.size, _ptr(out))
+        return out
+
+    def quantize_pack_f16(self, W):
+        """W fp32 [K, N] -> (Wq uint8 [K, N/2], scales uint16 [K/32, N] (binary16), zeros)."""
+        W = _c(W, np.float32)
+        K, N = W.shape
+        Wq = np.zeros((K, N // 2), np.uint8)
+        s = np.zeros((K // BLOCK, N), np.uint16)
+        z = np.zeros((K // BLOCK, N // 2), np.uint8)
+        _check("orc_w4h_quantize_pack",
+               self._l.orc_w4h_quantize_pack(_ptr(W), K, N, _ptr(Wq), _ptr(s), _ptr(z)))
+        return Wq, s, z
+
+    def w4h_matmul(self, x, Wq, scales16, zeros, bias=None):
+        """The fp16-scale format's matmul: the scales' fp32 values, then w4_matmul."""
+        return self.w4_matmul(x, Wq, self.f16_to_f32(scales16), zeros, bias)
+
+    def prepack_kmajor_f16(self, Wq, scales16, zeros, K, N):
+        """K-major copy with binary16 scales: (Pq, Ps uint16 [N, K/32], Pz)."""
+        Pq, Ps, Pz = self.prepack_kmajor(Wq, self.f16_to_f32(scales16), zeros, K, N)
+        back = self.f32_to_f16(Ps).reshape(Ps.shape)  # exact: every value came from binary16
+        return Pq, back, Pz
 
     # -- int8 head -------------------------------------------------------------
     def i8_quantize_head(self, E, ldq=None):

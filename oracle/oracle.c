@@ -40,9 +40,12 @@ static int clamp_int(float v, int lo, int hi)
     return (int)v;
 }
 
-/* One block: 32 weights w[r * stride], r = 0..31.  Writes s, z and q[0..31]. */
-static int quantize_block(const float *w, int64_t stride, float *s_out, uint8_t *z_out,
-                          uint8_t *q_out)
+/* One block: 32 weights w[r * stride], r = 0..31.  Writes s, z and q[0..31].
+ * With s16_out != NULL the scale is stored as binary16 (the fp16-scale
+ * variant): s16 = binary16((hi - lo) / 15) goes to *s16_out and z, q are taken
+ * against its value; s16 infinite is ORC_NONFINITE, s16 == 0 gives zeros.   */
+static int quantize_block(const float *w, int64_t stride, float *s_out, uint16_t *s16_out,
+                          uint8_t *z_out, uint8_t *q_out)
 {
     float lo = 0.0f, hi = 0.0f; /* the range always contains 0 */
     for (int r = 0; r < BLOCK; ++r) {
@@ -54,8 +57,14 @@ static int quantize_block(const float *w, int64_t stride, float *s_out, uint8_t 
     float range = hi - lo;
     float s = range / 15.0f;
     if (!isfinite(s)) return ORC_NONFINITE;
+    if (s16_out) {
+        uint16_t h = orc_f32_to_f16(s);
+        if ((h & 0x7C00) == 0x7C00) return ORC_NONFINITE;
+        *s16_out = h;
+        s = orc_f16_to_f32(h); /* the stored value */
+    }
     if (s == 0.0f) { /* all-zero block: every code and the zero point are 0 */
-        *s_out = 0.0f;
+        if (s_out) *s_out = 0.0f;
         *z_out = 0;
         for (int r = 0; r < BLOCK; ++r) q_out[r] = 0;
         return ORC_OK;
@@ -66,7 +75,7 @@ static int quantize_block(const float *w, int64_t stride, float *s_out, uint8_t 
         float t = rintf(w[r * stride] / s);
         q_out[r] = (uint8_t)clamp_int(t + (float)z, 0, 15);
     }
-    *s_out = s;
+    if (s_out) *s_out = s;
     *z_out = (uint8_t)z;
     return ORC_OK;
 }
@@ -83,8 +92,8 @@ int orc_w4_quantize_pack(const float *W, int64_t K, int64_t N,
     uint8_t qcol[BLOCK];
     for (int64_t b = 0; b < nb && st == ORC_OK; ++b) {
         for (int64_t n = 0; n < N; ++n) {
-            st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[b * N + n], &z[b * N + n],
-                                qcol);
+            st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[b * N + n], NULL,
+                                &z[b * N + n], qcol);
             if (st != ORC_OK) break;
             for (int r = 0; r < BLOCK; ++r) q[(b * BLOCK + r) * N + n] = qcol[r];
         }
@@ -248,4 +257,78 @@ int orc_i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
             out[t * K + k] = (float)((double)Q[k * ldq + tok] * (double)hs[tok]);
     }
     return ORC_OK;
+}
+
+/* ---- fp16-scale variant ------------------------------------------------------ */
+
+/* fp32 -> IEEE binary16 (1 sign bit, 5 exponent bits with bias 15, 10 fraction
+ * bits), rounded to nearest with ties to even.  Straight from the format: the
+ * representable values near |f| are the multiples of a quantum, 2^(e-10) for
+ * a normal value with exponent e in [-14, 15] and 2^-24 below 2^-14, so |f| is
+ * rounded to a multiple of its quantum with rint (ties to even), in double,
+ * where the division by a power of two and rint are exact.  |f| >= 65520 (the
+ * midpoint above 65504, rounding to even = upward) becomes infinity.        */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f)) return (uint16_t)(sign | 0x7E00);
+    double a = fabs((double)f);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e); /* a = m 2^e, m in [0.5, 1): the binary exponent of a is e - 1 */
+    int be = e - 1;
+    if (be < -14) be = -14; /* subnormal range: quantum 2^-24 */
+    double quantum = ldexp(1.0, be - 10);
+    double units = rint(a / quantum); /* in [0, 2048] */
+    double v = units * quantum;       /* the rounded magnitude */
+    if (v == 0.0) return sign;
+    if (v < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)units); /* subnormal */
+    frexp(v, &e);
+    int ev = e - 1; /* exponent of the rounded value (may be be + 1) */
+    double frac = v / ldexp(1.0, ev) - 1.0; /* in [0, 1), a multiple of 2^-10 */
+    return (uint16_t)(sign | (uint16_t)((ev + 15) << 10) | (uint16_t)(frac * 1024.0));
+}
+
+/* IEEE binary16 -> fp32 (exact: every binary16 value is an fp32 value).      */
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1, ex = (h >> 10) & 31, fr = h & 1023;
+    double v;
+    if (ex == 0) v = ldexp((double)fr, -24);
+    else if (ex == 31) v = fr ? NAN : INFINITY;
+    else v = ldexp(1.0 + fr / 1024.0, ex - 15);
+    return (float)(sign ? -v : v);
+}
+
+int orc_w4h_quantize_pack(const float *W, int64_t K, int64_t N,
+                          uint8_t *Wq, uint16_t *scales, uint8_t *zeros)
+{
+    if (bad_w4_shape(K, N)) return ORC_BAD_SHAPE;
+    int64_t nb = K / BLOCK;
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    uint8_t *z = (uint8_t *)malloc((size_t)(nb * N) + 1);
+    if (!q || !z) { free(q); free(z); return ORC_NO_MEMORY; }
+    int st = ORC_OK;
+    uint8_t qcol[BLOCK];
+    for (int64_t b = 0; b < nb && st == ORC_OK; ++b) {
+        for (int64_t n = 0; n < N; ++n) {
+            st = quantize_block(W + (b * BLOCK) * N + n, N, NULL, &scales[b * N + n],
+                                &z[b * N + n], qcol);
+            if (st != ORC_OK) break;
+            for (int r = 0; r < BLOCK; ++r) q[(b * BLOCK + r) * N + n] = qcol[r];
+        }
+    }
+    if (st == ORC_OK) {
+        orc_pack_u4(q, K * N, Wq);
+        orc_pack_u4(z, nb * N, zeros);
+    }
+    free(q);
+    free(z);
+    return st;
+}
+
+void orc_f16_array_to_f32(const uint16_t *h, int64_t count, float *out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = orc_f16_to_f32(h[i]);
 }

@@ -112,6 +112,25 @@ int orc_i8_head_logits(const float *x, int64_t K, const int8_t *Q, int64_t ldq,
 int orc_i8_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64_t ldq,
                  const float *hs, int64_t K, int64_t N, float *out);
 
+/* ---- fp16-scale variant of the format (page section "Quantization", the
+ * measurements table's "fp16 scales" file): the same codes and zero points,
+ * scales stored as IEEE binary16 bit patterns.  Dequantization still gives
+ * fp32: W_hat = fl32((q - z) * s) with s the binary16 value, so the fp32
+ * functions above apply after orc_f16_array_to_f32 on the scales.          */
+
+/* fp32 -> binary16 bits, round to nearest, ties to even; |f| >= 65520 -> inf. */
+uint16_t orc_f32_to_f16(float f);
+
+/* binary16 bits -> fp32 (exact).                                            */
+float orc_f16_to_f32(uint16_t h);
+void orc_f16_array_to_f32(const uint16_t *h, int64_t count, float *out);
+
+/* Quantizer with binary16 scales: per block s16 = binary16((hi - lo) / 15),
+ * then z and q as in orc_w4_quantize_pack against s = s16.  s16 == inf is
+ * ORC_NONFINITE; s16 == 0 gives s = z = q = 0.  scales uint16 [K/32, N].    */
+int orc_w4h_quantize_pack(const float *W, int64_t K, int64_t N,
+                          uint8_t *Wq, uint16_t *scales, uint8_t *zeros);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle as oracle_mod
 import synth
@@ -511,7 +512,114 @@ def pin_file_size(orc):
     assert abs(fp32 / 1e6 - g["fp32_MB"]) < 0.5, fp32
 
 
+# --------------------------------------------------------------------------
+# fp16-scale variant (the measurements table's "fp16 scales" file)
+# --------------------------------------------------------------------------
+def pin_f16_conversion(orc):
+    """binary16 rounding against numpy's IEEE conversion (a library routine)."""
+    g = np.random.default_rng(21)
+    edges = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -24, 2.0 ** -25,
+             3 * 2.0 ** -25, 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11,
+             1 + 3 * 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -20, 2047.5, 2049.0, 4095.0,
+             6.1e-5, 5.96e-8, 1e-8, float("inf"), float("-inf")]
+    vals = [np.float32(v) for v in edges]
+    vals += list((g.standard_normal(4000) * np.exp(g.uniform(-25, 12, 4000))).astype(np.float32))
+    vals += list(g.integers(0, 2 ** 32, 4000, dtype=np.uint64).astype(np.uint32).view(np.float32))
+    v = np.array([x for x in vals if not np.isnan(x)], np.float32)
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = orc.f32_to_f16(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(v[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
+    nan = orc.f32_to_f16(np.array([np.nan], np.float32))[0]
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
+    # every binary16 pattern back to fp32, exactly
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    back = orc.f16_to_f32(h)
+    ref32 = h.view(np.float16).astype(np.float32)
+    same = (back.view(np.uint32) == ref32.view(np.uint32)) | (np.isnan(back) & np.isnan(ref32))
+    assert same.all()
+
+
+def pin_f16_quantizer(orc):
+    """Stored scale = binary16((hi - lo) / 15); codes are the nearest ones to w
+    against that stored scale (exact rationals); the ends of the range are
+    reproduced within half a scale plus the scale's own rounding."""
+    g = np.random.default_rng(22)
+    cases = [synth.weights(64, 6, cfg=102),
+             (g.standard_normal((32, 4)) * 0.3 + 0.1).astype(np.float32),
+             (g.standard_normal((32, 4)) * 3e-5).astype(np.float32),      # subnormal scales
+             (g.standard_normal((32, 2)) * 9e4).astype(np.float32)]       # scales near the top
+    for W in cases:
+        K, N = W.shape
+        Wq, s16, zp = orc.quantize_pack_f16(W)
+        q, z = orc.unpack(Wq, zp, K, N)
+        for b in range(K // 32):
+            blk = W[32 * b:32 * b + 32]
+            for n in range(N):
+                col = blk[:, n]
+                lo = min(np.float32(0), col.min())
+                hi = max(np.float32(0), col.max())
+                s32 = np.float32(np.float32(hi - lo) / np.float32(15))
+                assert int(s16[b, n]) == int(np.array([s32]).astype(np.float16).view(np.uint16)[0])
+                sn = F(np.float16(s32).astype(np.float32))
+                if sn == 0:
+                    assert z[b, n] == 0 and not q[32 * b:32 * b + 32, n].any()
+                    continue
+                zn = int(z[b, n])
+                assert zn == min(15, max(0, int(np.rint(np.float32(-lo) / np.float32(sn)))))
+                for k in range(32):
+                    w = F(col[k])
+                    t = w / sn
+                    frac = t - (t.numerator // t.denominator)
+                    if abs(frac - Fraction(1, 2)) < Fraction(1, 2 ** 20):
+                        continue
+                    errs = [abs(w - (qq - zn) * sn) for qq in range(16)]
+                    assert errs[int(q[32 * b + k, n])] == min(errs)
+                # the ends: within s/2 plus 15 times the scale's rounding error
+                srel = abs(sn - F(s32))
+                slack = sn * Fraction(1, 2 ** 18) + 16 * srel
+                assert abs(F(lo) - (0 - zn) * sn) <= sn / 2 + slack
+                assert abs(F(hi) - (15 - zn) * sn) <= sn / 2 + slack
+
+
+def pin_f16_degenerate_and_errors(orc):
+    W = np.zeros((32, 6), np.float32)
+    W[:, 1] = 1e-8                    # scale below binary16's smallest: all zero codes
+    W[3, 2] = 1.0                     # one weight: s = fp16(1/15)
+    W[:, 3] = -0.5
+    W[:, 4] = 65504.0 * 15.0 * 0.5    # scale 32752: representable
+    Wq, s16, zp = orc.quantize_pack_f16(W)
+    q, z = orc.unpack(Wq, zp, 32, 6)
+    assert s16[0, 0] == 0 and s16[0, 1] == 0 and z[0, 1] == 0 and not q[:, 1].any()
+    assert s16[0, 2] == np.array([np.float32(1) / np.float32(15)]).astype(np.float16).view(np.uint16)[0]
+    assert q[3, 2] == 15 and z[0, 2] == 0
+    assert z[0, 3] == 15 and not q[:, 3].any()
+    assert not np.isinf(orc.f16_to_f32(s16[0, 4]))
+    big = np.zeros((32, 2), np.float32)
+    big[0, 0] = 1e6                   # (hi - lo) / 15 > 65504: the scale overflows
+    with pytest.raises(oracle_mod.OracleError):
+        orc.quantize_pack_f16(big)
+    nan = np.zeros((32, 2), np.float32)
+    nan[1, 1] = np.nan
+    with pytest.raises(oracle_mod.OracleError):
+        orc.quantize_pack_f16(nan)
+    # the fp16-scale matmul is the fp32 matmul on the scales' exact values
+    x = synth.activations(3, 64, cfg=103)
+    W = synth.weights(64, 4, cfg=103)
+    Wq, s16, zp = orc.quantize_pack_f16(W)
+    y, bound = orc.w4h_matmul(x, Wq, s16, zp)
+    What = orc.dequantize(Wq, orc.f16_to_f32(s16), zp, 64, 4)
+    for m in range(3):
+        for n in range(4):
+            exact = sum(F(x[m, k]) * F(What[k, n]) for k in range(64))
+            assert abs(F(y[m, n]) - exact) <= F(ulp32(y[m, n]))
+
+
 ALL_PINS = [
+    pin_f16_conversion,
+    pin_f16_quantizer,
+    pin_f16_degenerate_and_errors,
     pin_pack_worked_examples,
     pin_pack_exhaustive,
     pin_quantize_on_grid,

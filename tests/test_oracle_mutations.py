@@ -17,6 +17,21 @@ import oracle
 from oracle_pins import ALL_PINS
 
 MUTATIONS = {
+    "f16_truncates": (
+        "double units = rint(a / quantum); /* in [0, 2048] */",
+        "double units = floor(a / quantum); /* in [0, 2048] */"),
+    "f16_flushes_subnormals": (
+        "if (v < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)units); /* subnormal */",
+        "if (v < ldexp(1.0, -14)) return sign; /* subnormal */"),
+    "f16_overflow_at_max": (
+        "if (a >= 65520.0) return (uint16_t)(sign | 0x7C00);",
+        "if (a > 65504.0) return (uint16_t)(sign | 0x7C00);"),
+    "f16_codes_against_fp32_scale": (
+        "s = orc_f16_to_f32(h); /* the stored value */",
+        "s = h ? s : 0.0f; /* the stored value */"),
+    "f16_decode_bias_14": (
+        "else v = ldexp(1.0 + fr / 1024.0, ex - 15);",
+        "else v = ldexp(1.0 + fr / 1024.0, ex - 14);"),
     "pack_high_nibble_first": (
         "out[i] = (uint8_t)((v[2 * i] & 15) | ((v[2 * i + 1] & 15) << 4));",
         "out[i] = (uint8_t)((v[2 * i + 1] & 15) | ((v[2 * i] & 15) << 4));"),
@@ -48,8 +63,8 @@ MUTATIONS = {
         "int64_t blk = (k / BLOCK) * N + n;",
         "int64_t blk = n * (K / BLOCK) + (k / BLOCK);"),
     "quantize_scale_stored_transposed": (
-        "st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[b * N + n], &z[b * N + n],",
-        "st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[n * nb + b], &z[b * N + n],"),
+        "st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[b * N + n], NULL,",
+        "st = quantize_block(W + (b * BLOCK) * N + n, N, &scales[n * nb + b], NULL,"),
     "matmul_drops_bias": (
         "acc += (double)bias[n];",
         "acc += 0.0;"),
