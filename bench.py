@@ -153,7 +153,7 @@ def main():
         __slots__ = ("layer", "slot", "K", "N", "Wq", "s", "z", "P", "b", "x", "y", "bytes",
                      "flops")
 
-    def build_body(name, cfg, M, with_bias, outliers):
+    def build_body(name, cfg, M, with_bias, outliers, f16=False):
         shapes = synth.body(name)
         ahead = 16                  # bounded look-ahead: at most 16 fp32 matrices on the host
         futs = {}
@@ -168,13 +168,19 @@ def main():
             W = torch.from_numpy(futs.pop(i).result()).to(dev)
             m = Mat()
             m.layer, m.slot, m.K, m.N = l, s, K, N
-            m.Wq, m.s, m.z = w4.w4_quantize_pack(W)
-            m.P = w4.w4_prepack_kmajor(m.Wq, m.s, m.z) if K % 64 == 0 else None
+            if f16:  # fp16-scale variant: binary16 scales, K-major copy only
+                Wq, s16, z = w4.w4h_quantize_pack(W)
+                m.P = w4.w4h_prepack_kmajor(Wq, s16, z)
+                m.Wq = m.s = m.z = None
+                del Wq, s16, z
+            else:
+                m.Wq, m.s, m.z = w4.w4_quantize_pack(W)
+                m.P = w4.w4_prepack_kmajor(m.Wq, m.s, m.z) if K % 64 == 0 else None
             del W
             m.b = torch.from_numpy(synth.bias(N, cfg, l, s)).to(dev) if with_bias else None
             m.x = torch.from_numpy(synth.activations(M, K, cfg, l, s, outliers=outliers)).to(dev)
             m.y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            wbytes = K * N // 2 + (K // 32) * N * 4 + (K // 32) * N // 2
+            wbytes = K * N // 2 + (K // 32) * N * (2 if f16 else 4) + (K // 32) * N // 2
             m.bytes = wbytes + 4 * M * K + 4 * M * N + (4 * N if with_bias else 0)
             m.flops = 2 * M * K * N
             mats.append(m)
@@ -351,6 +357,20 @@ def main():
         del d16
         del graph
         dense.clear()
+        torch.cuda.empty_cache()
+
+        # the fp16-scale variant of the same body (0.578125 B/weight), M = 1
+        log("building the fp16-scale body ...")
+        dh = build_body("dense38", synth.CFG_DENSE38, 1, with_bias=False, outliers=False, f16=True)
+        gh = capture(lambda: run_pass(dh))
+        msh, _ = time_graph(gh, max(5, args.steps // 2), 2)
+        hbytes = sum(m.bytes for m in dh)
+        secondary["dense38_m1_pass_fp16_scales"] = {
+            "ms": round(msh, 4), "tokens_per_s": round(1e3 / msh, 1),
+            "GB_s": round(hbytes / (msh * 1e-3) / 1e9, 1),
+            "algorithmic_bytes_per_step": hbytes}
+        del gh
+        dh.clear()
         torch.cuda.empty_cache()
 
         gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)

@@ -167,6 +167,37 @@ int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint
                                 const void *workspace, size_t workspace_bytes);
 
 /* ---------------------------------------------------------------------------
+ * fp16-scale variant (page section "Quantization", the measurements table's
+ * "4-bit DequantizeLinear, fp16 scales" file): the same codes and zero points,
+ * each block scale stored as an IEEE binary16 bit pattern (uint16), 0.578125
+ * bytes per weight.  The quantizer rounds the fp32 scale (hi - lo) / 15 to
+ * binary16 (to nearest, ties to even) and takes the zero point and codes
+ * against that stored value; a scale that overflows binary16 (>= 65520) sets
+ * d_status to W4_ERR_NONFINITE, one that rounds to 0 gives an all-zero block.
+ * Dequantization is still fp32: w_hat = fl32((q - z) * s), s the binary16
+ * value.  Layouts, alignment, status codes and the result bound are those of
+ * the fp32-scale functions of the same name without the h; the K-major
+ * matmul needs the workspace w4_matmul_kmajor_workspace_bytes(M, K, N).     */
+int w4h_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, uint16_t *scales,
+                      uint8_t *zeros, int *d_status, void *stream);
+
+int w4h_dequantize(const uint8_t *Wq, const uint16_t *scales, const uint8_t *zeros, int64_t K,
+                   int64_t N, float *W_hat, void *stream);
+
+int w4h_prepack_kmajor(const uint8_t *Wq, const uint16_t *scales, const uint8_t *zeros,
+                       int64_t K, int64_t N, uint8_t *Pq, uint16_t *Ps, uint8_t *Pz,
+                       void *stream);
+
+int w4h_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                 const uint16_t *Ps, const uint8_t *Pz, int64_t N,
+                                 const float *bias, const float *y,
+                                 const void *workspace, size_t workspace_bytes);
+
+int w4h_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                      const uint16_t *Ps, const uint8_t *Pz, int64_t N, const float *bias,
+                      float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * int8 tied head (step 3).  E fp32 [K, N] -> Q int8 [K, ldq], hs fp32 [N]:
  * hs[n] = max_k |E[k, n]| / 127 (correctly rounded fp32 division),
  * Q[k, n] = clamp(rint(E[k, n] / hs[n]), -127, 127); a zero column gives

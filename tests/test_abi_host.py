@@ -35,7 +35,9 @@ def test_header_declares_the_entry_points():
                  "i8_head_workspace_bytes", "w4_check_matmul_args", "w4_strerror",
                  "w4_abi_version", "i8_prepack_head", "i8_head_logits_kmajor",
                  "i8_check_head_logits_kmajor_args", "i8_embed_kmajor",
-                 "i8_head_logits_rows", "i8_check_head_logits_rows_args"):
+                 "i8_head_logits_rows", "i8_check_head_logits_rows_args",
+                 "w4h_quantize_pack", "w4h_dequantize", "w4h_prepack_kmajor",
+                 "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args"):
         assert must in names
 
 
@@ -192,3 +194,20 @@ def test_head_rows_checks():
     if NO_GPU:
         assert w4.library().i8_head_logits_rows(A, 2, 768, A, 768, A, 100, A, None) == \
             w4.W4_ERR_DEVICE
+
+
+def test_f16_variant_checks():
+    lib = w4.library()
+    km = lib.w4h_check_matmul_kmajor_args
+    assert km(A, 1, 3072, A, A, A, 3072, None, A, None, 0) == w4.W4_OK
+    assert km(A, 1, 96, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_BAD_SHAPE
+    assert km(A, 1, 128, A, A + 8, A, 16, None, A, None, 0) == w4.W4_ERR_MISALIGNED
+    need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072)
+    assert km(A, 16, 3072, A, A, A, 3072, None, A, None, 0) == w4.W4_ERR_WORKSPACE
+    assert km(A, 16, 3072, A, A, A, 3072, None, A, A, need) == w4.W4_OK
+    assert lib.w4h_quantize_pack(A, 100, 64, A, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4h_quantize_pack(A, 64, 64, A, A + 2, A, None, None) == w4.W4_ERR_MISALIGNED
+    assert lib.w4h_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4h_dequantize(A, None, A, 32, 64, A, None) == w4.W4_ERR_NULL_PTR
+    if NO_GPU:
+        assert lib.w4h_quantize_pack(A, 64, 64, A, A, A, None, None) == w4.W4_ERR_DEVICE

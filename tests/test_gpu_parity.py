@@ -532,3 +532,64 @@ def test_kmajor_rejects_bad_shapes():
     A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
     assert lib.w4_matmul_kmajor(A, 1, 96, A, A, A, 16, None, A, None, 0, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.w4_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE
+
+
+# --------------------------------------------------------------------------
+# fp16-scale variant
+# --------------------------------------------------------------------------
+def f16_bits(t):
+    return host(t).view(np.uint16)
+
+
+def mixed_weights_f16(K, N, cfg):
+    W = mixed_weights(K, N, cfg)
+    g = np.random.default_rng(cfg)
+    if N >= 12:
+        W[:32, 8] = (g.standard_normal(32) * 1e-8).astype(np.float32)   # scale rounds to 0
+        W[:32, 9] = (g.standard_normal(32) * 3e-5).astype(np.float32)   # subnormal binary16 scale
+        W[:32, 10] = (g.standard_normal(32) * 9e4).astype(np.float32)   # scale near the top
+    return W
+
+
+@pytest.mark.parametrize("K,N", [(64, 16), (768, 2304), (3072, 768), (192, 530)])
+def test_f16_quantize_pack_bit_exact(K, N):
+    note(f"f16 quantize K={K} N={N}")
+    W = mixed_weights_f16(K, N, cfg=240)
+    Wq_r, s_r, z_r = ORC.quantize_pack_f16(W)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Wq, s, z = w4.w4h_quantize_pack(dev(W), d_status=st)
+    assert_bits(host(Wq), Wq_r, f"f16 Wq {K}x{N}")
+    assert_bits(f16_bits(s), s_r, f"f16 scales {K}x{N}")
+    assert_bits(host(z), z_r, f"f16 zeros {K}x{N}")
+    assert host(st)[0] == 0
+    W_hat = host(w4.w4h_dequantize(Wq, s, z))
+    assert_bits(W_hat, ORC.dequantize(Wq_r, ORC.f16_to_f32(s_r), z_r, K, N), f"f16 W_hat {K}x{N}")
+    P = w4.w4h_prepack_kmajor(Wq, s, z)
+    if K % 64 == 0:
+        Pq_r, Ps_r, Pz_r = ORC.prepack_kmajor_f16(Wq_r, s_r, z_r, K, N)
+        assert_bits(host(P[0]), Pq_r, "f16 Pq")
+        assert_bits(f16_bits(P[1]), Ps_r, "f16 Ps")
+        assert_bits(host(P[2]), Pz_r, "f16 Pz")
+
+
+def test_f16_scale_overflow_sets_status():
+    W = np.zeros((32, 4), np.float32)
+    W[0, 1] = 1e6                       # (hi - lo) / 15 > 65504
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    w4.w4h_quantize_pack(dev(W), d_status=st)
+    assert host(st)[0] == w4.W4_ERR_NONFINITE
+
+
+@pytest.mark.parametrize("K,N", [(768, 2304), (3072, 768), (128, 530), (8192, 512), (640, 96)])
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 58])
+def test_f16_matmul_kmajor(M, K, N):
+    note(f"f16 kmajor M={M} K={K} N={N}")
+    W = mixed_weights_f16(K, N, cfg=241)
+    x = synth.activations(M, K, cfg=241, slot=M, outliers=True)
+    b = synth.bias(N, cfg=241)
+    Wq, s16, z = ORC.quantize_pack_f16(W)
+    y_ref, bound = ORC.w4h_matmul(x, Wq, s16, z, b)
+    s_dev = torch.from_numpy(s16.view(np.float16)).to(DEV)
+    P = w4.w4h_prepack_kmajor(dev(Wq), s_dev, dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y, y_ref, bound, f"f16 kmajor M={M} {K}x{N}")

@@ -56,6 +56,11 @@ _SIGS = {
     "i8_check_head_logits_kmajor_args": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P]),
     "i8_head_logits_kmajor": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P]),
     "i8_embed_kmajor": (_INT, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _P, _P]),
+    "w4h_quantize_pack": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "w4h_dequantize": (_INT, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "w4h_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "w4h_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
+    "w4h_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "i8_check_head_logits_rows_args": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "i8_head_logits_rows": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P]),
 }
@@ -230,10 +235,14 @@ def w4_matmul_kmajor_workspace_bytes(M: int, K: int, N: int) -> int:
 def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: torch.Tensor,
                      bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
                      workspace: torch.Tensor | None = None):
-    """y fp32 [M, N] = x [M, K] . dequantize(K-major weights) (+ bias)."""
+    """y fp32 [M, N] = x [M, K] . dequantize(K-major weights) (+ bias).
+
+    Ps fp32 is the base format; Ps float16 (binary16 scales) the fp16-scale
+    variant (w4h_matmul_kmajor)."""
     _dev(x, torch.float32, "x")
     _dev(Pq, torch.uint8, "Pq")
-    _dev(Ps, torch.float32, "Ps")
+    f16 = Ps.dtype == torch.float16  # binary16 scales: the fp16-scale variant
+    _dev(Ps, torch.float16 if f16 else torch.float32, "Ps")
     _dev(Pz, torch.uint8, "Pz")
     if bias is not None:
         _dev(bias, torch.float32, "bias")
@@ -251,7 +260,8 @@ def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: to
     else:
         _dev(workspace, torch.uint8, "workspace")
         ws, wsb = workspace, workspace.numel()
-    _check("w4_matmul_kmajor", _lib.w4_matmul_kmajor(
+    fn = "w4h_matmul_kmajor" if f16 else "w4_matmul_kmajor"
+    _check(fn, getattr(_lib, fn)(
         _ptr(x), M, K, _ptr(Pq), _ptr(Ps), _ptr(Pz), N, _ptr(bias), _ptr(out),
         _ptr(ws), wsb, _stream(x.device)))
     return out
@@ -376,3 +386,45 @@ def i8_head_logits_rows(x: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor,
     _check("i8_head_logits_rows", _lib.i8_head_logits_rows(
         _ptr(x), M, K, _ptr(Qt), ldt, _ptr(hs), N, _ptr(out), _stream(Qt.device)))
     return out
+
+
+# -- fp16-scale variant: scales are float16 tensors (IEEE binary16) -------------
+def w4h_quantize_pack(W: torch.Tensor, d_status: torch.Tensor | None = None):
+    """W fp32 [K, N] -> (Wq uint8 [K, N/2], scales float16 [K/32, N], zeros uint8 [K/32, N/2])."""
+    _dev(W, torch.float32, "W")
+    K, N = W.shape
+    Wq = torch.empty((K, N // 2), dtype=torch.uint8, device=W.device)
+    s = torch.empty((K // BLOCK, N), dtype=torch.float16, device=W.device)
+    z = torch.empty((K // BLOCK, N // 2), dtype=torch.uint8, device=W.device)
+    if d_status is not None:
+        _dev(d_status, torch.int32, "d_status")
+    _check("w4h_quantize_pack", _lib.w4h_quantize_pack(
+        _ptr(W), K, N, _ptr(Wq), _ptr(s), _ptr(z), _ptr(d_status), _stream(W.device)))
+    return Wq, s, z
+
+
+def w4h_dequantize(Wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+    """-> W_hat fp32 [K, N] (scales float16)."""
+    _dev(Wq, torch.uint8, "Wq")
+    _dev(scales, torch.float16, "scales")
+    _dev(zeros, torch.uint8, "zeros")
+    K, N = Wq.shape[0], scales.shape[1]
+    out = torch.empty((K, N), dtype=torch.float32, device=Wq.device)
+    _check("w4h_dequantize", _lib.w4h_dequantize(_ptr(Wq), _ptr(scales), _ptr(zeros), K, N,
+                                                 _ptr(out), _stream(Wq.device)))
+    return out
+
+
+def w4h_prepack_kmajor(Wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+    """-> K-major copy (Pq uint8 [N, K/2], Ps float16 [N, K/32], Pz uint8 [N, K/64])."""
+    _dev(Wq, torch.uint8, "Wq")
+    _dev(scales, torch.float16, "scales")
+    _dev(zeros, torch.uint8, "zeros")
+    K, N = Wq.shape[0], scales.shape[1]
+    Pq = torch.empty((N, K // 2), dtype=torch.uint8, device=Wq.device)
+    Ps = torch.empty((N, K // BLOCK), dtype=torch.float16, device=Wq.device)
+    Pz = torch.empty((N, K // 64), dtype=torch.uint8, device=Wq.device)
+    _check("w4h_prepack_kmajor", _lib.w4h_prepack_kmajor(
+        _ptr(Wq), _ptr(scales), _ptr(zeros), K, N, _ptr(Pq), _ptr(Ps), _ptr(Pz),
+        _stream(Wq.device)))
+    return Pq, Ps, Pz

@@ -23,7 +23,7 @@ int check_w4_shape(int64_t K, int64_t N) {
     return W4_OK;
 }
 
-int check_packed(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
+int check_packed(const uint8_t *Wq, const void *scales, const uint8_t *zeros, int64_t K,
                  int64_t N) {
     if (!need(Wq, K * N) || !need(scales, K * N) || !need(zeros, K * N)) return W4_ERR_NULL_PTR;
     if (!aligned(Wq, 16) || !aligned(scales, 16) || !aligned(zeros, 16)) return W4_ERR_MISALIGNED;
@@ -81,15 +81,26 @@ const char *w4_strerror(int status) {
     }
 }
 
-int w4_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, float *scales,
-                     uint8_t *zeros, int *d_status, void *stream) {
+static int quantize_pack_impl(const float *W, int64_t K, int64_t N, uint8_t *Wq, void *scales, bool f16,
+                       uint8_t *zeros, int *d_status, void *stream) {
     int st = check_w4_shape(K, N);
     if (st) return st;
     if (!need(W, K * N)) return W4_ERR_NULL_PTR;
     if ((st = check_packed(Wq, scales, zeros, K, N))) return st;
     if (!aligned(W, 16) || !aligned(d_status, 4)) return W4_ERR_MISALIGNED;
     if ((st = device_check())) return st;
-    return launched(w4::launch_quantize_pack(W, K, N, Wq, scales, zeros, d_status, as_stream(stream)));
+    return launched(
+        w4::launch_quantize_pack(W, K, N, Wq, scales, f16, zeros, d_status, as_stream(stream)));
+}
+
+int w4_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, float *scales,
+                     uint8_t *zeros, int *d_status, void *stream) {
+    return quantize_pack_impl(W, K, N, Wq, scales, false, zeros, d_status, stream);
+}
+
+int w4h_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, uint16_t *scales,
+                      uint8_t *zeros, int *d_status, void *stream) {
+    return quantize_pack_impl(W, K, N, Wq, scales, true, zeros, d_status, stream);
 }
 
 int w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N, uint8_t *q,
@@ -104,15 +115,26 @@ int w4_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N, uin
     return launched(w4::launch_unpack(Wq, zeros, K, N, q, z, as_stream(stream)));
 }
 
-int w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
-                  int64_t N, float *W_hat, void *stream) {
+static int dequantize_impl(const uint8_t *Wq, const void *scales, bool f16, const uint8_t *zeros,
+                    int64_t K, int64_t N, float *W_hat, void *stream) {
     int st = check_w4_shape(K, N);
     if (st) return st;
     if ((st = check_packed(Wq, scales, zeros, K, N))) return st;
     if (!need(W_hat, K * N)) return W4_ERR_NULL_PTR;
     if (!aligned(W_hat, 8)) return W4_ERR_MISALIGNED;
     if ((st = device_check())) return st;
-    return launched(w4::launch_dequantize(Wq, scales, zeros, K, N, W_hat, as_stream(stream)));
+    return launched(
+        w4::launch_dequantize(Wq, scales, f16, zeros, K, N, W_hat, as_stream(stream)));
+}
+
+int w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
+                  int64_t N, float *W_hat, void *stream) {
+    return dequantize_impl(Wq, scales, false, zeros, K, N, W_hat, stream);
+}
+
+int w4h_dequantize(const uint8_t *Wq, const uint16_t *scales, const uint8_t *zeros, int64_t K,
+                   int64_t N, float *W_hat, void *stream) {
+    return dequantize_impl(Wq, scales, true, zeros, K, N, W_hat, stream);
 }
 
 size_t w4_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -152,8 +174,8 @@ int w4_matmul(const float *x, int64_t M, int64_t K, const uint8_t *Wq, const flo
                                        bias, y, workspace, as_stream(stream)));
 }
 
-int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
-                      int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz, void *stream) {
+static int prepack_kmajor_impl(const uint8_t *Wq, const void *scales, bool f16, const uint8_t *zeros,
+                        int64_t K, int64_t N, uint8_t *Pq, void *Ps, uint8_t *Pz, void *stream) {
     int st = check_w4_shape(K, N);
     if (st) return st;
     if (K % 64 != 0) return W4_ERR_BAD_SHAPE;
@@ -161,7 +183,18 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
     if ((st = check_packed(Pq, Ps, Pz, K, N))) return st;
     if (K * N == 0) return W4_OK;
     if ((st = device_check())) return st;
-    return launched(w4::launch_prepack_kmajor(Wq, scales, zeros, K, N, Pq, Ps, Pz, as_stream(stream)));
+    return launched(w4::launch_prepack_kmajor(Wq, scales, f16, zeros, K, N, Pq, Ps, Pz,
+                                              as_stream(stream)));
+}
+
+int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t K,
+                      int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz, void *stream) {
+    return prepack_kmajor_impl(Wq, scales, false, zeros, K, N, Pq, Ps, Pz, stream);
+}
+
+int w4h_prepack_kmajor(const uint8_t *Wq, const uint16_t *scales, const uint8_t *zeros, int64_t K,
+                       int64_t N, uint8_t *Pq, uint16_t *Ps, uint8_t *Pz, void *stream) {
+    return prepack_kmajor_impl(Wq, scales, true, zeros, K, N, Pq, Ps, Pz, stream);
 }
 
 size_t w4_matmul_kmajor_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -169,9 +202,9 @@ size_t w4_matmul_kmajor_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return w4::plan_x3(M, K, N).workspace;
 }
 
-int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
-                                const float *Ps, const uint8_t *Pz, int64_t N, const float *bias,
-                                const float *y, const void *workspace, size_t workspace_bytes) {
+static int check_matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                             const void *Ps, const uint8_t *Pz, int64_t N, const float *bias,
+                             const float *y, const void *workspace, size_t workspace_bytes) {
     if (M < 0) return W4_ERR_BAD_SHAPE;
     int st = check_w4_shape(K, N);
     if (st) return st;
@@ -190,23 +223,47 @@ int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint
     return W4_OK;
 }
 
-int w4_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
-                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *workspace,
-                     size_t workspace_bytes, void *stream) {
-    int st = w4_check_matmul_kmajor_args(x, M, K, Pq, Ps, Pz, N, bias, y, workspace,
-                                         workspace_bytes);
+static int matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const void *Ps,
+                       bool f16, const uint8_t *Pz, int64_t N, const float *bias, float *y,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_matmul_kmajor_impl(x, M, K, Pq, Ps, Pz, N, bias, y, workspace,
+                                      workspace_bytes);
     if (st) return st;
     if (M == 0 || N == 0) return W4_OK;
     if ((st = device_check())) return st;
-    if (K == 0)
-        return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, Pz, N,
-                                               bias, y, as_stream(stream)));
     const w4::X3Plan px = w4::plan_x3(M, K, N);
-    if (px.kind == w4::X3Plan::kRun)
-        return launched(w4::launch_mm_x3(px, x, M, K, Pq, Ps, Pz, N, bias, y, workspace,
+    if (K > 0 && px.kind == w4::X3Plan::kRun)
+        return launched(w4::launch_mm_x3(px, x, M, K, Pq, Ps, f16, Pz, N, bias, y, workspace,
                                          as_stream(stream)));
-    return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, Pz, N, bias,
-                                           y, as_stream(stream)));
+    return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, f16, Pz, N,
+                                           bias, y, as_stream(stream)));
+}
+
+int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                const float *Ps, const uint8_t *Pz, int64_t N, const float *bias,
+                                const float *y, const void *workspace, size_t workspace_bytes) {
+    return check_matmul_kmajor_impl(x, M, K, Pq, Ps, Pz, N, bias, y, workspace, workspace_bytes);
+}
+
+int w4h_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                 const uint16_t *Ps, const uint8_t *Pz, int64_t N,
+                                 const float *bias, const float *y, const void *workspace,
+                                 size_t workspace_bytes) {
+    return check_matmul_kmajor_impl(x, M, K, Pq, Ps, Pz, N, bias, y, workspace, workspace_bytes);
+}
+
+int w4_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
+                     const uint8_t *Pz, int64_t N, const float *bias, float *y, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    return matmul_kmajor_impl(x, M, K, Pq, Ps, false, Pz, N, bias, y, workspace, workspace_bytes,
+                              stream);
+}
+
+int w4h_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const uint16_t *Ps,
+                      const uint8_t *Pz, int64_t N, const float *bias, float *y, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return matmul_kmajor_impl(x, M, K, Pq, Ps, true, Pz, N, bias, y, workspace, workspace_bytes,
+                              stream);
 }
 
 int i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q, float *hs,

@@ -68,6 +68,15 @@ __device__ __forceinline__ void fma_word(float x, uint32_t qword, const NibblePa
     }
 }
 
+// binary16 scales: fp32 -> binary16 bits (round to nearest even; v_cvt_f16_f32
+// keeps subnormals, overflows to infinity) and back (exact).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
 // Undo the fp16-subnormal scaling of column c (0..7) of a packed word.
 __device__ __forceinline__ constexpr float nibble_unscale(int c) {
     return (c & 1) ? 1048576.0f /* 2^20 */ : 16777216.0f /* 2^24 */;

@@ -20,6 +20,8 @@
 // per-lane block sums are scaled, then summed over the column's lanes in a
 // fixed order: through LDS, a few lanes per output each adding a contiguous
 // run, then two lane exchanges.  Results are deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -42,11 +44,15 @@ __global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t *__restrict
 }
 
 // Scales and zero points, one thread per (column pair j, block pair c).
-__global__ __launch_bounds__(256) void k_prepack_blocks(const float *__restrict__ scales,
+template <bool H>
+__global__ __launch_bounds__(256) void k_prepack_blocks(const void *__restrict__ scales_v,
                                                         const uint8_t *__restrict__ zeros,
                                                         int64_t K, int64_t N,
-                                                        float *__restrict__ Ps,
+                                                        void *__restrict__ Ps_v,
                                                         uint8_t *__restrict__ Pz) {
+    typedef typename std::conditional<H, uint16_t, float>::type S;  // scale storage
+    const S *scales = static_cast<const S *>(scales_v);
+    S *Ps = static_cast<S *>(Ps_v);
     const int64_t NB = K / kBlock, half = N / 2, hb = NB / 2;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= hb * half) return;
@@ -102,10 +108,10 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // below 2^31 bytes).  CHECK clamps columns past N (ragged last workgroup);
 // without it every load is unconditional, so the compiler can start on
 // pass 0 while later passes are still in flight.
-template <int MR, int P, bool CHECK, bool LOOP>
+template <int MR, int P, bool CHECK, bool LOOP, bool H>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, int M, int K, const uint8_t *__restrict__ Pq,
-    const float *__restrict__ Ps, const uint8_t *__restrict__ Pz, int N,
+    const void *__restrict__ Ps, const uint8_t *__restrict__ Pz, int N,
     const float *__restrict__ bias, float *__restrict__ y, int G, int NBL) {
     extern __shared__ float red[];  // [MR][CC][NBL]
     const int L = threadIdx.x;
@@ -159,7 +165,8 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                     z_off = (uint32_t)(nl * (NB / 2) + (b >> 1));
                 }
                 w[p] = load_stream<u32x4_t>(Pq + q_off);
-                s[p] = Ps[s_off];
+                s[p] = H ? f16_bits_to_f32(static_cast<const uint16_t *>(Ps)[s_off])
+                         : static_cast<const float *>(Ps)[s_off];
                 zb[p] = Pz[z_off];
                 oq += sq;
                 os += ss;
@@ -221,22 +228,28 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
 
 }  // namespace
 
-hipError_t launch_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
-                                 int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz,
-                                 hipStream_t stream) {
+hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16,
+                                 const uint8_t *zeros, int64_t K, int64_t N, uint8_t *Pq, void *Ps,
+                                 uint8_t *Pz, hipStream_t stream) {
     const int64_t t1 = (K / 2) * (N / 2), t2 = (K / 64) * (N / 2);
     if (t1 > 0)
         hipLaunchKernelGGL(k_prepack_codes, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
                            Wq, K, N, Pq);
-    if (t2 > 0)
-        hipLaunchKernelGGL(k_prepack_blocks, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0,
-                           stream, scales, zeros, K, N, Ps, Pz);
+    if (t2 > 0) {
+        const dim3 grid((unsigned)((t2 + 255) / 256));
+        if (f16)
+            hipLaunchKernelGGL(k_prepack_blocks<true>, grid, dim3(256), 0, stream, scales, zeros, K,
+                               N, Ps, Pz);
+        else
+            hipLaunchKernelGGL(k_prepack_blocks<false>, grid, dim3(256), 0, stream, scales, zeros, K,
+                               N, Ps, Pz);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, int64_t K,
-                              const uint8_t *Pq, const float *Ps, const uint8_t *Pz, int64_t N,
-                              const float *bias, float *y, hipStream_t stream) {
+                              const uint8_t *Pq, const void *Ps, bool f16, const uint8_t *Pz,
+                              int64_t N, const float *bias, float *y, hipStream_t stream) {
     if (p.kind == KmajorPlan::kEmpty) return hipSuccess;
     if (p.kind == KmajorPlan::kBiasOnly) return launch_bias_fill(bias, M, N, y, stream);
     const int64_t C = (int64_t)p.groups * p.passes;
@@ -245,16 +258,22 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const bool check = (N % C) != 0;
     const bool loop = p.lanes_per_col < K / kBlock;
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
-    hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV>), grid, dim3(p.threads), shm, stream, x,   \
-                       (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups, p.lanes_per_col)
+    if (f16)                                                                                    \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true>), grid, dim3(p.threads), shm,    \
+                           stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups,      \
+                           p.lanes_per_col);                                                    \
+    else                                                                                        \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false>), grid, dim3(p.threads), shm,   \
+                           stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups,      \
+                           p.lanes_per_col)
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
         if (check) {                                                                            \
-            if (loop) W4_KM_LAUNCH(MRV, PV, true, true);                                        \
-            else W4_KM_LAUNCH(MRV, PV, true, false);                                            \
+            if (loop) { W4_KM_LAUNCH(MRV, PV, true, true); }                                    \
+            else { W4_KM_LAUNCH(MRV, PV, true, false); }                                        \
         } else {                                                                                \
-            if (loop) W4_KM_LAUNCH(MRV, PV, false, true);                                       \
-            else W4_KM_LAUNCH(MRV, PV, false, false);                                           \
+            if (loop) { W4_KM_LAUNCH(MRV, PV, false, true); }                                   \
+            else { W4_KM_LAUNCH(MRV, PV, false, false); }                                       \
         }                                                                                       \
         return hipGetLastError();                                                               \
     }

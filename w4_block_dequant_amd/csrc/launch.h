@@ -10,12 +10,14 @@
 
 namespace w4 {
 
-hipError_t launch_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq,
-                                float *scales, uint8_t *zeros, int *d_status, hipStream_t stream);
+// scales are fp32, or binary16 bit patterns when f16 is set
+hipError_t launch_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, void *scales,
+                                bool f16, uint8_t *zeros, int *d_status, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int64_t N,
                          uint8_t *q, uint8_t *z, hipStream_t stream);
-hipError_t launch_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
-                             int64_t K, int64_t N, float *out, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t *Wq, const void *scales, bool f16,
+                             const uint8_t *zeros, int64_t K, int64_t N, float *out,
+                             hipStream_t stream);
 
 hipError_t launch_gemv(const GemvPlan &plan, const float *x, int64_t K, const uint8_t *Wq,
                        const float *scales, const uint8_t *zeros, int64_t N, const float *bias,
@@ -26,12 +28,12 @@ hipError_t launch_small_m(const SmallMPlan &plan, const float *x, int64_t M, int
                           int64_t N, const float *bias, float *y, void *workspace,
                           hipStream_t stream);
 
-hipError_t launch_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
-                                 int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz,
-                                 hipStream_t stream);
+hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16,
+                                 const uint8_t *zeros, int64_t K, int64_t N, uint8_t *Pq, void *Ps,
+                                 uint8_t *Pz, hipStream_t stream);
 hipError_t launch_gemv_kmajor(const KmajorPlan &plan, const float *x, int64_t M, int64_t K,
-                              const uint8_t *Pq, const float *Ps, const uint8_t *Pz, int64_t N,
-                              const float *bias, float *y, hipStream_t stream);
+                              const uint8_t *Pq, const void *Ps, bool f16, const uint8_t *Pz,
+                              int64_t N, const float *bias, float *y, hipStream_t stream);
 
 hipError_t launch_bias_fill(const float *bias, int64_t M, int64_t N, float *y,
                             hipStream_t stream);
@@ -45,8 +47,8 @@ hipError_t launch_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64
                         const float *hs, int64_t K, int64_t N, float *out, int *d_status,
                         hipStream_t stream);
 hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
-                        const float *Ps, const uint8_t *Pz, int64_t N, const float *bias, float *y,
-                        void *workspace, hipStream_t stream);
+                        const void *Ps, bool f16, const uint8_t *Pz, int64_t N, const float *bias,
+                        float *y, void *workspace, hipStream_t stream);
 hipError_t launch_head_prepack(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *Qt,
                                int64_t ldt, hipStream_t stream);
 hipError_t launch_head_logits_kmajor(const float *x, int64_t K, const int8_t *Qt, int64_t ldt,

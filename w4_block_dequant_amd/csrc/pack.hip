@@ -2,7 +2,10 @@
 // the page "ONNX export, quantization and the browser runtime", section
 // "Quantization", step 2: blocks of 32 along K, one fp32 scale and one uint4
 // zero point per block, w_hat = (q - z) * scale.  All three are bit-exact
-// functions of their inputs.
+// functions of their inputs.  H = true is the variant with the scale stored
+// as binary16 (the same section's measurements table, "fp16 scales"): the
+// fp32 scale (hi - lo) / 15 is rounded to binary16 (to nearest, ties to even)
+// and the zero point and codes are taken against the stored value.
 #include "common.h"
 #include "launch.h"
 
@@ -20,9 +23,12 @@ __device__ __forceinline__ int clamp_code(float v, int lo, int hi) {
 }
 
 // Quantize one block column: 32 weights w[r] -> scale, zero point, codes.
-// Returns false if a weight is not finite or the scale overflows.
+// Returns false if a weight is not finite or the scale overflows.  With H the
+// scale is stored as binary16 (h_out) and used at that value.
+template <bool H>
 __device__ __forceinline__ bool quantize_column(const float (&w)[kBlock], float &s_out,
-                                                int &z_out, uint32_t (&q_out)[kBlock]) {
+                                                uint16_t &h_out, int &z_out,
+                                                uint32_t (&q_out)[kBlock]) {
     float lo = 0.0f, hi = 0.0f;  // zero-inclusive range
     bool finite = true;
 #pragma unroll
@@ -33,8 +39,13 @@ __device__ __forceinline__ bool quantize_column(const float (&w)[kBlock], float 
         if (v > hi) hi = v;
     }
     const float range = hi - lo;
-    const float s = range / 15.0f;
+    float s = range / 15.0f;
     finite &= __builtin_isfinite(s);
+    if (H) {
+        h_out = f32_to_f16_bits(s);
+        finite &= (h_out & 0x7C00u) != 0x7C00u;  // binary16 overflow
+        s = f16_bits_to_f32(h_out);
+    }
     if (s == 0.0f || !finite) {
         s_out = finite ? 0.0f : s;
         z_out = 0;
@@ -56,9 +67,10 @@ __device__ __forceinline__ bool quantize_column(const float (&w)[kBlock], float 
 // One thread per (K-block b, column pair j): reads 2 columns x 32 rows
 // (8 bytes per row, adjacent threads adjacent), writes 32 packed bytes of Wq,
 // two scales and one packed zero byte.
+template <bool H>
 __global__ __launch_bounds__(256) void k_quantize_pack(const float *__restrict__ W, int64_t K,
                                                        int64_t N, uint8_t *__restrict__ Wq,
-                                                       float *__restrict__ scales,
+                                                       void *__restrict__ scales,
                                                        uint8_t *__restrict__ zeros,
                                                        int *__restrict__ d_status) {
     const int64_t half = N / 2;
@@ -74,15 +86,20 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const float *__restrict__
         w1[r] = v.y;
     }
     float s0, s1;
+    uint16_t h0 = 0, h1 = 0;
     int z0, z1;
     uint32_t q0[kBlock], q1[kBlock];
-    bool ok = quantize_column(w0, s0, z0, q0);
-    ok &= quantize_column(w1, s1, z1, q1);
+    bool ok = quantize_column<H>(w0, s0, h0, z0, q0);
+    ok &= quantize_column<H>(w1, s1, h1, z1, q1);
     if (!ok) set_status(d_status, W4_ERR_NONFINITE);
     uint8_t *dst = Wq + b * kBlock * half + j;
 #pragma unroll
     for (int r = 0; r < kBlock; ++r) dst[r * half] = (uint8_t)(q0[r] | (q1[r] << 4));
-    reinterpret_cast<float2 *>(scales + b * N)[j] = make_float2(s0, s1);
+    if (H)
+        reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(scales) + b * N)[j] =
+            (uint32_t)h0 | ((uint32_t)h1 << 16);
+    else
+        reinterpret_cast<float2 *>(static_cast<float *>(scales) + b * N)[j] = make_float2(s0, s1);
     zeros[b * half + j] = (uint8_t)(z0 | (z1 << 4));
 }
 
@@ -104,8 +121,9 @@ __global__ __launch_bounds__(256) void k_unpack(const uint8_t *__restrict__ Wq,
 }
 
 // One thread per packed byte (k, j): W_hat[k, 2j], W_hat[k, 2j+1].
+template <bool H>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ Wq,
-                                                    const float *__restrict__ scales,
+                                                    const void *__restrict__ scales,
                                                     const uint8_t *__restrict__ zeros, int64_t K,
                                                     int64_t N, float *__restrict__ out) {
     const int64_t half = N / 2;
@@ -114,7 +132,14 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
     const int64_t k = i / half, j = i - k * half;
     const int64_t b = k / kBlock;
     const uint8_t qv = Wq[i], zv = zeros[b * half + j];
-    const float2 s = reinterpret_cast<const float2 *>(scales + b * N)[j];
+    float2 s;
+    if (H) {
+        const uint32_t hh =
+            reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(scales) + b * N)[j];
+        s = make_float2(f16_bits_to_f32((uint16_t)hh), f16_bits_to_f32((uint16_t)(hh >> 16)));
+    } else {
+        s = reinterpret_cast<const float2 *>(static_cast<const float *>(scales) + b * N)[j];
+    }
     // (q - z) is an exact small integer, so each output is one fp32 rounding
     const float d0 = (float)((int)(qv & 15) - (int)(zv & 15));
     const float d1 = (float)((int)(qv >> 4) - (int)(zv >> 4));
@@ -123,14 +148,17 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq,
-                                float *scales, uint8_t *zeros, int *d_status,
-                                hipStream_t stream) {
+hipError_t launch_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, void *scales,
+                                bool f16, uint8_t *zeros, int *d_status, hipStream_t stream) {
     const int64_t half = N / 2, nb = K / kBlock;
     if (half == 0 || nb == 0) return hipSuccess;
     dim3 grid((unsigned)((half + 255) / 256), (unsigned)nb);
-    hipLaunchKernelGGL(k_quantize_pack, grid, dim3(256), 0, stream, W, K, N, Wq, scales, zeros,
-                       d_status);
+    if (f16)
+        hipLaunchKernelGGL(k_quantize_pack<true>, grid, dim3(256), 0, stream, W, K, N, Wq, scales,
+                           zeros, d_status);
+    else
+        hipLaunchKernelGGL(k_quantize_pack<false>, grid, dim3(256), 0, stream, W, K, N, Wq, scales,
+                           zeros, d_status);
     return hipGetLastError();
 }
 
@@ -144,12 +172,18 @@ hipError_t launch_unpack(const uint8_t *Wq, const uint8_t *zeros, int64_t K, int
     return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
-                             int64_t K, int64_t N, float *out, hipStream_t stream) {
+hipError_t launch_dequantize(const uint8_t *Wq, const void *scales, bool f16,
+                             const uint8_t *zeros, int64_t K, int64_t N, float *out,
+                             hipStream_t stream) {
     const int64_t total = K * (N / 2);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_dequantize, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       Wq, scales, zeros, K, N, out);
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (f16)
+        hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(256), 0, stream, Wq, scales, zeros, K, N,
+                           out);
+    else
+        hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(256), 0, stream, Wq, scales, zeros, K,
+                           N, out);
     return hipGetLastError();
 }
 

@@ -59,10 +59,10 @@ struct QuadLoads {
     float2 xv[MT][4];   // this thread's activation pair, per m-tile and block
 };
 
-template <int MT, int NT, int QPW, int DQ>
+template <int MT, int NT, int QPW, int DQ, bool H>
 __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int M, int K,
                                                const uint8_t *__restrict__ Pq,
-                                               const float *__restrict__ Ps,
+                                               const void *__restrict__ Ps,
                                                const uint8_t *__restrict__ Pz, int N,
                                                const float *__restrict__ bias,
                                                float *__restrict__ y, int npad,
@@ -108,7 +108,15 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             R.w[t] = load_stream<u32x4_t>(Pq + oq[t] + 64u * q);  // block 4 q + g
-            R.s[t] = *reinterpret_cast<const f32x4_t *>(Ps + os[t] + 4u * q);
+            if (H) {  // four binary16 scales
+                const u32x2_t h = *reinterpret_cast<const u32x2_t *>(
+                    static_cast<const uint16_t *>(Ps) + os[t] + 4u * q);
+                R.s[t] = f32x4_t{f16_bits_to_f32((uint16_t)h.x), f16_bits_to_f32((uint16_t)(h.x >> 16)),
+                                 f16_bits_to_f32((uint16_t)h.y), f16_bits_to_f32((uint16_t)(h.y >> 16))};
+            } else {
+                R.s[t] = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(Ps) + os[t] +
+                                                            4u * q);
+            }
             R.z[t] = *reinterpret_cast<const uint16_t *>(Pz + oz[t] + 2u * q);
         }
 #pragma unroll
@@ -245,15 +253,20 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
 }  // namespace
 
 hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
-                        const float *Ps, const uint8_t *Pz, int64_t N, const float *bias, float *y,
-                        void *workspace, hipStream_t stream) {
+                        const void *Ps, bool f16, const uint8_t *Pz, int64_t N, const float *bias,
+                        float *y, void *workspace, hipStream_t stream) {
     const dim3 grid((unsigned)p.col_wgs, (unsigned)p.splits, (unsigned)p.mgroups);
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     bool launched = false;
 #define W4_X3(MTV, NTV, QV, DQV)                                                                \
     if (!launched && p.mt == MTV && p.nt == NTV && p.quads_per_wg == QV) {                      \
-        hipLaunchKernelGGL((k_mm_x3<MTV, NTV, QV, DQV>), grid, dim3(256), 0, stream, x, (int)M,  \
-                           (int)K, Pq, Ps, Pz, (int)N, bias, y, (int)p.npad, part);             \
+        if (f16)                                                                                \
+            hipLaunchKernelGGL((k_mm_x3<MTV, NTV, QV, DQV, true>), grid, dim3(256), 0, stream, x, \
+                               (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, (int)p.npad, part);  \
+        else                                                                                    \
+            hipLaunchKernelGGL((k_mm_x3<MTV, NTV, QV, DQV, false>), grid, dim3(256), 0, stream,   \
+                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, (int)p.npad,      \
+                               part);                                                           \
         launched = true;                                                                        \
     }
 #define W4_X3_Q(MTV, NTV, DQV)                                                                  \
