@@ -419,12 +419,16 @@ def main():
         secondary["i8_head_768x50257"] = head_times
 
         # full-sequence logits [58 x 50257] (the export before the last-position
-        # slice): one launch over the token-major table, 8 table copies in turn
+        # slice): the digit image of x, then one pass over the token-major
+        # table; 8 table copies in turn
         xs = torch.from_numpy(synth.activations(synth.GPT2_PROMPT, synth.GPT2_HIDDEN,
                                                 synth.CFG_HEAD)).to(dev)
         outs = torch.empty((synth.GPT2_PROMPT, synth.GPT2_VOCAB), device=dev)
         tabs = [Qk.clone() for _ in range(8)]
-        gs = capture(lambda: [w4.i8_head_logits_rows(xs, tabs[i % 8], hsk, out=outs)
+        wsr = torch.empty(w4.library().i8_head_rows_workspace_bytes(
+            synth.GPT2_PROMPT, synth.GPT2_HIDDEN), dtype=torch.uint8, device=dev)
+        gs = capture(lambda: [w4.i8_head_logits_rows(xs, tabs[i % 8], hsk, out=outs,
+                                                     workspace=wsr)
                               for i in range(16)])
         mss, _ = time_graph(gs, 10, 2)
         del gs, tabs

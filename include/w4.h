@@ -255,14 +255,22 @@ int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int6
  * step 4): logits[m, n] = hs[n] * sum_k x[m, k] * Qt[n, k] for every row m of
  * x [M, K] (fp32, row-major, 4-byte aligned), logits [M, N] fp32.  Same
  * arithmetic and precision condition as i8_head_logits_kmajor, with one
- * exponent per row.  K % 64 == 0, K <= 2048; N * ldt < 2^31; one launch,
- * no workspace.                                                             */
+ * exponent per row.  K % 64 == 0, K <= 2048; N * ldt < 2^31.  Two launches:
+ * the int8 digit image of x is written once to the workspace (caller-owned,
+ * device memory, 256-byte aligned, at least i8_head_rows_workspace_bytes(M,
+ * K) bytes: 16 K bytes per group of 4 rows plus 4 bytes per row; contents on
+ * entry do not matter and are overwritten), then the table is streamed once
+ * past all rows.  Missing or short workspace: W4_ERR_WORKSPACE.            */
+size_t i8_head_rows_workspace_bytes(int64_t M, int64_t K);
+
 int i8_check_head_logits_rows_args(const float *x, int64_t M, int64_t K, const int8_t *Qt,
                                    int64_t ldt, const float *hs, int64_t N,
-                                   const float *logits);
+                                   const float *logits, const void *workspace,
+                                   size_t workspace_bytes);
 
 int i8_head_logits_rows(const float *x, int64_t M, int64_t K, const int8_t *Qt, int64_t ldt,
-                        const float *hs, int64_t N, float *logits, void *stream);
+                        const float *hs, int64_t N, float *logits, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* Token lookup from Qt (step 3): out[t, k] = fl32(Qt[tokens[t], k] * hs[tokens[t]]),
  * fp32 [T, K], bit-exact; ids outside [0, N) as in i8_embed.               */

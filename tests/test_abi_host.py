@@ -36,6 +36,7 @@ def test_header_declares_the_entry_points():
                  "w4_abi_version", "i8_prepack_head", "i8_head_logits_kmajor",
                  "i8_check_head_logits_kmajor_args", "i8_embed_kmajor",
                  "i8_head_logits_rows", "i8_check_head_logits_rows_args",
+                 "i8_head_rows_workspace_bytes",
                  "w4h_quantize_pack", "w4h_dequantize", "w4h_prepack_kmajor",
                  "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args"):
         assert must in names
@@ -182,17 +183,26 @@ def test_head_kmajor_checks():
 
 
 def test_head_rows_checks():
-    chk = w4.library().i8_check_head_logits_rows_args
-    assert chk(A, 58, 768, A, 768, A, 50257, A) == w4.W4_OK
-    assert chk(A, 58, 4096, A, 4096, A, 100, A) == w4.W4_ERR_BAD_SHAPE   # K > 2048
-    assert chk(A, 58, 800, A, 800, A, 100, A) == w4.W4_ERR_BAD_SHAPE     # K % 64 != 0
-    assert chk(A, -1, 768, A, 768, A, 100, A) == w4.W4_ERR_BAD_SHAPE
-    assert chk(None, 0, 768, None, 768, None, 100, None) == w4.W4_OK
-    assert chk(A, 2, 768, None, 768, A, 100, A) == w4.W4_ERR_NULL_PTR
-    assert chk(A + 2, 2, 768, A, 768, A, 100, A) == w4.W4_ERR_MISALIGNED
-    assert chk(A, 2, 768, A + 8, 768, A, 100, A) == w4.W4_ERR_MISALIGNED
+    lib = w4.library()
+    chk = lib.i8_check_head_logits_rows_args
+    need = lib.i8_head_rows_workspace_bytes(58, 768)
+    # 15 groups of 4 rows x 16 K bytes, rounded to 256, then one int per row
+    assert need == (15 * 16 * 768 + 255) // 256 * 256 + 4 * 58
+    assert lib.i8_head_rows_workspace_bytes(0, 768) == 0
+    W = A
+    assert chk(A, 58, 768, A, 768, A, 50257, A, W, need) == w4.W4_OK
+    assert chk(A, 58, 768, A, 768, A, 50257, A, W, need - 1) == w4.W4_ERR_WORKSPACE
+    assert chk(A, 58, 768, A, 768, A, 50257, A, None, need) == w4.W4_ERR_WORKSPACE
+    assert chk(A, 58, 768, A, 768, A, 50257, A, W + 16, need) == w4.W4_ERR_MISALIGNED
+    assert chk(A, 58, 4096, A, 4096, A, 100, A, W, 1 << 30) == w4.W4_ERR_BAD_SHAPE  # K > 2048
+    assert chk(A, 58, 800, A, 800, A, 100, A, W, 1 << 30) == w4.W4_ERR_BAD_SHAPE    # K % 64 != 0
+    assert chk(A, -1, 768, A, 768, A, 100, A, W, 1 << 30) == w4.W4_ERR_BAD_SHAPE
+    assert chk(None, 0, 768, None, 768, None, 100, None, None, 0) == w4.W4_OK
+    assert chk(A, 2, 768, None, 768, A, 100, A, W, need) == w4.W4_ERR_NULL_PTR
+    assert chk(A + 2, 2, 768, A, 768, A, 100, A, W, need) == w4.W4_ERR_MISALIGNED
+    assert chk(A, 2, 768, A + 8, 768, A, 100, A, W, need) == w4.W4_ERR_MISALIGNED
     if NO_GPU:
-        assert w4.library().i8_head_logits_rows(A, 2, 768, A, 768, A, 100, A, None) == \
+        assert lib.i8_head_logits_rows(A, 2, 768, A, 768, A, 100, A, W, need, None) == \
             w4.W4_ERR_DEVICE
 
 

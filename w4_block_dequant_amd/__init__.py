@@ -61,8 +61,9 @@ _SIGS = {
     "w4h_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
     "w4h_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
     "w4h_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
-    "i8_check_head_logits_rows_args": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
-    "i8_head_logits_rows": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P]),
+    "i8_head_rows_workspace_bytes": (_SZ, [_I64, _I64]),
+    "i8_check_head_logits_rows_args": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _SZ]),
+    "i8_head_logits_rows": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -372,8 +373,11 @@ def i8_embed_kmajor(tokens: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor, K:
 
 
 def i8_head_logits_rows(x: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor,
-                        out: torch.Tensor | None = None):
-    """x fp32 [M, K] -> logits fp32 [M, N] for every row (token-major table Qt [N, ldt])."""
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """x fp32 [M, K] -> logits fp32 [M, N] for every row (token-major table Qt [N, ldt]).
+
+    `workspace`: uint8, at least i8_head_rows_workspace_bytes(M, K) bytes (the
+    digit image of x); the shared per-device scratch when not given."""
     _dev(x, torch.float32, "x")
     _dev(Qt, torch.int8, "Qt")
     _dev(hs, torch.float32, "hs")
@@ -383,8 +387,15 @@ def i8_head_logits_rows(x: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor,
         raise ValueError("hs must have N elements")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=Qt.device)
+    need = _lib.i8_head_rows_workspace_bytes(M, K)
+    if workspace is None:
+        ws, wsb = _workspace.get(Qt.device, need)
+    else:
+        _dev(workspace, torch.uint8, "workspace")
+        ws, wsb = workspace, workspace.numel()
     _check("i8_head_logits_rows", _lib.i8_head_logits_rows(
-        _ptr(x), M, K, _ptr(Qt), ldt, _ptr(hs), N, _ptr(out), _stream(Qt.device)))
+        _ptr(x), M, K, _ptr(Qt), ldt, _ptr(hs), N, _ptr(out), _ptr(ws), wsb,
+        _stream(Qt.device)))
     return out
 
 

@@ -355,29 +355,40 @@ int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int6
         w4::launch_head_logits_kmajor(x_last, K, Qt, ldt, hs, N, logits, as_stream(stream)));
 }
 
+size_t i8_head_rows_workspace_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    return w4::head_rows_workspace(M, K);
+}
+
 int i8_check_head_logits_rows_args(const float *x, int64_t M, int64_t K, const int8_t *Qt,
-                                   int64_t ldt, const float *hs, int64_t N, const float *logits) {
+                                   int64_t ldt, const float *hs, int64_t N, const float *logits,
+                                   const void *workspace, size_t workspace_bytes) {
     if (M < 0 || K < 64 || K % 64 != 0 || K > 2048 || N < 0 || ldt < K || ldt % 16 != 0)
         return W4_ERR_BAD_SHAPE;
     if (N > 0 && N > ((int64_t)1 << 31) / ldt - 1) return W4_ERR_BAD_SHAPE;
     if (M > 0 && (M > ((int64_t)1 << 31) / K - 1 || M > kMaxElems / (N > 0 ? N : 1) ||
-                  (M + 3) / 4 * ((N + 511) / 512) * 8 > ((int64_t)1 << 31) - 1))
+                  (M + 3) / 4 > ((int64_t)1 << 31) / (16 * K) - 1))
         return W4_ERR_BAD_SHAPE;
     if (M == 0 || N == 0) return W4_OK;
     if (!x || !Qt || !hs || !logits) return W4_ERR_NULL_PTR;
     if (!aligned(x, 4) || !aligned(Qt, 16) || !aligned(hs, 4) || !aligned(logits, 4))
         return W4_ERR_MISALIGNED;
+    if (workspace == nullptr || workspace_bytes < w4::head_rows_workspace(M, K))
+        return W4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
     return W4_OK;
 }
 
 int i8_head_logits_rows(const float *x, int64_t M, int64_t K, const int8_t *Qt, int64_t ldt,
-                        const float *hs, int64_t N, float *logits, void *stream) {
-    int st = i8_check_head_logits_rows_args(x, M, K, Qt, ldt, hs, N, logits);
+                        const float *hs, int64_t N, float *logits, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    int st = i8_check_head_logits_rows_args(x, M, K, Qt, ldt, hs, N, logits, workspace,
+                                            workspace_bytes);
     if (st) return st;
     if (M == 0 || N == 0) return W4_OK;
     if ((st = device_check())) return st;
-    return launched(
-        w4::launch_head_rows_kmajor(x, M, K, Qt, ldt, hs, N, logits, as_stream(stream)));
+    return launched(w4::launch_head_rows_kmajor(x, M, K, Qt, ldt, hs, N, logits, workspace,
+                                                as_stream(stream)));
 }
 
 int i8_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t ldt,

@@ -19,6 +19,8 @@
 // combined exactly in fp64, so the only rounding is that of x to fixed point
 // (at most 2^-30 max|x| per element) and the final scaling by hs[n] 2^(e-30).
 // Non-finite x gives NaN logits.
+#include <limits.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -177,56 +179,35 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits_mfma(const float *__
     }
 }
 
-// Full-sequence logits: 4 rows of x per workgroup.  A-operand row 4 r + l is
-// digit l of row r (each row has its own exponent e_r), so all 16 rows of the
-// MFMA carry data and lane (g, c) ends with the four digit sums of row g,
-// column c.  The table is the same B operand as above.  Workgroups that share
-// a 64-token tile (one per group of 4 rows) are given ids that map to the same
-// XCD (ids are dealt to the 8 XCDs in turn), so the tile's table rows come
-// from HBM about once and from that XCD's L2 for the other row groups.
-template <int CH, int XPT>
-__global__ __launch_bounds__(256) void k_head_rows_mfma(const float *__restrict__ x, int M, int K,
-                                                        const int8_t *__restrict__ Qt, int ldt,
-                                                        const float *__restrict__ hs, int N,
-                                                        float *__restrict__ logits, int ntiles,
-                                                        int nrg) {
-    extern __shared__ i32x4_t limbs_v[];  // [16][K] bytes: row 4 r + l = digit l of row r
-    int8_t *limbs = reinterpret_cast<int8_t *>(limbs_v);
+// Full-sequence logits, first launch: the digit image of x, built once.
+// One workgroup per group of 4 rows.  A-operand row 4 r + l of the group is
+// digit l of row r (each row has its own exponent e_r), laid out as the MFMA
+// reads it: img[group][j][4 r + l][kk] holds the digit of x[4 group + r,
+// 64 j + kk], so one 16-row x 64-byte block per K-step j.  erow[m] is e_m, or
+// INT_MIN for a row with a non-finite entry.  Rows past M are zero.
+template <int XPT>
+__global__ __launch_bounds__(256) void k_head_digits(const float *__restrict__ x, int M, int K,
+                                                     int8_t *__restrict__ img,
+                                                     int *__restrict__ erow) {
+    extern __shared__ i32x4_t dimg_v[];  // [K / 64][16][64] bytes
+    int8_t *dimg = reinterpret_cast<int8_t *>(dimg_v);
     __shared__ float wmax[4][4];
-    const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
-    const int tile = (local / nrg) * 8 + xcd, rg = local % nrg;
-    if (tile >= ntiles) return;  // whole workgroup, before any barrier
-    const int m0 = 4 * rg;
+    const int m0 = 4 * blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const int nbase = tile * 64 + wave * 16;
-    const int n = min(nbase + c, N - 1);
-    const int NJ = K / 64, RK = 4 * K;
+    const int RK = 4 * K;
 
-    // x of the 4 rows first, then the table rows (as in the 1-row kernel)
     float xv[XPT];  // element e = tid + 256 i of the 4 x K block
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int e = min(tid + 256 * i, RK - 1);
-        const int r = e / K;
-        xv[i] = x[(size_t)min(m0 + r, M - 1) * K + (e - r * K)];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t rowoff = (uint32_t)n * (uint32_t)ldt + 16u * g;
-    u32x4_t b[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-        b[j] = load_stream<u32x4_t>(Qt + rowoff + 64u * (uint32_t)min(j, NJ - 1));
-    __builtin_amdgcn_sched_barrier(0);
-
-    // per-row max |x| (a non-finite entry makes its row's max infinite)
-    float mr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int e = tid + 256 * i;
         const int r = e / K;
-        const bool valid = e < RK && m0 + r < M;
-        if (!valid) xv[i] = 0.0f;
+        xv[i] = (e < RK && m0 + r < M) ? x[(size_t)(m0 + r) * K + (e - r * K)] : 0.0f;
+    }
+    // per-row max |x| (a non-finite entry makes its row's max infinite)
+    float mr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int r = (tid + 256 * i) / K;
         const float a = __builtin_isfinite(xv[i]) ? __builtin_fabsf(xv[i]) : __builtin_inff();
 #pragma unroll
         for (int q = 0; q < 4; ++q) mr[q] = (r == q) ? __builtin_fmaxf(mr[q], a) : mr[q];
@@ -248,6 +229,17 @@ __global__ __launch_bounds__(256) void k_head_rows_mfma(const float *__restrict_
         er[q] = 0;
         if (okr[q] && am > 0.0f) (void)__builtin_frexpf(am, &er[q]);
     }
+    if (tid < 4 && m0 + tid < M) {
+        int e = er[0];
+        bool ok = okr[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (tid == q) {
+                e = er[q];
+                ok = okr[q];
+            }
+        erow[m0 + tid] = ok ? e : INT_MIN;
+    }
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int e = tid + 256 * i;
@@ -268,52 +260,133 @@ __global__ __launch_bounds__(256) void k_head_rows_mfma(const float *__restrict_
             const int v2 = (v1 - l1) >> 8;
             const int l2 = (int)(int8_t)(v2 & 0xFF);
             const int l3 = (v2 - l2) >> 8;
-            int8_t *lr = limbs + (4 * r) * K + k;
-            lr[0] = (int8_t)l0;
-            lr[K] = (int8_t)l1;
-            lr[2 * K] = (int8_t)l2;
-            lr[3 * K] = (int8_t)l3;
+            int8_t *d = dimg + ((k >> 6) * 16 + 4 * r) * 64 + (k & 63);
+            d[0] = (int8_t)l0;
+            d[64] = (int8_t)l1;
+            d[128] = (int8_t)l2;
+            d[192] = (int8_t)l3;
         }
     }
     __syncthreads();
+    i32x4_t *dst = reinterpret_cast<i32x4_t *>(img + (size_t)blockIdx.x * 16 * K);
+    for (int i = tid; i < K; i += 256) dst[i] = dimg_v[i];  // 16 K bytes
+}
 
-    i32x4_t acc = {0, 0, 0, 0};
-    for (int j0 = 0; j0 < NJ; j0 += CH) {
-        if (j0 > 0) {
+// Row groups per LDS chunk: two chunk buffers of at most 32 KB of digit
+// blocks each (16 K bytes per group, K >= 64), so at most 32 groups.
+constexpr int kHeadRowsMaxChunk = 32;
+
+// Copy `elems` 16-byte elements (a multiple of 64) from global memory to LDS
+// with the direct global-to-LDS load: wave w moves elements w*64 + 256 i +
+// lane, no registers involved, completion counted by vmcnt.
+__device__ __forceinline__ void copy_to_lds(const i32x4_t *__restrict__ src, i32x4_t *dst,
+                                            int elems, int wave, int lane) {
+    for (int i0 = wave * 64; i0 < elems; i0 += 256)
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src + i0 + lane),
+                                         reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                             reinterpret_cast<uintptr_t>(dst + i0)),
+                                         16, 0, 0);
+}
+
+// Full-sequence logits, second launch: the table stays in registers, the
+// rows stream past it.  Wave w of workgroup b owns TB tiles of 16 tokens
+// (tokens 16 (TB (4 b + w) + t) + c); it loads their table rows once, as the
+// B operands of all K / 64 steps, then takes every row group in turn.  The
+// digit blocks come through LDS in chunks of row groups, double-buffered: the
+// direct global-to-LDS copy of chunk i + 1 is in flight while the MFMAs run on
+// chunk i.  Each A operand read from LDS feeds TB MFMAs, and lane (g, c) ends
+// with the four digit sums of row 4 group + g, token c of each tile, combined
+// exactly as in the one-row kernel.  The table comes from HBM once; x only
+// through the small digit image.
+template <int TB, int NJM>
+__global__ __launch_bounds__(256) void k_head_rows_mfma(const int8_t *__restrict__ img,
+                                                        const int *__restrict__ erow, int M,
+                                                        int K, const int8_t *__restrict__ Qt,
+                                                        int ldt, const float *__restrict__ hs,
+                                                        int N, float *__restrict__ logits,
+                                                        int chunk) {
+    extern __shared__ i32x4_t abuf[];  // [2][chunk][K / 64][16][64] bytes
+    __shared__ int es[2][kHeadRowsMaxChunk * 4];  // exponents of each buffer's rows
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int NJ = K / 64, nrg = (M + 3) / 4;
+    const int tb0 = (blockIdx.x * 4 + wave) * 16 * TB;
+    const int per_rg = NJ * 64;  // 16-byte elements per row group
+    i32x4_t *bufs[2] = {abuf, abuf + chunk * per_rg};
+    const i32x4_t *src = reinterpret_cast<const i32x4_t *>(img);
+
+    // stage one chunk (rows 4 rg0 ...) into buffer q: digit blocks and exponents
+    auto stage = [&](int rg0, int q) {
+        const int cnt = min(chunk, nrg - rg0);
+        copy_to_lds(src + (size_t)rg0 * per_rg, bufs[q], cnt * per_rg, wave, lane);
+        if (wave == 0 && lane < 4 * cnt && 4 * rg0 + lane < M)
+            __builtin_amdgcn_global_load_lds(
+                static_cast<const void *>(erow + 4 * rg0 + lane),
+                reinterpret_cast<__attribute__((address_space(3))) void *>(
+                    reinterpret_cast<uintptr_t>(&es[q][0])),
+                4, 0, 0);
+    };
+
+    stage(0, 0);
+    u32x4_t b[TB][NJM];
+    float hsv[TB];
 #pragma unroll
-            for (int j = 0; j < CH; ++j)
-                b[j] = load_stream<u32x4_t>(Qt + rowoff + 64u * (uint32_t)min(j0 + j, NJ - 1));
-        }
+    for (int t = 0; t < TB; ++t) {
+        const int n = min(tb0 + 16 * t + c, N - 1);
+        const uint32_t rowoff = (uint32_t)n * (uint32_t)ldt + 16u * g;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int jj = j0 + j;
-            if (jj < NJ) {
-                const i32x4_t a =
-                    *reinterpret_cast<const i32x4_t *>(limbs + c * K + 64 * jj + 16 * g);
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                    a, __builtin_bit_cast(i32x4_t, b[j]), acc, 0, 0, 0);
-            }
-        }
+        for (int j = 0; j < NJM; ++j)
+            b[t][j] = load_stream<u32x4_t>(Qt + rowoff + 64u * (uint32_t)min(j, NJ - 1));
+        hsv[t] = hs[n];
     }
 
-    // lane (g, c) holds the four digit sums of row m0 + g, column nbase + c
-    const int m = m0 + g;
-    if (m < M && nbase + c < N) {
-        int eg = er[0];
-        bool og = okr[0];
+    int q = 0;
+    for (int rg0 = 0; rg0 < nrg; rg0 += chunk, q ^= 1) {
+        const int cnt = min(chunk, nrg - rg0);
+        // this chunk's copies (and the table rows) have landed, in every wave;
+        // every wave is also done with the other buffer (read last round)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (rg0 + chunk < nrg) stage(rg0 + chunk, q ^ 1);
+        const i32x4_t *cb = bufs[q];
+        for (int r = 0; r < cnt; ++r) {
+            i32x4_t acc[TB];
 #pragma unroll
-        for (int q = 1; q < 4; ++q)
-            if (g == q) {
-                eg = er[q];
-                og = okr[q];
+            for (int t = 0; t < TB; ++t) acc[t] = i32x4_t{0, 0, 0, 0};
+            // straight-line: steps past K read a valid block and multiply a
+            // zero A operand (adds exactly 0), so the LDS reads can be issued
+            // ahead of the MFMAs
+            const i32x4_t *ap = cb + r * per_rg + c * 4 + g;
+            i32x4_t a[NJM];
+#pragma unroll
+            for (int j = 0; j < NJM; ++j) a[j] = ap[min(j, NJ - 1) * 64];
+#pragma unroll
+            for (int j = 0; j < NJM; ++j) {
+                const i32x4_t aj = j < NJ ? a[j] : i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        aj, __builtin_bit_cast(i32x4_t, b[t][j]), acc[t], 0, 0, 0);
             }
-        float out = __builtin_nanf("");
-        if (og) {
-            const double t = ((double)acc[3] * 16777216.0 + (double)acc[2] * 65536.0) +
-                             ((double)acc[1] * 256.0 + (double)acc[0]);
-            out = (float)(__builtin_ldexp(t, eg - 30) * (double)hs[n]);
+            const int m = 4 * (rg0 + r) + g;
+            if (m < M) {
+                const int e = es[q][4 * r + g];
+#pragma unroll
+                for (int t = 0; t < TB; ++t) {
+                    const int n = tb0 + 16 * t + c;
+                    if (n < N) {
+                        float out = __builtin_nanf("");
+                        if (e != INT_MIN) {
+                            const double v = ((double)acc[t][3] * 16777216.0 +
+                                              (double)acc[t][2] * 65536.0) +
+                                             ((double)acc[t][1] * 256.0 + (double)acc[t][0]);
+                            out = (float)(__builtin_ldexp(v, e - 30) * (double)hsv[t]);
+                        }
+                        logits[(size_t)m * N + n] = out;
+                    }
+                }
+            }
         }
-        logits[(size_t)m * N + nbase + c] = out;
     }
 }
 
@@ -358,20 +431,44 @@ hipError_t launch_head_logits_kmajor(const float *x, int64_t K, const int8_t *Qt
     return hipGetLastError();
 }
 
+size_t head_rows_workspace(int64_t M, int64_t K) {
+    const int64_t nrg = (M + 3) / 4;
+    const size_t img = ((size_t)nrg * 16 * K + 255) / 256 * 256;
+    return img + (size_t)4 * M;
+}
+
 hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const int8_t *Qt,
                                   int64_t ldt, const float *hs, int64_t N, float *logits,
-                                  hipStream_t stream) {
-    const int ntiles = (int)((N + 63) / 64), nrg = (int)((M + 3) / 4);
-    const int64_t wgs = (int64_t)((ntiles + 7) / 8) * 8 * nrg;
-    const size_t shm = (size_t)16 * K;
-#define W4_HR(CHV, XV)                                                                            \
-    hipLaunchKernelGGL((k_head_rows_mfma<CHV, XV>), dim3((unsigned)wgs), dim3(256), shm, stream, x, \
-                       (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits, ntiles, nrg)
-    if (K <= 256) W4_HR(4, 4);
-    else if (K <= 512) W4_HR(8, 8);
-    else if (K <= 768) W4_HR(12, 12);
-    else if (K <= 1024) W4_HR(16, 16);
-    else W4_HR(16, 32);
+                                  void *workspace, hipStream_t stream) {
+    const int64_t nrg = (M + 3) / 4;
+    int8_t *img = static_cast<int8_t *>(workspace);
+    int *erow = reinterpret_cast<int *>(img + (head_rows_workspace(M, K) - (size_t)4 * M));
+    const size_t dshm = (size_t)16 * K;
+#define W4_HD(XV)                                                                                 \
+    hipLaunchKernelGGL((k_head_digits<XV>), dim3((unsigned)nrg), dim3(256), dshm, stream, x,      \
+                       (int)M, (int)K, img, erow)
+    if (K <= 256) W4_HD(4);
+    else if (K <= 512) W4_HD(8);
+    else if (K <= 1024) W4_HD(16);
+    else W4_HD(32);
+#undef W4_HD
+    // two LDS buffers of a chunk of row groups each, at most 32 KB per buffer
+    // (64 KB per workgroup, so two workgroups fit a compute unit)
+    const int64_t per_rg = (int64_t)16 * K;
+    int64_t chunk = ((int64_t)32 << 10) / per_rg;
+    if (chunk < 1) chunk = 1;
+    if (chunk > kHeadRowsMaxChunk) chunk = kHeadRowsMaxChunk;
+    if (chunk > nrg) chunk = nrg;
+    const size_t shm = (size_t)(2 * chunk * per_rg);
+#define W4_HR(TBV, NJV)                                                                           \
+    hipLaunchKernelGGL((k_head_rows_mfma<TBV, NJV>),                                             \
+                       dim3((unsigned)((N + 64 * TBV - 1) / (64 * TBV))), dim3(256), shm, stream, \
+                       img, erow, (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits, (int)chunk)
+    if (K <= 256) W4_HR(2, 4);
+    else if (K <= 512) W4_HR(2, 8);
+    else if (K <= 768) W4_HR(2, 12);
+    else if (K <= 1024) W4_HR(2, 16);
+    else W4_HR(1, 32);
 #undef W4_HR
     return hipGetLastError();
 }

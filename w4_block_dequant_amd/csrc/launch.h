@@ -54,9 +54,10 @@ hipError_t launch_head_prepack(const int8_t *Q, int64_t K, int64_t N, int64_t ld
 hipError_t launch_head_logits_kmajor(const float *x, int64_t K, const int8_t *Qt, int64_t ldt,
                                      const float *hs, int64_t N, float *logits,
                                      hipStream_t stream);
+size_t head_rows_workspace(int64_t M, int64_t K);
 hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const int8_t *Qt,
                                   int64_t ldt, const float *hs, int64_t N, float *logits,
-                                  hipStream_t stream);
+                                  void *workspace, hipStream_t stream);
 hipError_t launch_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t ldt,
                                const float *hs, int64_t K, int64_t N, float *out, int *d_status,
                                hipStream_t stream);

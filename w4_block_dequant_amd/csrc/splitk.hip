@@ -8,23 +8,35 @@
 namespace w4 {
 namespace {
 
+// Grid: x over groups of 4 columns, y strides over rows (no index division).  Each
+// thread adds 4 adjacent outputs with 16-byte reads of every plane (npad is
+// a multiple of 4 and the planes are 256-byte aligned), in split order.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ part,
-                                                       int64_t splits, int64_t rows, int64_t N,
+                                                       int splits, int64_t rows, int N,
                                                        int64_t npad,
                                                        const float *__restrict__ bias,
                                                        const float *__restrict__ col_scale,
                                                        float unit, float *__restrict__ y) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= rows * N) return;
-    const int64_t m = i / N, n = i - m * N;
-    const float *p = part + m * npad + n;
+    const int n0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (n0 >= N) return;
     const int64_t plane = rows * npad;
-    float v = 0.0f;
-#pragma unroll 8
-    for (int64_t s = 0; s < splits; ++s) v += p[s * plane];
-    if (col_scale) v = (v * unit) * col_scale[n];
-    if (bias) v += bias[n];
-    y[i] = v;
+    for (int64_t m = blockIdx.y; m < rows; m += gridDim.y) {
+        const float *p = part + m * npad + n0;
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+        for (int s = 0; s < splits; ++s)
+            v += *reinterpret_cast<const f32x4_t *>(p + s * plane);
+        float *yo = y + m * N;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + j;
+            if (n >= N) break;
+            float r = v[j];
+            if (col_scale) r = (r * unit) * col_scale[n];
+            if (bias) r += bias[n];
+            yo[n] = r;
+        }
+    }
 }
 
 }  // namespace
@@ -32,10 +44,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 hipError_t launch_splitk_reduce(const float *part, int64_t splits, int64_t rows, int64_t N,
                                 int64_t npad, const float *bias, const float *col_scale,
                                 float unit, float *y, hipStream_t stream) {
-    const int64_t total = rows * N;
-    if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       part, splits, rows, N, npad, bias, col_scale, unit, y);
+    if (rows == 0 || N == 0) return hipSuccess;
+    const int64_t groups = (N + 3) / 4;
+    const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
+    hipLaunchKernelGGL(k_splitk_reduce, grid, dim3(256), 0, stream, part, (int)splits, rows,
+                       (int)N, npad, bias, col_scale, unit, y);
     return hipGetLastError();
 }
 
