@@ -77,6 +77,10 @@ _SIGS = {
     "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
     "orc_f16_array_to_f32": (None, [_P, _I64, _P]),
     "orc_w4h_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "orc_gelu": (ctypes.c_double, [ctypes.c_double]),
+    "orc_silu": (ctypes.c_double, [ctypes.c_double]),
+    "orc_w4_matmul_ep": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, ctypes.c_int,
+                                         _P, _P]),
 }
 
 
@@ -207,6 +211,38 @@ class Oracle:
                self._l.orc_w4_matmul(_ptr(x), M, K, _ptr(_c(Wq, np.uint8)),
                                      _ptr(_c(scales, np.float32)), _ptr(_c(zeros, np.uint8)),
                                      N, _ptr(b), _ptr(y), _ptr(bound)))
+        return y, bound
+
+    # -- fused epilogues -----------------------------------------------------------
+    ACTS = {"none": 0, "gelu": 1, "swiglu": 2}
+
+    def gelu(self, v):
+        """gelu (tanh form) of each element, fp64."""
+        f = self._l.orc_gelu
+        return np.array([f(float(a)) for a in np.asarray(v, np.float64).reshape(-1)]).reshape(
+            np.shape(v))
+
+    def silu(self, v):
+        """silu of each element, fp64."""
+        f = self._l.orc_silu
+        return np.array([f(float(a)) for a in np.asarray(v, np.float64).reshape(-1)]).reshape(
+            np.shape(v))
+
+    def w4_matmul_ep(self, x, Wq, scales, zeros, bias=None, residual=None, act="none"):
+        """act(x . dequantize(W) + bias) (+ residual) -> (y [M, N_out], bound [M, N_out])."""
+        x = _c(x, np.float32)
+        M, K = x.shape
+        N = _c(scales, np.float32).shape[1]
+        a = self.ACTS[act]
+        nout = N // 2 if act == "swiglu" else N
+        b = None if bias is None else _c(bias, np.float32)
+        r = None if residual is None else _c(residual, np.float32)
+        y = np.zeros((M, nout), np.float32)
+        bound = np.zeros((M, nout), np.float64)
+        _check("orc_w4_matmul_ep",
+               self._l.orc_w4_matmul_ep(_ptr(x), M, K, _ptr(_c(Wq, np.uint8)),
+                                        _ptr(_c(scales, np.float32)), _ptr(_c(zeros, np.uint8)),
+                                        N, _ptr(b), _ptr(r), a, _ptr(y), _ptr(bound)))
         return y, bound
 
     # -- fp16-scale variant ------------------------------------------------------

@@ -163,26 +163,47 @@ int orc_w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t 
     return ORC_OK;
 }
 
+/* Row m of x . W + bias in fp64 (t[n], unrounded) and each output's bound
+ * 1e-5 * (sum_k |x w| + |bias|) + 1e-6 (tb[n]).                             */
+static void row_f64(const float *xr, int64_t K, const float *W, int64_t N, const float *bias,
+                    double *t, double *tb)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = (double)xr[k] * (double)W[k * N + n];
+            acc += p;
+            mag += fabs(p);
+        }
+        if (bias) {
+            acc += (double)bias[n];
+            mag += fabs((double)bias[n]);
+        }
+        t[n] = acc;
+        tb[n] = 1e-5 * mag + 1e-6;
+    }
+}
+
 int orc_matmul_f64(const float *x, int64_t M, int64_t K, const float *W, int64_t N,
                    const float *bias, float *y, double *bound)
 {
     if (M < 0 || K < 0 || N < 0) return ORC_BAD_SHAPE;
+    double *t = (double *)malloc((size_t)N * sizeof(double) + 1);
+    double *tb = (double *)malloc((size_t)N * sizeof(double) + 1);
+    if (!t || !tb) {
+        free(t);
+        free(tb);
+        return ORC_NO_MEMORY;
+    }
     for (int64_t m = 0; m < M; ++m) {
+        row_f64(x + m * K, K, W, N, bias, t, tb);
         for (int64_t n = 0; n < N; ++n) {
-            double acc = 0.0, mag = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                double p = (double)x[m * K + k] * (double)W[k * N + n];
-                acc += p;
-                mag += fabs(p);
-            }
-            if (bias) {
-                acc += (double)bias[n];
-                mag += fabs((double)bias[n]);
-            }
-            y[m * N + n] = (float)acc;
-            if (bound) bound[m * N + n] = 1e-5 * mag + 1e-6;
+            y[m * N + n] = (float)t[n];
+            if (bound) bound[m * N + n] = tb[n];
         }
     }
+    free(t);
+    free(tb);
     return ORC_OK;
 }
 
@@ -331,4 +352,64 @@ int orc_w4h_quantize_pack(const float *W, int64_t K, int64_t N,
 void orc_f16_array_to_f32(const uint16_t *h, int64_t count, float *out)
 {
     for (int64_t i = 0; i < count; ++i) out[i] = orc_f16_to_f32(h[i]);
+}
+
+/* ---- fused epilogues ---------------------------------------------------- */
+
+double orc_gelu(double v)
+{
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));
+}
+
+double orc_silu(double v)
+{
+    return v / (1.0 + exp(-v));
+}
+
+int orc_w4_matmul_ep(const float *x, int64_t M, int64_t K,
+                     const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t N,
+                     const float *bias, const float *residual, int act, float *y,
+                     double *bound)
+{
+    if (M < 0 || bad_w4_shape(K, N)) return ORC_BAD_SHAPE;
+    if (act != ORC_ACT_NONE && act != ORC_ACT_GELU && act != ORC_ACT_SWIGLU)
+        return ORC_BAD_SHAPE;
+    if (act == ORC_ACT_SWIGLU && N % 2 != 0) return ORC_BAD_SHAPE;
+    const int64_t nout = act == ORC_ACT_SWIGLU ? N / 2 : N;
+    float *W_hat = (float *)malloc((size_t)(K * N) * sizeof(float) + 1);
+    double *t = (double *)malloc((size_t)N * sizeof(double) + 1);
+    double *tb = (double *)malloc((size_t)N * sizeof(double) + 1);
+    if (!W_hat || !t || !tb) {
+        free(W_hat);
+        free(t);
+        free(tb);
+        return ORC_NO_MEMORY;
+    }
+    int st = orc_w4_dequantize(Wq, scales, zeros, K, N, W_hat);
+    for (int64_t m = 0; st == ORC_OK && m < M; ++m) {
+        row_f64(x + m * K, K, W_hat, N, bias, t, tb);  /* pre-activation values */
+        for (int64_t i = 0; i < nout; ++i) {
+            double o, b;
+            if (act == ORC_ACT_SWIGLU) {
+                const double g = t[2 * i], u = t[2 * i + 1], sg = orc_silu(g);
+                o = sg * u;
+                b = 1.1 * fabs(u) * tb[2 * i] + fabs(sg) * tb[2 * i + 1] +
+                    ldexp(fabs(g) * fabs(u) + fabs(o), -20);
+            } else if (act == ORC_ACT_GELU) {
+                o = orc_gelu(t[i]);
+                b = 1.13 * tb[i] + ldexp(fabs(t[i]) + fabs(o), -20);
+            } else {
+                o = t[i];
+                b = tb[i];
+            }
+            if (residual) o += (double)residual[m * nout + i];
+            y[m * nout + i] = (float)o;
+            if (bound) bound[m * nout + i] = b + ldexp(fabs(o), -23);
+        }
+    }
+    free(W_hat);
+    free(t);
+    free(tb);
+    return st;
 }

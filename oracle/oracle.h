@@ -131,6 +131,32 @@ void orc_f16_array_to_f32(const uint16_t *h, int64_t count, float *out);
 int orc_w4h_quantize_pack(const float *W, int64_t K, int64_t N,
                           uint8_t *Wq, uint16_t *scales, uint8_t *zeros);
 
+/* ---- Fused epilogues (pages "rlx-web": a SwiGLU MLP; "zero-tvm": a fused
+ * gate + up + SiLU kernel and a fused residual add; GPT-2's MLP activation is
+ * GELU, which the pages do not spell out: the tanh form is our reading).
+ * t[m, n] = sum_k x[m, k] * W_hat[k, n] + bias[n], kept in fp64, then
+ *   ORC_ACT_NONE:   o[m, n] = t[m, n]
+ *   ORC_ACT_GELU:   o[m, n] = gelu(t[m, n])
+ *   ORC_ACT_SWIGLU: o[m, i] = silu(t[m, 2 i]) * t[m, 2 i + 1]   (N even)
+ * (gate and up columns interleaved), y = fl32(o + residual) with residual
+ * [M, N_out] optional, N_out = N / 2 for SWIGLU, else N.                   */
+enum { ORC_ACT_NONE = 0, ORC_ACT_GELU = 1, ORC_ACT_SWIGLU = 2 };
+
+/* gelu(v) = v / 2 * (1 + tanh(sqrt(2 / pi) * (v + 0.044715 v^3)))          */
+double orc_gelu(double v);
+/* silu(v) = v / (1 + exp(-v))                                               */
+double orc_silu(double v);
+
+/* bound[m, n_out]: the tolerance an fp32 implementation is held to, from the
+ * matmul bound B = 1e-5 * (sum_k |x w| + |bias|) + 1e-6 of each pre-activation
+ * value carried through the activation's slope (|gelu'| <= 1.13, |silu'| <=
+ * 1.1), plus 2^-20 of the magnitudes entering the activation for its fp32
+ * evaluation and 2^-23 |y| for the final additions.                        */
+int orc_w4_matmul_ep(const float *x, int64_t M, int64_t K,
+                     const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t N,
+                     const float *bias, const float *residual, int act, float *y,
+                     double *bound);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,11 @@ different route to the same fact.
   * head: one-hot rows, sign symmetry, full use of [-127, 127], the
     round-trip bound, exact rational logits;
   * embedding lookup: rows of the dequantized table;
-  * byte budget: the GPT-2 small q4 file size the page prints.
+  * byte budget: the GPT-2 small q4 file size the page prints;
+  * fused epilogues: GELU against the exact (erf) GELU within the tanh form's
+    known 5e-4 gap, SiLU against its tanh form, the odd-part identity
+    f(v) - f(-v) = v of both, and one-hot rows through the epilogue (exact
+    pre-activation values, gate/up pairing, a closed gate).
 """
 from __future__ import annotations
 
@@ -616,7 +620,78 @@ def pin_f16_degenerate_and_errors(orc):
             assert abs(F(y[m, n]) - exact) <= F(ulp32(y[m, n]))
 
 
+# --------------------------------------------------------------------------
+# fused epilogues
+# --------------------------------------------------------------------------
+def pin_activations(orc):
+    import math
+    v = np.concatenate([np.linspace(-8.0, 8.0, 161), [-30.0, -1e-3, 1e-3, 30.0]])
+    g = orc.gelu(v)
+    si = orc.silu(v)
+    assert orc.gelu([0.0])[0] == 0.0 and orc.silu([0.0])[0] == 0.0
+    for a, ga, sa in zip(v, g, si):
+        # both are v times a sigmoid-like gate: f(v) - f(-v) = v
+        assert abs((ga - orc.gelu([-a])[0]) - a) <= 1e-14 * (1 + abs(a))
+        assert abs((sa - orc.silu([-a])[0]) - a) <= 1e-14 * (1 + abs(a))
+        # the tanh form stays within 5e-4 of the exact (erf) GELU
+        assert abs(ga - 0.5 * a * (1.0 + math.erf(a / math.sqrt(2.0)))) <= 5e-4
+        # silu through tanh instead of exp: v/2 (1 + tanh(v/2))
+        assert abs(sa - 0.5 * a * (1.0 + math.tanh(0.5 * a))) <= 1e-14 * (1 + abs(a))
+    # far tails: the identity and the zero gate
+    assert abs(orc.gelu([12.0])[0] - 12.0) < 1e-12 and abs(orc.gelu([-12.0])[0]) < 1e-12
+    assert abs(orc.silu([-40.0])[0]) < 1e-15
+
+
+def pin_epilogue_matmul(orc):
+    K, N = 64, 8
+    W, q, z, s = _on_grid(K, N, seed=11)
+    Wq, sc, zp = orc.quantize_pack(W)
+    What = orc.dequantize(Wq, sc, zp, K, N)
+    assert np.array_equal(What, W)  # on-grid weights come back exactly
+    b = (np.arange(N, dtype=np.float32) - 3.0) * np.float32(0.25)
+    # one-hot rows: t = row k of W + bias, exact in fp64
+    x = np.eye(K, dtype=np.float32)[[0, 5, 33, 63]]
+    t = What[[0, 5, 33, 63]].astype(np.float64) + b[None, :]
+    r4 = np.linspace(-1.0, 1.0, 4 * N, dtype=np.float32).reshape(4, N)
+    # no activation: fl32(t + r)
+    y, bound = orc.w4_matmul_ep(x, Wq, sc, zp, b, r4, act="none")
+    for m in range(4):
+        for n in range(N):
+            assert y[m, n] == f32_round(F(t[m, n]) + F(r4[m, n]))
+    y0, b0 = orc.w4_matmul(x, Wq, sc, zp, b)
+    yn, bn = orc.w4_matmul_ep(x, Wq, sc, zp, b, None, act="none")
+    assert np.array_equal(yn, y0)
+    assert np.allclose(bn, b0 + np.ldexp(np.abs(y0.astype(np.float64)), -23), rtol=1e-12, atol=0)
+    # GELU on t, then the residual
+    y, bound = orc.w4_matmul_ep(x, Wq, sc, zp, b, r4, act="gelu")
+    want = (orc.gelu(t) + r4).astype(np.float32)
+    assert np.array_equal(y, want)
+    assert (bound >= 1.13e-6).all() and np.isfinite(bound).all()
+    # SwiGLU: columns 2i (gate) and 2i+1 (up) of t
+    r2 = r4[:, : N // 2]
+    y, bound = orc.w4_matmul_ep(x, Wq, sc, zp, b, r2, act="swiglu")
+    assert y.shape == (4, N // 2)
+    for m in range(4):
+        for i in range(N // 2):
+            gt, up = t[m, 2 * i], t[m, 2 * i + 1]
+            gate = 0.5 * gt * (1.0 + np.tanh(0.5 * gt))  # silu(g) through tanh
+            want = gate * up + float(r2[m, i])
+            assert abs(float(y[m, i]) - want) <= ulp32(want) + 1e-15 * abs(gate * up), (m, i)
+    # a zero gate closes its output: W's gate column 0 is zero -> y = r
+    Wz = W.copy()
+    Wz[:, 0] = 0.0
+    Wq2, sc2, zp2 = orc.quantize_pack(Wz)
+    y, _ = orc.w4_matmul_ep(x, Wq2, sc2, zp2, None, r2, act="swiglu")
+    assert np.array_equal(y[:, 0], r2[:, 0])
+    # an unknown activation code is a shape error
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod._check("orc_w4_matmul_ep", orc._l.orc_w4_matmul_ep(
+            None, 0, K, None, None, None, N, None, None, 7, None, None))
+
+
 ALL_PINS = [
+    pin_activations,
+    pin_epilogue_matmul,
     pin_f16_conversion,
     pin_f16_quantizer,
     pin_f16_degenerate_and_errors,

@@ -4,9 +4,11 @@ Each mutant is the oracle's C source with one textual change, compiled into a
 temporary directory with the oracle's own flags.  The mistakes cover every
 step: nibble order, the block range, rounding, the scale divisor, the code
 formula, the zero point's sign, the dequantization formula and its block
-index, the matmul's bias, indexing and accumulation precision, the bound, and
-the head's scale and rounding.  A mutant that passes every pin would mean the
-pins cannot tell that mistake from the correct oracle.
+index, the matmul's bias, indexing and accumulation precision, the bound, the
+head's scale and rounding, and the fused epilogues (GELU's constants, SiLU's
+sign, the SwiGLU pairing, the order of activation and residual).  A mutant
+that passes every pin would mean the pins cannot tell that mistake from the
+correct oracle.
 """
 import os
 import shutil
@@ -17,6 +19,22 @@ import oracle
 from oracle_pins import ALL_PINS
 
 MUTATIONS = {
+    "gelu_coefficient_typo": (
+        "return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));",
+        "return 0.5 * v * (1.0 + tanh(c * (v + 0.44715 * v * v * v)));"),
+    "gelu_missing_half": (
+        "return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));",
+        "return v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));"),
+    "silu_sign": (
+        "return v / (1.0 + exp(-v));",
+        "return v / (1.0 + exp(v));"),
+    "swiglu_pair_swapped": (
+        "const double g = t[2 * i], u = t[2 * i + 1], sg = orc_silu(g);",
+        "const double g = t[2 * i + 1], u = t[2 * i], sg = orc_silu(g);"),
+    "epilogue_residual_before_act": (
+        "                o = orc_gelu(t[i]);",
+        "                o = orc_gelu(t[i] + (residual ? (double)residual[m * nout + i] : 0.0));"),
+
     "f16_truncates": (
         "double units = rint(a / quantum); /* in [0, 2048] */",
         "double units = floor(a / quantum); /* in [0, 2048] */"),
@@ -69,14 +87,14 @@ MUTATIONS = {
         "acc += (double)bias[n];",
         "acc += 0.0;"),
     "matmul_weight_transposed": (
-        "double p = (double)x[m * K + k] * (double)W[k * N + n];",
-        "double p = (double)x[m * K + k] * (double)W[n * K + k];"),
+        "double p = (double)xr[k] * (double)W[k * N + n];",
+        "double p = (double)xr[k] * (double)W[n * K + k];"),
     "matmul_fp32_accumulation": (
         "double acc = 0.0, mag = 0.0;",
         "float acc = 0.0f; double mag = 0.0;"),
     "bound_uses_abs_of_sum": (
-        "if (bound) bound[m * N + n] = 1e-5 * mag + 1e-6;",
-        "if (bound) bound[m * N + n] = 1e-5 * fabs(acc) + 1e-6;"),
+        "tb[n] = 1e-5 * mag + 1e-6;",
+        "tb[n] = 1e-5 * fabs(acc) + 1e-6;"),
     "head_scale_over_128": (
         "float s = amax / 127.0f;",
         "float s = amax / 128.0f;"),
