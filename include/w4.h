@@ -197,6 +197,36 @@ int w4h_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                       const uint16_t *Ps, const uint8_t *Pz, int64_t N, const float *bias,
                       float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- fused epilogues on the K-major matmul -------------------------------
+ * Pages "rlx-web" (a SwiGLU MLP) and "zero-tvm" (a fused gate + up + SiLU
+ * kernel, a fused residual add); GPT-2's MLP activation, GELU, in its tanh
+ * form.  With t = x . W_hat + bias as w4_matmul_kmajor computes it:
+ *   W4_ACT_NONE    y[m, n] = t[m, n]                              [M, N]
+ *   W4_ACT_GELU    y[m, n] = gelu(t[m, n]),
+ *                  gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ *   W4_ACT_SWIGLU  y[m, i] = silu(t[m, 2i]) * t[m, 2i+1],  silu(v) = v / (1 + e^-v)
+ *                  (gate and up columns interleaved by the caller; y is [M, N/2])
+ * then y += residual (fp32, same shape as y, 4-byte aligned; may be y itself
+ * for an in-place residual add, no other overlap).  Every output is within
+ * the matmul bound carried through the activation's slope (|gelu'| <= 1.13,
+ * |silu'| <= 1.1) plus a few fp32 roundings of the activation's evaluation.
+ * Workspace: w4_matmul_kmajor_workspace_bytes(M, K, N).  An unknown act is
+ * W4_ERR_BAD_SHAPE.                                                        */
+#define W4_ACT_NONE 0
+#define W4_ACT_GELU 1
+#define W4_ACT_SWIGLU 2
+
+int w4_check_matmul_kmajor_ep_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                   const float *Ps, const uint8_t *Pz, int64_t N,
+                                   const float *bias, const float *residual, int act,
+                                   const float *y, const void *workspace,
+                                   size_t workspace_bytes);
+
+int w4_matmul_kmajor_ep(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                        const float *Ps, const uint8_t *Pz, int64_t N, const float *bias,
+                        const float *residual, int act, float *y, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * int8 tied head (step 3).  E fp32 [K, N] -> Q int8 [K, ldq], hs fp32 [N]:
  * hs[n] = max_k |E[k, n]| / 127 (correctly rounded fp32 division),

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                  "w4_abi_version", "i8_prepack_head", "i8_head_logits_kmajor",
                  "i8_check_head_logits_kmajor_args", "i8_embed_kmajor",
                  "i8_head_logits_rows", "i8_check_head_logits_rows_args",
-                 "i8_head_rows_workspace_bytes",
+                 "i8_head_rows_workspace_bytes", "w4_matmul_kmajor_ep",
+                 "w4_check_matmul_kmajor_ep_args",
                  "w4h_quantize_pack", "w4h_dequantize", "w4h_prepack_kmajor",
                  "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args"):
         assert must in names
@@ -221,3 +222,20 @@ def test_f16_variant_checks():
     assert lib.w4h_dequantize(A, None, A, 32, 64, A, None) == w4.W4_ERR_NULL_PTR
     if NO_GPU:
         assert lib.w4h_quantize_pack(A, 64, 64, A, A, A, None, None) == w4.W4_ERR_DEVICE
+
+
+def test_kmajor_epilogue_checks():
+    chk = w4.library().w4_check_matmul_kmajor_ep_args
+    M, K, N = 1, 768, 2304
+    for act in (0, 1, 2):
+        assert chk(A, M, K, A, A, A, N, A, A, act, A, None, 0) == w4.W4_OK
+    assert chk(A, M, K, A, A, A, N, A, A, 3, A, None, 0) == w4.W4_ERR_BAD_SHAPE
+    assert chk(A, M, K, A, A, A, N, A, A, -1, A, None, 0) == w4.W4_ERR_BAD_SHAPE
+    assert chk(A, M, K, A, A, A, N, A, A + 2, 1, A, None, 0) == w4.W4_ERR_MISALIGNED
+    assert chk(A, M, K, A, A, A, N, None, None, 2, A, None, 0) == w4.W4_OK
+    ws = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072)
+    assert chk(A, 16, 3072, A, A, A, 3072, None, A, 2, A, None, 0) == \
+        (w4.W4_ERR_WORKSPACE if ws else w4.W4_OK)
+    if NO_GPU:
+        assert w4.library().w4_matmul_kmajor_ep(A, M, K, A, A, A, N, A, A, 1, A, None, 0,
+                                                None) == w4.W4_ERR_DEVICE

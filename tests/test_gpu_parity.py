@@ -593,3 +593,75 @@ def test_f16_matmul_kmajor(M, K, N):
     P = w4.w4h_prepack_kmajor(dev(Wq), s_dev, dev(z))
     y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
     assert_bound(y, y_ref, bound, f"f16 kmajor M={M} {K}x{N}")
+
+
+# --------------------------------------------------------------------------
+# fused epilogues (GELU, SwiGLU on interleaved gate/up columns, residual add)
+# --------------------------------------------------------------------------
+EP_CASES = [("none", True), ("gelu", False), ("gelu", True), ("swiglu", False), ("swiglu", True)]
+# (M, K, N): the decode GEMV (M <= 4), its row loop (M > 4 with K % 128 != 0),
+# the matrix cores with one split and with split-K, a ragged N, and K = 2048
+# (one column slot per workgroup: an odd column count is made even for SwiGLU)
+EP_SHAPES = [(1, 768, 2304), (1, 3072, 768), (3, 192, 530), (4, 2048, 768), (1, 2048, 768),
+             (7, 64, 96), (16, 768, 2304), (58, 768, 768), (16, 3072, 3072), (65, 256, 530)]
+
+
+@pytest.mark.parametrize("M,K,N", EP_SHAPES)
+@pytest.mark.parametrize("act,res", EP_CASES)
+def test_kmajor_epilogue(M, K, N, act, res):
+    note(f"epilogue act={act} residual={res} M={M} K={K} N={N} "
+         f"ws={w4.w4_matmul_kmajor_workspace_bytes(M, K, N)}")
+    W = mixed_weights(K, N, cfg=241)
+    x = synth.activations(M, K, cfg=241, slot=M, outliers=True)
+    b = synth.bias(N, cfg=241)
+    nout = N // 2 if act == "swiglu" else N
+    r = synth.activations(M, nout, cfg=242, slot=M) if res else None
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, b, r, act=act)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b), act=act,
+                                 residual=None if r is None else dev(r)))
+    assert y.shape == (M, nout)
+    assert_bound(y, y_ref, bound, f"epilogue {act}{'+res' if res else ''} M={M} {K}x{N}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_kmajor_epilogue_in_place_residual(M):
+    """residual == y: the residual stream updated in place (out-proj / down-proj)."""
+    K, N = 3072, 768
+    W = mixed_weights(K, N, cfg=243)
+    x = synth.activations(M, K, cfg=243, slot=M)
+    r = synth.activations(M, N, cfg=244, slot=M)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, None, r, act="none")
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    h = dev(r)
+    w4.w4_matmul_kmajor(dev(x), *P, act="none", residual=h, out=h)
+    assert_bound(host(h), y_ref, bound, f"in-place residual M={M}")
+
+
+def test_kmajor_epilogue_bias_only_and_plain_path_unchanged():
+    K, N, M = 0, 64, 3
+    b = synth.bias(N, cfg=245)
+    r = synth.activations(M, N // 2, cfg=245)
+    Wq = np.zeros((0, N // 2), np.uint8)
+    s = np.zeros((0, N), np.float32)
+    zp = np.zeros((0, N // 2), np.uint8)
+    x = np.zeros((M, 0), np.float32)
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, zp, b, r, act="swiglu")
+    P = (torch.zeros((N, 0), dtype=torch.uint8, device=DEV),
+         torch.zeros((N, 0), dtype=torch.float32, device=DEV),
+         torch.zeros((N, 0), dtype=torch.uint8, device=DEV))
+    y = host(w4.w4_matmul_kmajor(torch.zeros((M, 0), device=DEV), *P, bias=dev(b),
+                                 act="swiglu", residual=dev(r)))
+    assert_bound(y, y_ref, bound, "K=0 swiglu epilogue")
+    # act "none" without a residual takes the plain entry point: bit-identical
+    K, N, M = 768, 2304, 16
+    W = mixed_weights(K, N, cfg=246)
+    P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
+    x = dev(synth.activations(M, K, cfg=246))
+    bb = dev(synth.bias(N, cfg=246))
+    y0 = host(w4.w4_matmul_kmajor(x, *P, bias=bb))
+    zero = torch.zeros((M, N), device=DEV)
+    y1 = host(w4.w4_matmul_kmajor(x, *P, bias=bb, residual=zero))
+    assert_bits(y1, y0 + 0.0, "epilogue with a zero residual")

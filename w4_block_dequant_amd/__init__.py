@@ -62,6 +62,10 @@ _SIGS = {
     "w4h_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
     "w4h_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "i8_head_rows_workspace_bytes": (_SZ, [_I64, _I64]),
+    "w4_check_matmul_kmajor_ep_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P,
+                                              _P, _SZ]),
+    "w4_matmul_kmajor_ep": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P, _P, _SZ,
+                                   _P]),
     "i8_check_head_logits_rows_args": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _SZ]),
     "i8_head_logits_rows": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
 }
@@ -233,13 +237,19 @@ def w4_matmul_kmajor_workspace_bytes(M: int, K: int, N: int) -> int:
     return _lib.w4_matmul_kmajor_workspace_bytes(M, K, N)
 
 
+ACTS = {"none": 0, "gelu": 1, "swiglu": 2}  # W4_ACT_NONE, W4_ACT_GELU, W4_ACT_SWIGLU
+
+
 def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: torch.Tensor,
                      bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                     workspace: torch.Tensor | None = None):
-    """y fp32 [M, N] = x [M, K] . dequantize(K-major weights) (+ bias).
+                     workspace: torch.Tensor | None = None, act: str = "none",
+                     residual: torch.Tensor | None = None):
+    """y fp32 = act(x [M, K] . dequantize(K-major weights) (+ bias)) (+ residual).
 
     Ps fp32 is the base format; Ps float16 (binary16 scales) the fp16-scale
-    variant (w4h_matmul_kmajor)."""
+    variant (w4h_matmul_kmajor, no epilogue).  act: "none" (y [M, N]), "gelu"
+    (y [M, N]) or "swiglu" (gate/up columns interleaved, y [M, N/2]); an
+    epilogue or a residual goes through w4_matmul_kmajor_ep."""
     _dev(x, torch.float32, "x")
     _dev(Pq, torch.uint8, "Pq")
     f16 = Ps.dtype == torch.float16  # binary16 scales: the fp16-scale variant
@@ -247,12 +257,22 @@ def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: to
     _dev(Pz, torch.uint8, "Pz")
     if bias is not None:
         _dev(bias, torch.float32, "bias")
+    if act not in ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    ep = act != "none" or residual is not None
+    if ep and f16:
+        raise ValueError("the fused epilogue takes fp32 scales")
     M, K = x.shape
     N = Pq.shape[0]
     if Pq.shape != (N, K // 2) or Ps.shape != (N, K // BLOCK):
         raise ValueError("K-major weights do not match x")
+    nout = N // 2 if act == "swiglu" else N
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+        if residual.shape != (M, nout):
+            raise ValueError("residual must be [M, N_out]")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        out = torch.empty((M, nout), dtype=torch.float32, device=x.device)
     else:
         _dev(out, torch.float32, "out")
     need = _lib.w4_matmul_kmajor_workspace_bytes(M, K, N)
@@ -261,6 +281,11 @@ def w4_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pz: to
     else:
         _dev(workspace, torch.uint8, "workspace")
         ws, wsb = workspace, workspace.numel()
+    if ep:
+        _check("w4_matmul_kmajor_ep", _lib.w4_matmul_kmajor_ep(
+            _ptr(x), M, K, _ptr(Pq), _ptr(Ps), _ptr(Pz), N, _ptr(bias), _ptr(residual),
+            ACTS[act], _ptr(out), _ptr(ws), wsb, _stream(x.device)))
+        return out
     fn = "w4h_matmul_kmajor" if f16 else "w4_matmul_kmajor"
     _check(fn, getattr(_lib, fn)(
         _ptr(x), M, K, _ptr(Pq), _ptr(Ps), _ptr(Pz), N, _ptr(bias), _ptr(out),

@@ -203,9 +203,12 @@ size_t w4_matmul_kmajor_workspace_bytes(int64_t M, int64_t K, int64_t N) {
 }
 
 static int check_matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
-                             const void *Ps, const uint8_t *Pz, int64_t N, const float *bias,
-                             const float *y, const void *workspace, size_t workspace_bytes) {
+                                    const void *Ps, const uint8_t *Pz, int64_t N,
+                                    const float *bias, const float *y, const void *workspace,
+                                    size_t workspace_bytes, const float *residual = nullptr,
+                                    int act = W4_ACT_NONE) {
     if (M < 0) return W4_ERR_BAD_SHAPE;
+    if (act != W4_ACT_NONE && act != W4_ACT_GELU && act != W4_ACT_SWIGLU) return W4_ERR_BAD_SHAPE;
     int st = check_w4_shape(K, N);
     if (st) return st;
     if (K % 64 != 0) return W4_ERR_BAD_SHAPE;
@@ -216,27 +219,31 @@ static int check_matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const 
         return W4_ERR_BAD_SHAPE;
     if (!need(x, M * K) || !y) return W4_ERR_NULL_PTR;
     if ((st = check_packed(Pq, Ps, Pz, K, N))) return st;
-    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4)) return W4_ERR_MISALIGNED;
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4) || !aligned(residual, 4))
+        return W4_ERR_MISALIGNED;
     const size_t need_ws = w4::plan_x3(M, K, N).workspace;
     if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return W4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
     return W4_OK;
 }
 
-static int matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const void *Ps,
-                       bool f16, const uint8_t *Pz, int64_t N, const float *bias, float *y,
-                       void *workspace, size_t workspace_bytes, void *stream) {
+static int matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                              const void *Ps, bool f16, const uint8_t *Pz, int64_t N,
+                              const float *bias, float *y, void *workspace,
+                              size_t workspace_bytes, void *stream,
+                              const float *residual = nullptr, int act = W4_ACT_NONE) {
     int st = check_matmul_kmajor_impl(x, M, K, Pq, Ps, Pz, N, bias, y, workspace,
-                                      workspace_bytes);
+                                      workspace_bytes, residual, act);
     if (st) return st;
     if (M == 0 || N == 0) return W4_OK;
     if ((st = device_check())) return st;
     const w4::X3Plan px = w4::plan_x3(M, K, N);
     if (K > 0 && px.kind == w4::X3Plan::kRun)
-        return launched(w4::launch_mm_x3(px, x, M, K, Pq, Ps, f16, Pz, N, bias, y, workspace,
-                                         as_stream(stream)));
-    return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, f16, Pz, N,
-                                           bias, y, as_stream(stream)));
+        return launched(w4::launch_mm_x3(px, x, M, K, Pq, Ps, f16, Pz, N, bias, residual, act, y,
+                                         workspace, as_stream(stream)));
+    return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N, act == W4_ACT_SWIGLU), x, M,
+                                           K, Pq, Ps, f16, Pz, N, bias, residual, act, y,
+                                           as_stream(stream)));
 }
 
 int w4_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
@@ -264,6 +271,23 @@ int w4h_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, c
                       size_t workspace_bytes, void *stream) {
     return matmul_kmajor_impl(x, M, K, Pq, Ps, true, Pz, N, bias, y, workspace, workspace_bytes,
                               stream);
+}
+
+int w4_check_matmul_kmajor_ep_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                   const float *Ps, const uint8_t *Pz, int64_t N,
+                                   const float *bias, const float *residual, int act,
+                                   const float *y, const void *workspace,
+                                   size_t workspace_bytes) {
+    return check_matmul_kmajor_impl(x, M, K, Pq, Ps, Pz, N, bias, y, workspace, workspace_bytes,
+                                    residual, act);
+}
+
+int w4_matmul_kmajor_ep(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                        const float *Ps, const uint8_t *Pz, int64_t N, const float *bias,
+                        const float *residual, int act, float *y, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    return matmul_kmajor_impl(x, M, K, Pq, Ps, false, Pz, N, bias, y, workspace, workspace_bytes,
+                              stream, residual, act);
 }
 
 int i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q, float *hs,

@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "epilogue.h"
 #include "launch.h"
 
 namespace w4 {
@@ -108,11 +109,12 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // below 2^31 bytes).  CHECK clamps columns past N (ragged last workgroup);
 // without it every load is unconditional, so the compiler can start on
 // pass 0 while later passes are still in flight.
-template <int MR, int P, bool CHECK, bool LOOP, bool H>
+template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, int M, int K, const uint8_t *__restrict__ Pq,
     const void *__restrict__ Ps, const uint8_t *__restrict__ Pz, int N,
-    const float *__restrict__ bias, float *__restrict__ y, int G, int NBL) {
+    const float *__restrict__ bias, const float *__restrict__ residual, int act,
+    float *__restrict__ y, int G, int NBL) {
     extern __shared__ float red[];  // [MR][CC][NBL]
     const int L = threadIdx.x;
     const int g = L / NBL, bl = L - g * NBL;
@@ -189,6 +191,15 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                     const float t = __builtin_fmaf(accO[r], 1048576.0f, accE[r] * 16777216.0f);
                     part[r][p] = __builtin_fmaf(s[p], t, part[r][p]);
                 }
+                // Keep each pass's arithmetic here, in load order, so that it
+                // waits only for its own data: the partial sums are read only
+                // by the reduction below, and the compiler would otherwise sink
+                // every pass's FMAs there, behind the last load.  An empty asm
+                // that reads and writes each partial pins them in place; the
+                // scheduling barrier keeps later passes' unpacking out of it.
+#pragma unroll
+                for (int r = 0; r < MR; ++r) asm volatile("" : "+v"(part[r][p]));
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -222,11 +233,49 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         if (parts == 4) v += __shfl_xor(v, 2);
         const int r = o / CC, c = o - r * CC;
         const int n = n0 + c, m = m0 + r;
-        if (q == 0 && n < N && m < M) y[(size_t)m * N + n] = bias ? v + bias[n] : v;
+        if (EP) {  // the fused epilogue, in its own instantiation
+            if (bias && n < N) v += bias[n];
+            if (act == W4_ACT_SWIGLU) {
+                // CC is even, so column pair (c, c + 1), c even, is outputs o
+                // and o + 1: the next group of `parts` lanes, same wave and round
+                const float up = __shfl_down(v, parts);
+                if (q == 0 && (c & 1) == 0 && n < N && m < M)
+                    ep_store_glu(v, up, residual, y, (size_t)m * (N / 2) + n / 2);
+            } else if (q == 0 && n < N && m < M) {
+                ep_store(v, act, residual, y, (size_t)m * N + n);
+            }
+        } else if (q == 0 && n < N && m < M) {
+            y[(size_t)m * N + n] = bias ? v + bias[n] : v;
+        }
     }
 }
 
+// K = 0: every pre-activation value is the bias (or 0); the epilogue alone,
+// one thread per output.
+__global__ __launch_bounds__(256) void k_epilogue_only(const float *__restrict__ bias, int64_t M,
+                                                       int64_t N,
+                                                       const float *__restrict__ residual,
+                                                       int act, float *__restrict__ y) {
+    const int64_t nout = act == W4_ACT_SWIGLU ? N / 2 : N;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * nout) return;
+    const int64_t j = i - (i / nout) * nout;
+    if (act == W4_ACT_SWIGLU)
+        ep_store_glu(bias ? bias[2 * j] : 0.0f, bias ? bias[2 * j + 1] : 0.0f, residual, y, i);
+    else
+        ep_store(bias ? bias[j] : 0.0f, act, residual, y, i);
+}
+
 }  // namespace
+
+hipError_t launch_epilogue_only(const float *bias, int64_t M, int64_t N, const float *residual,
+                                int act, float *y, hipStream_t stream) {
+    const int64_t total = M * (act == W4_ACT_SWIGLU ? N / 2 : N);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_epilogue_only, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, bias, M, N, residual, act, y);
+    return hipGetLastError();
+}
 
 hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16,
                                  const uint8_t *zeros, int64_t K, int64_t N, uint8_t *Pq, void *Ps,
@@ -249,23 +298,32 @@ hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16
 
 hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, int64_t K,
                               const uint8_t *Pq, const void *Ps, bool f16, const uint8_t *Pz,
-                              int64_t N, const float *bias, float *y, hipStream_t stream) {
+                              int64_t N, const float *bias, const float *residual, int act,
+                              float *y, hipStream_t stream) {
     if (p.kind == KmajorPlan::kEmpty) return hipSuccess;
-    if (p.kind == KmajorPlan::kBiasOnly) return launch_bias_fill(bias, M, N, y, stream);
+    if (p.kind == KmajorPlan::kBiasOnly) {
+        if (act == W4_ACT_NONE && !residual) return launch_bias_fill(bias, M, N, y, stream);
+        return launch_epilogue_only(bias, M, N, residual, act, y, stream);
+    }
     const int64_t C = (int64_t)p.groups * p.passes;
     const dim3 grid((unsigned)((N + C - 1) / C), (unsigned)((M + p.rows - 1) / p.rows));
     const size_t shm = (size_t)p.rows * C * p.lanes_per_col * sizeof(float);
     const bool check = (N % C) != 0;
     const bool loop = p.lanes_per_col < K / kBlock;
+    const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
     if (f16)                                                                                    \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true>), grid, dim3(p.threads), shm,    \
-                           stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups,      \
-                           p.lanes_per_col);                                                    \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false>), grid, dim3(p.threads),  \
+                           shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
+                           act, y, p.groups, p.lanes_per_col);                                  \
+    else if (ep)                                                                                \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true>), grid, dim3(p.threads),  \
+                           shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
+                           act, y, p.groups, p.lanes_per_col);                                  \
     else                                                                                        \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false>), grid, dim3(p.threads), shm,   \
-                           stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, p.groups,      \
-                           p.lanes_per_col)
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false>), grid, dim3(p.threads), \
+                           shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
+                           act, y, p.groups, p.lanes_per_col)
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
         if (check) {                                                                            \

@@ -33,7 +33,11 @@ hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16
                                  uint8_t *Pz, hipStream_t stream);
 hipError_t launch_gemv_kmajor(const KmajorPlan &plan, const float *x, int64_t M, int64_t K,
                               const uint8_t *Pq, const void *Ps, bool f16, const uint8_t *Pz,
-                              int64_t N, const float *bias, float *y, hipStream_t stream);
+                              int64_t N, const float *bias, const float *residual, int act,
+                              float *y, hipStream_t stream);
+// The fused epilogue alone (K = 0: the pre-activation values are the bias).
+hipError_t launch_epilogue_only(const float *bias, int64_t M, int64_t N, const float *residual,
+                                int act, float *y, hipStream_t stream);
 
 hipError_t launch_bias_fill(const float *bias, int64_t M, int64_t N, float *y,
                             hipStream_t stream);
@@ -48,7 +52,8 @@ hipError_t launch_embed(const int64_t *tokens, int64_t T, const int8_t *Q, int64
                         hipStream_t stream);
 hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                         const void *Ps, bool f16, const uint8_t *Pz, int64_t N, const float *bias,
-                        float *y, void *workspace, hipStream_t stream);
+                        const float *residual, int act, float *y, void *workspace,
+                        hipStream_t stream);
 hipError_t launch_head_prepack(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *Qt,
                                int64_t ldt, hipStream_t stream);
 hipError_t launch_head_logits_kmajor(const float *x, int64_t K, const int8_t *Qt, int64_t ldt,

@@ -126,7 +126,7 @@ SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N) {
     return p;
 }
 
-KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N) {
+KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     KmajorPlan p{};
     if (N == 0 || M == 0) {
         p.kind = KmajorPlan::kEmpty;
@@ -188,6 +188,8 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N) {
             p.passes = allowed[i];
             found = true;
         }
+    // an odd column count only arises with one column slot and 1 or 3 passes
+    if (even_cols && (p.groups * p.passes) % 2 != 0) p.passes = p.passes == 3 ? 4 : 2;
     return p;
 }
 

@@ -70,7 +70,9 @@ struct KmajorPlan {
     int rows = 1, passes = 1, groups = 1, lanes_per_col = 64, threads = 64;
 };
 
-KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N);
+// even_cols: a workgroup's column count (groups * passes) must be even, so
+// that the SwiGLU epilogue's column pairs stay within one workgroup.
+KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols = false);
 
 // ---- M > 4 rows on the K-major layout: bf16 matrix cores, fp32 accuracy ------
 // Workgroup: 4 waves x nt tiles of 16 columns, all rows of one 64-row group

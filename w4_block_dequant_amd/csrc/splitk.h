@@ -15,8 +15,11 @@ namespace w4 {
 // y[m, n] (row stride N) from `splits` partial planes of `rows` x npad floats;
 // `scale` multiplies the sum before the bias is added (used by the int8 head
 // to apply its fp16-subnormal unit and per-token scale: pass col_scale).
+// `act` and `residual` are the fused epilogue (epilogue.h); with
+// W4_ACT_SWIGLU, y has N / 2 columns.
 hipError_t launch_splitk_reduce(const float *part, int64_t splits, int64_t rows, int64_t N,
                                 int64_t npad, const float *bias, const float *col_scale,
-                                float unit, float *y, hipStream_t stream);
+                                float unit, float *y, hipStream_t stream,
+                                const float *residual = nullptr, int act = W4_ACT_NONE);
 
 }  // namespace w4

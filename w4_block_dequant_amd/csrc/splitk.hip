@@ -1,5 +1,6 @@
 // Second stage of the split-K kernels: a parallel, fixed-order sum of the
 // partial planes (see splitk.h).
+#include "epilogue.h"
 #include "launch.h"
 #include "splitk.h"
 
@@ -16,7 +17,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
                                                        int64_t npad,
                                                        const float *__restrict__ bias,
                                                        const float *__restrict__ col_scale,
-                                                       float unit, float *__restrict__ y) {
+                                                       float unit,
+                                                       const float *__restrict__ residual,
+                                                       int act, float *__restrict__ y) {
     const int n0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
     if (n0 >= N) return;
     const int64_t plane = rows * npad;
@@ -26,15 +29,26 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 #pragma unroll 4
         for (int s = 0; s < splits; ++s)
             v += *reinterpret_cast<const f32x4_t *>(p + s * plane);
-        float *yo = y + m * N;
+        float t[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = n0 + j;
-            if (n >= N) break;
             float r = v[j];
-            if (col_scale) r = (r * unit) * col_scale[n];
-            if (bias) r += bias[n];
-            yo[n] = r;
+            if (n < N) {
+                if (col_scale) r = (r * unit) * col_scale[n];
+                if (bias) r += bias[n];
+            }
+            t[j] = r;
+        }
+        if (act == W4_ACT_SWIGLU) {  // N even: pairs (n0, n0 + 1), (n0 + 2, n0 + 3)
+            const int64_t no = N / 2;
+#pragma unroll
+            for (int j = 0; j < 4; j += 2)
+                if (n0 + j < N) ep_store_glu(t[j], t[j + 1], residual, y, m * no + (n0 + j) / 2);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + j < N) ep_store(t[j], act, residual, y, m * N + n0 + j);
         }
     }
 }
@@ -43,12 +57,13 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 
 hipError_t launch_splitk_reduce(const float *part, int64_t splits, int64_t rows, int64_t N,
                                 int64_t npad, const float *bias, const float *col_scale,
-                                float unit, float *y, hipStream_t stream) {
+                                float unit, float *y, hipStream_t stream, const float *residual,
+                                int act) {
     if (rows == 0 || N == 0) return hipSuccess;
     const int64_t groups = (N + 3) / 4;
     const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
     hipLaunchKernelGGL(k_splitk_reduce, grid, dim3(256), 0, stream, part, (int)splits, rows,
-                       (int)N, npad, bias, col_scale, unit, y);
+                       (int)N, npad, bias, col_scale, unit, residual, act, y);
     return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@
 // processed.  Workgroups along K (split-K) write partial sums that the
 // fixed-order reduce kernel adds (splitk.h), so results are deterministic.
 #include "common.h"
+#include "epilogue.h"
 #include "launch.h"
 #include "splitk.h"
 
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
                                                const void *__restrict__ Ps,
                                                const uint8_t *__restrict__ Pz, int N,
                                                const float *__restrict__ bias,
+                                               const float *__restrict__ residual, int act,
                                                float *__restrict__ y, int npad,
                                                float *__restrict__ part) {
     // A operands of a quad: [buffer][block][m-tile][part][lane]; two buffers
@@ -230,22 +232,29 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
         }
     }
 
-    // lane (g, c) holds D[4 g + v][c] of each (m-tile, column tile)
+    // lane (g, c) holds D[4 g + v][c] of each (m-tile, column tile).  No lane
+    // leaves before the SwiGLU exchange: column pair (c, c + 1), c even, is
+    // lanes (l, l + 1) of the same row group.
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int n = nw + 16 * t + c;
-            if (n >= N) continue;
-            const float bn = (splits == 1 && bias) ? bias[n] : 0.0f;
+            const float bn = (splits == 1 && bias && n < N) ? bias[n] : 0.0f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = m0 + 16 * i + 4 * g + v;
-                if (m >= M) continue;
-                if (splits == 1)
-                    y[(size_t)m * N + n] = acc[i][t][v] + bn;
-                else
-                    part[((size_t)split * M + m) * npad + n] = acc[i][t][v];
+                const bool in = n < N && m < M;
+                if (splits > 1) {
+                    if (in) part[((size_t)split * M + m) * npad + n] = acc[i][t][v];
+                } else if (act == W4_ACT_SWIGLU) {
+                    const float tv = acc[i][t][v] + bn;
+                    const float up = __shfl_down(tv, 1);
+                    if (in && (c & 1) == 0)
+                        ep_store_glu(tv, up, residual, y, (size_t)m * (N / 2) + n / 2);
+                } else if (in) {
+                    ep_store(acc[i][t][v] + bn, act, residual, y, (size_t)m * N + n);
+                }
             }
         }
 }
@@ -254,7 +263,8 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
 
 hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                         const void *Ps, bool f16, const uint8_t *Pz, int64_t N, const float *bias,
-                        float *y, void *workspace, hipStream_t stream) {
+                        const float *residual, int act, float *y, void *workspace,
+                        hipStream_t stream) {
     const dim3 grid((unsigned)p.col_wgs, (unsigned)p.splits, (unsigned)p.mgroups);
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     bool launched = false;
@@ -262,11 +272,12 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
     if (!launched && p.mt == MTV && p.nt == NTV && p.quads_per_wg == QV) {                      \
         if (f16)                                                                                \
             hipLaunchKernelGGL((k_mm_x3<MTV, NTV, QV, DQV, true>), grid, dim3(256), 0, stream, x, \
-                               (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, (int)p.npad, part);  \
+                               (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y,       \
+                               (int)p.npad, part);                                              \
         else                                                                                    \
             hipLaunchKernelGGL((k_mm_x3<MTV, NTV, QV, DQV, false>), grid, dim3(256), 0, stream,   \
-                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, y, (int)p.npad,      \
-                               part);                                                           \
+                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y,    \
+                               (int)p.npad, part);                                              \
         launched = true;                                                                        \
     }
 #define W4_X3_Q(MTV, NTV, DQV)                                                                  \
@@ -280,7 +291,8 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
     if (!launched) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    return launch_splitk_reduce(part, p.splits, M, N, p.npad, bias, nullptr, 1.0f, y, stream);
+    return launch_splitk_reduce(part, p.splits, M, N, p.npad, bias, nullptr, 1.0f, y, stream,
+                                residual, act);
 }
 
 }  // namespace w4
