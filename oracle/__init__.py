@@ -35,6 +35,7 @@ CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-s
 
 OK, BAD_SHAPE, NONFINITE, NO_MEMORY = 0, 1, 2, 3
 BLOCK = 32
+GROUP = 64
 
 
 class OracleError(RuntimeError):
@@ -77,6 +78,10 @@ _SIGS = {
     "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
     "orc_f16_array_to_f32": (None, [_P, _I64, _P]),
     "orc_w4h_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "orc_w4g_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "orc_w4g_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "orc_w4g_prepack_kmajor": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P]),
+    "orc_w4g_matmul": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
     "orc_gelu": (ctypes.c_double, [ctypes.c_double]),
     "orc_silu": (ctypes.c_double, [ctypes.c_double]),
     "orc_w4_matmul_ep": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, ctypes.c_int,
@@ -211,6 +216,48 @@ class Oracle:
                self._l.orc_w4_matmul(_ptr(x), M, K, _ptr(_c(Wq, np.uint8)),
                                      _ptr(_c(scales, np.float32)), _ptr(_c(zeros, np.uint8)),
                                      N, _ptr(b), _ptr(y), _ptr(bound)))
+        return y, bound
+
+    # -- group-64 affine variant ---------------------------------------------------
+    def quantize_pack_g64(self, W):
+        """W fp32 [K, N] -> (Wq uint8 [K, N/2], scales fp32 [K/64, N], mins fp32 [K/64, N])."""
+        W = _c(W, np.float32)
+        K, N = W.shape
+        Wq = np.zeros((K, N // 2), np.uint8)
+        s = np.zeros((K // GROUP, N), np.float32)
+        m = np.zeros((K // GROUP, N), np.float32)
+        _check("orc_w4g_quantize_pack", self._l.orc_w4g_quantize_pack(
+            _ptr(W), K, N, _ptr(Wq), _ptr(s), _ptr(m)))
+        return Wq, s, m
+
+    def dequantize_g64(self, Wq, scales, mins, K, N):
+        out = np.zeros((K, N), np.float32)
+        _check("orc_w4g_dequantize", self._l.orc_w4g_dequantize(
+            _ptr(_c(Wq, np.uint8)), _ptr(_c(scales, np.float32)), _ptr(_c(mins, np.float32)),
+            K, N, _ptr(out)))
+        return out
+
+    def prepack_kmajor_g64(self, Wq, scales, mins, K, N):
+        """-> (Pq uint8 [N, K/2], Ps fp32 [N, K/64], Pm fp32 [N, K/64])."""
+        Pq = np.zeros((N, K // 2), np.uint8)
+        Ps = np.zeros((N, K // GROUP), np.float32)
+        Pm = np.zeros((N, K // GROUP), np.float32)
+        _check("orc_w4g_prepack_kmajor", self._l.orc_w4g_prepack_kmajor(
+            _ptr(_c(Wq, np.uint8)), _ptr(_c(scales, np.float32)), _ptr(_c(mins, np.float32)),
+            K, N, _ptr(Pq), _ptr(Ps), _ptr(Pm)))
+        return Pq, Ps, Pm
+
+    def w4g_matmul(self, x, Wq, scales, mins, bias=None):
+        """y = x . dequantize_g64(W) (+ bias) -> (y [M, N], bound [M, N])."""
+        x = _c(x, np.float32)
+        M, K = x.shape
+        N = _c(scales, np.float32).shape[1]
+        b = None if bias is None else _c(bias, np.float32)
+        y = np.zeros((M, N), np.float32)
+        bound = np.zeros((M, N), np.float64)
+        _check("orc_w4g_matmul", self._l.orc_w4g_matmul(
+            _ptr(x), M, K, _ptr(_c(Wq, np.uint8)), _ptr(_c(scales, np.float32)),
+            _ptr(_c(mins, np.float32)), N, _ptr(b), _ptr(y), _ptr(bound)))
         return y, bound
 
     # -- fused epilogues -----------------------------------------------------------

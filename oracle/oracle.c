@@ -138,29 +138,40 @@ int orc_w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zer
     return ORC_OK;
 }
 
+/* Codes of the [K, N] tensor packed along N -> column-major, packed along K.  */
+static int transpose_codes(const uint8_t *Wq, int64_t K, int64_t N, uint8_t *Pq)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    uint8_t *qt = (uint8_t *)malloc((size_t)(K * N) + 1);
+    if (!q || !qt) { free(q); free(qt); return ORC_NO_MEMORY; }
+    orc_unpack_u4(Wq, K * N, q);
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) qt[n * K + k] = q[k * N + n];
+    orc_pack_u4(qt, K * N, Pq);
+    free(q);
+    free(qt);
+    return ORC_OK;
+}
+
 int orc_w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zeros,
                           int64_t K, int64_t N, uint8_t *Pq, float *Ps, uint8_t *Pz)
 {
     if (bad_w4_shape(K, N) || K % 64 != 0) return ORC_BAD_SHAPE;
     int64_t nb = K / BLOCK;
-    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
     uint8_t *z = (uint8_t *)malloc((size_t)(nb * N) + 1);
-    uint8_t *qt = (uint8_t *)malloc((size_t)(K * N) + 1);
     uint8_t *zt = (uint8_t *)malloc((size_t)(nb * N) + 1);
-    if (!q || !z || !qt || !zt) { free(q); free(z); free(qt); free(zt); return ORC_NO_MEMORY; }
-    orc_w4_unpack(Wq, zeros, K, N, q, z);
-    /* transpose the unpacked codes and zero points to column-major, then pack */
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t n = 0; n < N; ++n) qt[n * K + k] = q[k * N + n];
+    if (!z || !zt) { free(z); free(zt); return ORC_NO_MEMORY; }
+    int st = transpose_codes(Wq, K, N, Pq);
+    /* the zero points and scales go column-major the same way */
+    orc_unpack_u4(zeros, nb * N, z);
     for (int64_t b = 0; b < nb; ++b)
         for (int64_t n = 0; n < N; ++n) {
             zt[n * nb + b] = z[b * N + n];
             Ps[n * nb + b] = scales[b * N + n];
         }
-    orc_pack_u4(qt, K * N, Pq);
     orc_pack_u4(zt, nb * N, Pz);
-    free(q); free(z); free(qt); free(zt);
-    return ORC_OK;
+    free(z); free(zt);
+    return st;
 }
 
 /* Row m of x . W + bias in fp64 (t[n], unrounded) and each output's bound
@@ -411,5 +422,94 @@ int orc_w4_matmul_ep(const float *x, int64_t M, int64_t K,
     free(W_hat);
     free(t);
     free(tb);
+    return st;
+}
+
+/* ---- group-64 affine variant -------------------------------------------- */
+
+static int bad_w4g_shape(int64_t K, int64_t N)
+{
+    return K < 0 || N < 0 || K % ORC_GROUP != 0 || N % 2 != 0;
+}
+
+int orc_w4g_quantize_pack(const float *W, int64_t K, int64_t N,
+                          uint8_t *Wq, float *scales, float *mins)
+{
+    if (bad_w4g_shape(K, N)) return ORC_BAD_SHAPE;
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    if (!q) return ORC_NO_MEMORY;
+    int st = ORC_OK;
+    for (int64_t g = 0; g < K / ORC_GROUP && st == ORC_OK; ++g) {
+        for (int64_t n = 0; n < N && st == ORC_OK; ++n) {
+            const float *w = W + (g * ORC_GROUP) * N + n;
+            float lo = w[0], hi = w[0];
+            for (int r = 0; r < ORC_GROUP; ++r) {
+                float v = w[r * N];
+                if (!isfinite(v)) { st = ORC_NONFINITE; break; }
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            if (st != ORC_OK) break;
+            float range = hi - lo;
+            float sc = range / 15.0f;
+            if (!isfinite(sc)) { st = ORC_NONFINITE; break; }
+            scales[g * N + n] = sc;
+            mins[g * N + n] = lo;
+            for (int r = 0; r < ORC_GROUP; ++r) {
+                int qv = 0;
+                if (sc != 0.0f) {
+                    float d = w[r * N] - lo;
+                    qv = clamp_int(rintf(d / sc), 0, 15);
+                }
+                q[(g * ORC_GROUP + r) * N + n] = (uint8_t)qv;
+            }
+        }
+    }
+    if (st == ORC_OK) orc_pack_u4(q, K * N, Wq);
+    free(q);
+    return st;
+}
+
+int orc_w4g_dequantize(const uint8_t *Wq, const float *scales, const float *mins,
+                       int64_t K, int64_t N, float *W_hat)
+{
+    if (bad_w4g_shape(K, N)) return ORC_BAD_SHAPE;
+    uint8_t *q = (uint8_t *)malloc((size_t)(K * N) + 1);
+    if (!q) return ORC_NO_MEMORY;
+    orc_unpack_u4(Wq, K * N, q);
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t grp = (k / ORC_GROUP) * N + n;
+            /* C99 fmaf: q * s + m with a single rounding */
+            W_hat[k * N + n] = fmaf((float)q[k * N + n], scales[grp], mins[grp]);
+        }
+    free(q);
+    return ORC_OK;
+}
+
+int orc_w4g_prepack_kmajor(const uint8_t *Wq, const float *scales, const float *mins,
+                           int64_t K, int64_t N, uint8_t *Pq, float *Ps, float *Pm)
+{
+    if (bad_w4g_shape(K, N)) return ORC_BAD_SHAPE;
+    int st = transpose_codes(Wq, K, N, Pq);
+    const int64_t ng = K / ORC_GROUP;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < ng; ++g) {
+            Ps[n * ng + g] = scales[g * N + n];
+            Pm[n * ng + g] = mins[g * N + n];
+        }
+    return st;
+}
+
+int orc_w4g_matmul(const float *x, int64_t M, int64_t K,
+                   const uint8_t *Wq, const float *scales, const float *mins, int64_t N,
+                   const float *bias, float *y, double *bound)
+{
+    if (M < 0 || bad_w4g_shape(K, N)) return ORC_BAD_SHAPE;
+    float *W_hat = (float *)malloc((size_t)(K * N) * sizeof(float) + 1);
+    if (!W_hat) return ORC_NO_MEMORY;
+    int st = orc_w4g_dequantize(Wq, scales, mins, K, N, W_hat);
+    if (st == ORC_OK) st = orc_matmul_f64(x, M, K, W_hat, N, bias, y, bound);
+    free(W_hat);
     return st;
 }

@@ -157,6 +157,30 @@ int orc_w4_matmul_ep(const float *x, int64_t M, int64_t K,
                      const float *bias, const float *residual, int act, float *y,
                      double *bound);
 
+/* ---- Group-64 affine variant (zero-tvm README, the kernel A/B table:
+ * "4-bit/group-64/affine"; the int4 matmul family it measures).  The page
+ * names the format only; this is its plainest reading (R18): per group of
+ * 64 consecutive rows k = 64 g .. 64 g + 63 of column n,
+ *   lo = min w, hi = max w, s = fl32(fl32(hi - lo) / 15), m = lo,
+ *   q = clamp(rint(fl32(fl32(w - lo) / s)), 0, 15)   (s == 0: q = 0),
+ *   W_hat = fl32(q * s + m)   (one rounding: fused multiply-add),
+ * so the group's minimum is reproduced exactly and the range is the data's
+ * own (no zero point).  Codes packed like Wq ([K, N/2], pairs along N, low
+ * nibble first); scales and mins fp32 [K/64, N]; 0.625 B/weight.  K % 64 == 0,
+ * N even; a non-finite weight or range is ORC_NONFINITE.                    */
+#define ORC_GROUP 64
+int orc_w4g_quantize_pack(const float *W, int64_t K, int64_t N,
+                          uint8_t *Wq, float *scales, float *mins);
+int orc_w4g_dequantize(const uint8_t *Wq, const float *scales, const float *mins,
+                       int64_t K, int64_t N, float *W_hat);
+/* K-major copy: Pq as orc_w4_prepack_kmajor's, Ps and Pm fp32 [N, K/64].     */
+int orc_w4g_prepack_kmajor(const uint8_t *Wq, const float *scales, const float *mins,
+                           int64_t K, int64_t N, uint8_t *Pq, float *Ps, float *Pm);
+/* dequantize, then orc_matmul_f64 (same bound).                             */
+int orc_w4g_matmul(const float *x, int64_t M, int64_t K,
+                   const uint8_t *Wq, const float *scales, const float *mins, int64_t N,
+                   const float *bias, float *y, double *bound);
+
 #ifdef __cplusplus
 }
 #endif

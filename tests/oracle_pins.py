@@ -22,6 +22,10 @@ different route to the same fact.
     round-trip bound, exact rational logits;
   * embedding lookup: rows of the dequantized table;
   * byte budget: the GPT-2 small q4 file size the page prints;
+  * group-64 affine variant: on-grid groups reproduced exactly, the byte
+    count, brute-force nearest codes in exact rationals, the minimum kept
+    exactly, constant groups, every code through the single-rounding
+    dequantization, exact rational matmuls;
   * fused epilogues: GELU against the exact (erf) GELU within the tanh form's
     known 5e-4 gap, SiLU against its tanh form, the odd-part identity
     f(v) - f(-v) = v of both, and one-hot rows through the epilogue (exact
@@ -689,7 +693,126 @@ def pin_epilogue_matmul(orc):
             None, 0, K, None, None, None, N, None, None, 7, None, None))
 
 
+# --------------------------------------------------------------------------
+# group-64 affine variant
+# --------------------------------------------------------------------------
+GROUP = 64
+
+
+def _on_grid_g64(K, N, seed):
+    """w = q * 2**e + m per group, with m a multiple of 2**e and codes 0 and 15
+    both present, so that s = 2**e and the minimum m are exact."""
+    g = np.random.default_rng(seed)
+    ng = K // GROUP
+    e = g.integers(-10, -3, size=(ng, N))
+    mz = g.integers(-40, 20, size=(ng, N))
+    q = g.integers(0, 16, size=(K, N)).astype(np.uint8)
+    for b in range(ng):
+        for n in range(N):
+            r0, r1 = g.choice(GROUP, size=2, replace=False)
+            q[b * GROUP + r0, n] = 0
+            q[b * GROUP + r1, n] = 15
+    s = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    m = (mz * s).astype(np.float32)
+    W = (q.astype(np.float32) * np.repeat(s, GROUP, axis=0) +
+         np.repeat(m, GROUP, axis=0)).astype(np.float32)
+    return W, q, s, m
+
+
+def pin_g64_on_grid_and_layout(orc):
+    K, N = 192, 6
+    W, q, s, m = _on_grid_g64(K, N, seed=21)
+    Wq, sc, mn = orc.quantize_pack_g64(W)
+    assert np.array_equal(sc, s) and np.array_equal(mn, m)
+    assert np.array_equal(orc.unpack_u4(Wq).reshape(K, N), q)
+    assert np.array_equal(orc.dequantize_g64(Wq, sc, mn, K, N), W)
+    # bytes per weight: 4-bit codes plus two fp32 per 64 weights
+    assert Wq.nbytes + sc.nbytes + mn.nbytes == K * N * 5 // 8
+    # K-major copy: transposed codes packed along K, scales and mins transposed
+    Pq, Ps, Pm = orc.prepack_kmajor_g64(Wq, sc, mn, K, N)
+    assert np.array_equal(orc.unpack_u4(Pq).reshape(N, K), np.ascontiguousarray(q.T))
+    assert np.array_equal(Ps, np.ascontiguousarray(s.T)) and np.array_equal(Pm, np.ascontiguousarray(m.T))
+    for bad in ((32, 4), (64, 3)):
+        with pytest.raises(oracle_mod.OracleError):
+            orc.quantize_pack_g64(np.zeros(bad, np.float32))
+
+
+def pin_g64_nearest_code_and_bounds(orc):
+    g = np.random.default_rng(22)
+    cases = [synth.weights(64, 4, cfg=121),
+             (g.standard_normal((64, 4)) * 0.3 + 0.1).astype(np.float32),
+             np.abs(g.standard_normal((128, 2))).astype(np.float32) + np.float32(5.0)]
+    for W in cases:
+        K, N = W.shape
+        Wq, sc, mn = orc.quantize_pack_g64(W)
+        q = orc.unpack_u4(Wq).reshape(K, N)
+        What = orc.dequantize_g64(Wq, sc, mn, K, N)
+        for b in range(K // GROUP):
+            for n in range(N):
+                col = W[b * GROUP:(b + 1) * GROUP, n]
+                lo, hi = F(col.min()), F(col.max())
+                sn, mm = F(sc[b, n]), F(mn[b, n])
+                assert mm == lo                             # the offset is the minimum
+                assert abs(sn - (hi - lo) / 15) <= F(ulp32(float(sn)))
+                for r in range(GROUP):
+                    k = b * GROUP + r
+                    w = F(W[k, n])
+                    t = (w - mm) / sn
+                    frac = t - (t.numerator // t.denominator)
+                    if abs(frac - Fraction(1, 2)) >= Fraction(1, 2 ** 20):
+                        errs = [abs(w - (qq * sn + mm)) for qq in range(16)]
+                        assert errs[int(q[k, n])] == min(errs), (k, n)
+                    # round trip: half a step plus the roundings of w - lo, of
+                    # the quotient and of W_hat
+                    assert abs(F(What[k, n]) - w) <= sn / 2 + sn * Fraction(1, 2 ** 18) + \
+                        F(ulp32(float(W[k, n])))
+                kmin = b * GROUP + int(np.argmin(col))
+                assert int(q[kmin, n]) == 0 and What[kmin, n] == col.min()
+    # a constant group: s = 0, every code 0, W_hat = the constant exactly
+    Wc = np.full((64, 2), np.float32(-0.3), np.float32)
+    Wc[:, 1] = np.float32(7.25)
+    Wq, sc, mn = orc.quantize_pack_g64(Wc)
+    assert (sc == 0).all() and not orc.unpack_u4(Wq).any()
+    assert np.array_equal(orc.dequantize_g64(Wq, sc, mn, 64, 2), Wc)
+    bad = np.zeros((64, 2), np.float32)
+    bad[3, 1] = np.inf
+    with pytest.raises(oracle_mod.OracleError):
+        orc.quantize_pack_g64(bad)
+
+
+def pin_g64_dequant_and_matmul(orc):
+    # every code with sampled scales and offsets: W_hat = q s + m rounded once
+    ng, N = 4, 16
+    K = ng * GROUP
+    q = np.array([[(k + n) % 16 for n in range(N)] for k in range(K)], np.uint8)
+    g = np.random.default_rng(23)
+    s = (np.abs(g.standard_normal((ng, N))) * 0.01).astype(np.float32)
+    m = (g.standard_normal((ng, N)) * 0.05).astype(np.float32)
+    s[0, :3] = [np.float32(1e-40), np.float32(1.0) / np.float32(3.0), np.float32(2.0 ** 60)]
+    m[0, :3] = [np.float32(0.0), np.float32(-5.0), np.float32(-(2.0 ** 63))]
+    Wq = orc.pack_u4(q.reshape(-1)).reshape(K, N // 2)
+    What = orc.dequantize_g64(Wq, s, m, K, N)
+    for k in range(K):
+        for n in range(N):
+            b = k // GROUP
+            want = f32_round(int(q[k, n]) * F(s[b, n]) + F(m[b, n]))
+            assert What[k, n] == want, (k, n, What[k, n], want)
+    # the matmul is the plain fp64 matmul on W_hat, exact on tiny shapes
+    for M, K, N in ((1, 64, 2), (3, 128, 6)):
+        W = synth.weights(K, N, cfg=124, slot=M)
+        x = synth.activations(M, K, cfg=124, slot=M, outliers=True)
+        b = synth.bias(N, cfg=124, slot=M)
+        Wq, sc, mn = orc.quantize_pack_g64(W)
+        What = orc.dequantize_g64(Wq, sc, mn, K, N)
+        for bias in (None, b):
+            y, bound = orc.w4g_matmul(x, Wq, sc, mn, bias)
+            _exact_check(y, bound, x, What, bias)
+
+
 ALL_PINS = [
+    pin_g64_on_grid_and_layout,
+    pin_g64_nearest_code_and_bounds,
+    pin_g64_dequant_and_matmul,
     pin_activations,
     pin_epilogue_matmul,
     pin_f16_conversion,

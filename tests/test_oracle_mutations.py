@@ -6,7 +6,9 @@ step: nibble order, the block range, rounding, the scale divisor, the code
 formula, the zero point's sign, the dequantization formula and its block
 index, the matmul's bias, indexing and accumulation precision, the bound, the
 head's scale and rounding, and the fused epilogues (GELU's constants, SiLU's
-sign, the SwiGLU pairing, the order of activation and residual).  A mutant
+sign, the SwiGLU pairing, the order of activation and residual) and the
+group-64 affine variant (range, offset, rounding, the single-rounding
+dequantization, its K-major copy).  A mutant
 that passes every pin would mean the pins cannot tell that mistake from the
 correct oracle.
 """
@@ -19,6 +21,21 @@ import oracle
 from oracle_pins import ALL_PINS
 
 MUTATIONS = {
+    "g64_range_includes_zero": (
+        "            float lo = w[0], hi = w[0];",
+        "            float lo = fminf(w[0], 0.0f), hi = fmaxf(w[0], 0.0f);"),
+    "g64_offset_is_max": (
+        "            mins[g * N + n] = lo;",
+        "            mins[g * N + n] = hi;"),
+    "g64_truncates": (
+        "qv = clamp_int(rintf(d / sc), 0, 15);",
+        "qv = clamp_int(truncf(d / sc), 0, 15);"),
+    "g64_dequant_two_roundings": (
+        "W_hat[k * N + n] = fmaf((float)q[k * N + n], scales[grp], mins[grp]);",
+        "W_hat[k * N + n] = (float)q[k * N + n] * scales[grp] + mins[grp];"),
+    "g64_prepack_mins_are_scales": (
+        "            Pm[n * ng + g] = mins[g * N + n];",
+        "            Pm[n * ng + g] = scales[g * N + n];"),
     "gelu_coefficient_typo": (
         "return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));",
         "return 0.5 * v * (1.0 + tanh(c * (v + 0.44715 * v * v * v)));"),
