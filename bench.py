@@ -153,7 +153,7 @@ def main():
         __slots__ = ("layer", "slot", "K", "N", "Wq", "s", "z", "P", "b", "x", "y", "bytes",
                      "flops")
 
-    def build_body(name, cfg, M, with_bias, outliers, f16=False):
+    def build_body(name, cfg, M, with_bias, outliers, f16=False, g64=False):
         shapes = synth.body(name)
         ahead = 16                  # bounded look-ahead: at most 16 fp32 matrices on the host
         futs = {}
@@ -173,6 +173,11 @@ def main():
                 m.P = w4.w4h_prepack_kmajor(Wq, s16, z)
                 m.Wq = m.s = m.z = None
                 del Wq, s16, z
+            elif g64:  # group-64 affine variant: K-major copy only
+                Wq, sg, mg = w4.w4g_quantize_pack(W)
+                m.P = w4.w4g_prepack_kmajor(Wq, sg, mg)
+                m.Wq = m.s = m.z = None
+                del Wq, sg, mg
             else:
                 m.Wq, m.s, m.z = w4.w4_quantize_pack(W)
                 m.P = w4.w4_prepack_kmajor(m.Wq, m.s, m.z) if K % 64 == 0 else None
@@ -180,7 +185,10 @@ def main():
             m.b = torch.from_numpy(synth.bias(N, cfg, l, s)).to(dev) if with_bias else None
             m.x = torch.from_numpy(synth.activations(M, K, cfg, l, s, outliers=outliers)).to(dev)
             m.y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            wbytes = K * N // 2 + (K // 32) * N * (2 if f16 else 4) + (K // 32) * N // 2
+            if g64:  # codes + fp32 scale and minimum per 64 rows
+                wbytes = K * N // 2 + 2 * 4 * (K // 64) * N
+            else:
+                wbytes = K * N // 2 + (K // 32) * N * (2 if f16 else 4) + (K // 32) * N // 2
             m.bytes = wbytes + 4 * M * K + 4 * M * N + (4 * N if with_bias else 0)
             m.flops = 2 * M * K * N
             mats.append(m)
@@ -342,6 +350,32 @@ def main():
     # ------------------------------------------------------------- secondary
     secondary = {}
     if not args.skip_secondary:
+        # The same M=1 pass with the fused epilogues of a decode layer: SwiGLU
+        # on the gate+up matmul (columns read as interleaved gate/up pairs,
+        # 8192 outputs), the residual add on the out- and down-projections
+        # (in place on one residual-stream row); QKV plain.
+        resid = torch.zeros((1, synth.DENSE38_SHAPES[1][1]), device=dev)
+        glu = torch.empty((1, synth.DENSE38_SHAPES[2][1] // 2), device=dev)
+
+        def run_pass_ep(mats):
+            for m in mats:
+                if m.slot == 2:
+                    w4.w4_matmul_kmajor(m.x, *m.P, act="swiglu", out=glu)
+                elif m.slot in (1, 3):
+                    w4.w4_matmul_kmajor(m.x, *m.P, residual=resid, out=resid)
+                else:
+                    w4.w4_matmul_kmajor(m.x, *m.P, bias=m.b, out=m.y)
+
+        gep = capture(lambda: run_pass_ep(dense))
+        msep, _ = time_graph(gep, max(5, args.steps // 2), 2)
+        del gep
+        secondary["dense38_m1_pass_fused_epilogues"] = {
+            "ms": round(msep, 4), "tokens_per_s": round(1e3 / msep, 1),
+            "vs_plain_pass": round(msep / ms, 4),
+            "note": "SwiGLU fused into gate+up, residual add fused into out- and "
+                    "down-projections; same weight bytes"}
+        log(f"fused-epilogue pass: {secondary['dense38_m1_pass_fused_epilogues']}")
+
         # 3.8B body at M = 16 (batched decode), same weights
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
         fl16 = sum(m.flops for m in d16)
@@ -371,6 +405,22 @@ def main():
             "algorithmic_bytes_per_step": hbytes}
         del gh
         dh.clear()
+        torch.cuda.empty_cache()
+
+        # the group-64 affine variant of the same body (0.625 B/weight), M = 1
+        log("building the group-64 affine body ...")
+        dg = build_body("dense38", synth.CFG_DENSE38, 1, with_bias=False, outliers=False,
+                        g64=True)
+        gg64 = capture(lambda: [w4.w4g_matmul_kmajor(m.x, *m.P, out=m.y) for m in dg])
+        msg64, _ = time_graph(gg64, max(5, args.steps // 2), 2)
+        del gg64
+        g64_bytes = sum(m.bytes for m in dg)
+        secondary["dense38_m1_pass_group64_affine"] = {
+            "ms": round(msg64, 4), "tokens_per_s": round(1e3 / msg64, 1),
+            "GB_s": round(g64_bytes / (msg64 * 1e-3) / 1e9, 1),
+            "algorithmic_bytes_per_step": g64_bytes}
+        log(f"group-64 affine pass: {secondary['dense38_m1_pass_group64_affine']}")
+        dg.clear()
         torch.cuda.empty_cache()
 
         gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)

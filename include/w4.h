@@ -197,6 +197,41 @@ int w4h_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                       const uint16_t *Ps, const uint8_t *Pz, int64_t N, const float *bias,
                       float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- group-64 affine variant ---------------------------------------------
+ * The format of zero-tvm's kernel A/B ("4-bit/group-64/affine"; zero-tvm
+ * README, the A/B table against LM Studio).  The page names it only; the
+ * reading taken: per group of 64 consecutive rows k of column n,
+ *   lo = min w, hi = max w, s = (hi - lo) / 15, m = lo        (fp32),
+ *   q = clamp(rint((w - lo) / s), 0, 15)  (s = 0: q = 0),
+ *   W_hat = fma(q, s, m)                                      (one rounding),
+ * so the group minimum is exact and no zero point is stored.
+ *   Wq      uint8 [K, N/2]   as in the base format (pairs along N, low first)
+ *   scales  fp32  [K/64, N]
+ *   mins    fp32  [K/64, N]
+ * 0.625 B/weight.  K % 64 == 0, N even; arrays 16-byte aligned.  Quantize,
+ * dequantize and the K-major copy are bit-exact; a non-finite weight or range
+ * sets *d_status = W4_ERR_NONFINITE (as w4_quantize_pack).                 */
+int w4g_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, float *scales,
+                      float *mins, int *d_status, void *stream);
+
+int w4g_dequantize(const uint8_t *Wq, const float *scales, const float *mins, int64_t K,
+                   int64_t N, float *W_hat, void *stream);
+
+/* K-major copy: Pq uint8 [N, K/2] (as w4_prepack_kmajor), Ps and Pm fp32
+ * [N, K/64] (scales and minima transposed).                                */
+int w4g_prepack_kmajor(const uint8_t *Wq, const float *scales, const float *mins, int64_t K,
+                       int64_t N, uint8_t *Pq, float *Ps, float *Pm, void *stream);
+
+/* y [M, N] = x [M, K] . W_hat (+ bias), on the K-major copy; every output
+ * within the bound of w4_matmul.  The decode GEMV for every M (rows four at a
+ * time; M <= 262140); no workspace, one launch.                            */
+int w4g_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                 const float *Ps, const float *Pm, int64_t N, const float *bias,
+                                 const float *y);
+
+int w4g_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
+                      const float *Pm, int64_t N, const float *bias, float *y, void *stream);
+
 /* ---- fused epilogues on the K-major matmul -------------------------------
  * Pages "rlx-web" (a SwiGLU MLP) and "zero-tvm" (a fused gate + up + SiLU
  * kernel, a fused residual add); GPT-2's MLP activation, GELU, in its tanh

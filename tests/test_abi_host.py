@@ -37,6 +37,8 @@ def test_header_declares_the_entry_points():
                  "i8_check_head_logits_kmajor_args", "i8_embed_kmajor",
                  "i8_head_logits_rows", "i8_check_head_logits_rows_args",
                  "i8_head_rows_workspace_bytes", "w4_matmul_kmajor_ep",
+                 "w4g_quantize_pack", "w4g_dequantize", "w4g_prepack_kmajor",
+                 "w4g_check_matmul_kmajor_args", "w4g_matmul_kmajor",
                  "w4_check_matmul_kmajor_ep_args",
                  "w4h_quantize_pack", "w4h_dequantize", "w4h_prepack_kmajor",
                  "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args"):
@@ -239,3 +241,20 @@ def test_kmajor_epilogue_checks():
     if NO_GPU:
         assert w4.library().w4_matmul_kmajor_ep(A, M, K, A, A, A, N, A, A, 1, A, None, 0,
                                                 None) == w4.W4_ERR_DEVICE
+
+
+def test_g64_checks():
+    lib = w4.library()
+    chk = lib.w4g_check_matmul_kmajor_args
+    assert chk(A, 1, 3072, A, A, A, 9216, None, A) == w4.W4_OK
+    assert chk(A, 1, 3072 + 32, A, A, A, 9216, None, A) == w4.W4_ERR_BAD_SHAPE   # K % 64
+    assert chk(A, 1, 3072, A, A, A, 9215, None, A) == w4.W4_ERR_BAD_SHAPE       # N odd
+    assert chk(A, 4 * 65536, 64, A, A, A, 8, None, A) == w4.W4_ERR_BAD_SHAPE    # grid rows
+    assert chk(A, 1, 3072, A, A + 8, A, 9216, None, A) == w4.W4_ERR_MISALIGNED
+    assert chk(A, 1, 3072, A, A, None, 9216, None, A) == w4.W4_ERR_NULL_PTR
+    assert chk(None, 0, 3072, None, None, None, 9216, None, None) == w4.W4_OK
+    if NO_GPU:
+        assert lib.w4g_quantize_pack(A, 64, 8, A, A, A, None, None) == w4.W4_ERR_DEVICE
+        assert lib.w4g_matmul_kmajor(A, 1, 64, A, A, A, 8, None, A, None) == w4.W4_ERR_DEVICE
+    assert lib.w4g_quantize_pack(A, 96, 8, A, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4g_dequantize(A, A, A, 64, 8, A + 4, None) == w4.W4_ERR_MISALIGNED

@@ -665,3 +665,82 @@ def test_kmajor_epilogue_bias_only_and_plain_path_unchanged():
     zero = torch.zeros((M, N), device=DEV)
     y1 = host(w4.w4_matmul_kmajor(x, *P, bias=bb, residual=zero))
     assert_bits(y1, y0 + 0.0, "epilogue with a zero residual")
+
+
+# --------------------------------------------------------------------------
+# group-64 affine variant
+# --------------------------------------------------------------------------
+G64_SHAPES = [(64, 2), (128, 34), (192, 530), (768, 2304), (3072, 768), (8192, 512)]
+
+
+@pytest.mark.parametrize("K,N", G64_SHAPES)
+def test_g64_quantize_dequantize_prepack_bit_exact(K, N):
+    note(f"g64 quantize/dequantize/prepack K={K} N={N}")
+    W = mixed_weights(K, N, cfg=251)
+    Wq_r, s_r, m_r = ORC.quantize_pack_g64(W)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Wq, s, m = w4.w4g_quantize_pack(dev(W), d_status=st)
+    assert int(host(st)[0]) == 0
+    assert_bits(host(Wq), Wq_r, f"g64 Wq {K}x{N}")
+    assert_bits(host(s), s_r, f"g64 scales {K}x{N}")
+    assert_bits(host(m), m_r, f"g64 mins {K}x{N}")
+    assert_bits(host(w4.w4g_dequantize(Wq, s, m)), ORC.dequantize_g64(Wq_r, s_r, m_r, K, N),
+                f"g64 W_hat {K}x{N}")
+    for name, a, b in zip(("Pq", "Ps", "Pm"), w4.w4g_prepack_kmajor(Wq, s, m),
+                          ORC.prepack_kmajor_g64(Wq_r, s_r, m_r, K, N)):
+        assert_bits(host(a), b, f"g64 {name} {K}x{N}")
+
+
+def test_g64_nonfinite_sets_status():
+    W = synth.weights(128, 8, cfg=252)
+    W[70, 3] = np.nan
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    w4.w4g_quantize_pack(dev(W), d_status=st)
+    assert int(host(st)[0]) == w4.W4_ERR_NONFINITE
+
+
+@pytest.mark.parametrize("K,N", [(64, 16), (768, 2304), (3072, 768), (192, 530), (8192, 512),
+                                 (1024, 1008)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 58])
+def test_g64_matmul_kmajor(M, K, N):
+    note(f"g64 matmul M={M} K={K} N={N}")
+    W = mixed_weights(K, N, cfg=253)
+    x = synth.activations(M, K, cfg=253, slot=M, outliers=True)
+    b = synth.bias(N, cfg=253)
+    Wq, s, m = ORC.quantize_pack_g64(W)
+    y_ref, bound = ORC.w4g_matmul(x, Wq, s, m, b)
+    P = w4.w4g_prepack_kmajor(dev(Wq), dev(s), dev(m))
+    y = host(w4.w4g_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y, y_ref, bound, f"g64 M={M} {K}x{N}")
+
+
+@pytest.mark.parametrize("slot", range(4))
+def test_g64_dense38_full_size_sampled(slot):
+    K, N = synth.DENSE38_SHAPES[slot]
+    note(f"g64 dense38 slot {slot} K={K} N={N} (sampled columns)")
+    W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=0, slot=slot)
+    x = synth.activations(1, K, cfg=synth.CFG_DENSE38, layer=0, slot=slot, outliers=True)
+    P = w4.w4g_prepack_kmajor(*w4.w4g_quantize_pack(dev(W)))
+    y = host(w4.w4g_matmul_kmajor(dev(x), *P))
+    pairs = sample_pairs(N, 48, seed=20 + slot)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    Wq, s, m = ORC.quantize_pack_g64(W[:, cols])
+    y_ref, bound = ORC.w4g_matmul(x, Wq, s, m)
+    assert_bound(y[:, cols], y_ref, bound, f"g64 dense38 {K}x{N}")
+
+
+def test_g64_special_inputs():
+    K, N, M = 768, 2304, 4
+    W = mixed_weights(K, N, cfg=254)
+    Wq, s, m = ORC.quantize_pack_g64(W)
+    P = w4.w4g_prepack_kmajor(dev(Wq), dev(s), dev(m))
+    base = synth.activations(M, K, cfg=254)
+    cases = {"zeros": np.zeros((M, K), np.float32),
+             "one-hot rows": np.eye(M, K, 7, dtype=np.float32),
+             "tiny": base * np.float32(1e-30),
+             "huge": base * np.float32(1e30),
+             "spread": base * np.where(np.arange(K) % 3 == 0, 1e3, 1e-3).astype(np.float32)}
+    for name, x in cases.items():
+        y_ref, bound = ORC.w4g_matmul(x, Wq, s, m)
+        y = host(w4.w4g_matmul_kmajor(dev(x), *P))
+        assert_bound(y, y_ref, bound, f"g64 x={name}")

@@ -62,6 +62,11 @@ _SIGS = {
     "w4h_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
     "w4h_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "i8_head_rows_workspace_bytes": (_SZ, [_I64, _I64]),
+    "w4g_quantize_pack": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "w4g_dequantize": (_INT, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "w4g_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "w4g_check_matmul_kmajor_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "w4g_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
     "w4_check_matmul_kmajor_ep_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P,
                                               _P, _SZ]),
     "w4_matmul_kmajor_ep": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P, _P, _SZ,
@@ -464,3 +469,71 @@ def w4h_prepack_kmajor(Wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tens
         _ptr(Wq), _ptr(scales), _ptr(zeros), K, N, _ptr(Pq), _ptr(Ps), _ptr(Pz),
         _stream(Wq.device)))
     return Pq, Ps, Pz
+
+
+# -- group-64 affine variant: fp32 scales and minima per 64 rows ----------------
+GROUP = 64
+
+
+def w4g_quantize_pack(W: torch.Tensor, d_status: torch.Tensor | None = None):
+    """W fp32 [K, N] -> (Wq uint8 [K, N/2], scales fp32 [K/64, N], mins fp32 [K/64, N])."""
+    _dev(W, torch.float32, "W")
+    K, N = W.shape
+    Wq = torch.empty((K, N // 2), dtype=torch.uint8, device=W.device)
+    s = torch.empty((K // GROUP, N), dtype=torch.float32, device=W.device)
+    m = torch.empty((K // GROUP, N), dtype=torch.float32, device=W.device)
+    if d_status is not None:
+        _dev(d_status, torch.int32, "d_status")
+    _check("w4g_quantize_pack", _lib.w4g_quantize_pack(_ptr(W), K, N, _ptr(Wq), _ptr(s), _ptr(m),
+                                                       _ptr(d_status), _stream(W.device)))
+    return Wq, s, m
+
+
+def w4g_dequantize(Wq: torch.Tensor, scales: torch.Tensor, mins: torch.Tensor):
+    """-> W_hat fp32 [K, N] = q * s + m (one rounding)."""
+    _dev(Wq, torch.uint8, "Wq")
+    _dev(scales, torch.float32, "scales")
+    _dev(mins, torch.float32, "mins")
+    K, N = Wq.shape[0], scales.shape[1]
+    out = torch.empty((K, N), dtype=torch.float32, device=Wq.device)
+    _check("w4g_dequantize", _lib.w4g_dequantize(_ptr(Wq), _ptr(scales), _ptr(mins), K, N,
+                                                 _ptr(out), _stream(Wq.device)))
+    return out
+
+
+def w4g_prepack_kmajor(Wq: torch.Tensor, scales: torch.Tensor, mins: torch.Tensor):
+    """-> (Pq uint8 [N, K/2], Ps fp32 [N, K/64], Pm fp32 [N, K/64])."""
+    _dev(Wq, torch.uint8, "Wq")
+    _dev(scales, torch.float32, "scales")
+    _dev(mins, torch.float32, "mins")
+    K, N = Wq.shape[0], scales.shape[1]
+    Pq = torch.empty((N, K // 2), dtype=torch.uint8, device=Wq.device)
+    Ps = torch.empty((N, K // GROUP), dtype=torch.float32, device=Wq.device)
+    Pm = torch.empty((N, K // GROUP), dtype=torch.float32, device=Wq.device)
+    _check("w4g_prepack_kmajor", _lib.w4g_prepack_kmajor(
+        _ptr(Wq), _ptr(scales), _ptr(mins), K, N, _ptr(Pq), _ptr(Ps), _ptr(Pm),
+        _stream(Wq.device)))
+    return Pq, Ps, Pm
+
+
+def w4g_matmul_kmajor(x: torch.Tensor, Pq: torch.Tensor, Ps: torch.Tensor, Pm: torch.Tensor,
+                      bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """y fp32 [M, N] = x [M, K] . W_hat (+ bias) on the group-64 affine K-major copy."""
+    _dev(x, torch.float32, "x")
+    _dev(Pq, torch.uint8, "Pq")
+    _dev(Ps, torch.float32, "Ps")
+    _dev(Pm, torch.float32, "Pm")
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+    M, K = x.shape
+    N = Pq.shape[0]
+    if Pq.shape != (N, K // 2) or Ps.shape != (N, K // GROUP) or Pm.shape != Ps.shape:
+        raise ValueError("K-major weights do not match x")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, torch.float32, "out")
+    _check("w4g_matmul_kmajor", _lib.w4g_matmul_kmajor(
+        _ptr(x), M, K, _ptr(Pq), _ptr(Ps), _ptr(Pm), N, _ptr(bias), _ptr(out),
+        _stream(x.device)))
+    return out

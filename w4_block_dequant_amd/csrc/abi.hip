@@ -221,6 +221,9 @@ static int check_matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const 
     if ((st = check_packed(Pq, Ps, Pz, K, N))) return st;
     if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4) || !aligned(residual, 4))
         return W4_ERR_MISALIGNED;
+    // off the matrix cores the GEMV takes rows in groups of 4 on the grid's y axis
+    if (w4::plan_x3(M, K, N).kind != w4::X3Plan::kRun && (M + 3) / 4 > 65535)
+        return W4_ERR_BAD_SHAPE;
     const size_t need_ws = w4::plan_x3(M, K, N).workspace;
     if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return W4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
@@ -288,6 +291,82 @@ int w4_matmul_kmajor_ep(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                         size_t workspace_bytes, void *stream) {
     return matmul_kmajor_impl(x, M, K, Pq, Ps, false, Pz, N, bias, y, workspace, workspace_bytes,
                               stream, residual, act);
+}
+
+// ---- group-64 affine variant ------------------------------------------------
+static int check_g64_shape(int64_t K, int64_t N) {
+    if (K < 0 || N < 0 || K % 64 != 0 || N % 2 != 0) return W4_ERR_BAD_SHAPE;
+    if (K > kMaxElems / (N > 0 ? N : 1)) return W4_ERR_BAD_SHAPE;
+    return W4_OK;
+}
+
+static int check_g64_packed(const uint8_t *Wq, const float *scales, const float *mins, int64_t K,
+                            int64_t N) {
+    if (!need(Wq, K * N) || !need(scales, K * N) || !need(mins, K * N)) return W4_ERR_NULL_PTR;
+    if (!aligned(Wq, 16) || !aligned(scales, 16) || !aligned(mins, 16)) return W4_ERR_MISALIGNED;
+    return W4_OK;
+}
+
+int w4g_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq, float *scales,
+                      float *mins, int *d_status, void *stream) {
+    int st = check_g64_shape(K, N);
+    if (st) return st;
+    if (!need(W, K * N)) return W4_ERR_NULL_PTR;
+    if ((st = check_g64_packed(Wq, scales, mins, K, N))) return st;
+    if (!aligned(W, 16) || !aligned(d_status, 4)) return W4_ERR_MISALIGNED;
+    if ((st = device_check())) return st;
+    return launched(
+        w4::launch_g64_quantize_pack(W, K, N, Wq, scales, mins, d_status, as_stream(stream)));
+}
+
+int w4g_dequantize(const uint8_t *Wq, const float *scales, const float *mins, int64_t K,
+                   int64_t N, float *W_hat, void *stream) {
+    int st = check_g64_shape(K, N);
+    if (st) return st;
+    if ((st = check_g64_packed(Wq, scales, mins, K, N))) return st;
+    if (!need(W_hat, K * N)) return W4_ERR_NULL_PTR;
+    if (!aligned(W_hat, 8)) return W4_ERR_MISALIGNED;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_g64_dequantize(Wq, scales, mins, K, N, W_hat, as_stream(stream)));
+}
+
+int w4g_prepack_kmajor(const uint8_t *Wq, const float *scales, const float *mins, int64_t K,
+                       int64_t N, uint8_t *Pq, float *Ps, float *Pm, void *stream) {
+    int st = check_g64_shape(K, N);
+    if (st) return st;
+    if ((st = check_g64_packed(Wq, scales, mins, K, N))) return st;
+    if ((st = check_g64_packed(Pq, Ps, Pm, K, N))) return st;
+    if ((st = device_check())) return st;
+    return launched(
+        w4::launch_prepack_g64(Wq, scales, mins, K, N, Pq, Ps, Pm, as_stream(stream)));
+}
+
+int w4g_check_matmul_kmajor_args(const float *x, int64_t M, int64_t K, const uint8_t *Pq,
+                                 const float *Ps, const float *Pm, int64_t N, const float *bias,
+                                 const float *y) {
+    if (M < 0) return W4_ERR_BAD_SHAPE;
+    int st = check_g64_shape(K, N);
+    if (st) return st;
+    if (M > kMaxElems / (K > 0 ? K : 1) || M > kMaxElems / (N > 0 ? N : 1)) return W4_ERR_BAD_SHAPE;
+    if (M == 0 || N == 0) return W4_OK;
+    if (K * N >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) || M * N >= ((int64_t)1 << 31))
+        return W4_ERR_BAD_SHAPE;
+    if ((M + 3) / 4 > 65535) return W4_ERR_BAD_SHAPE;
+    if (!need(x, M * K) || !y) return W4_ERR_NULL_PTR;
+    if ((st = check_g64_packed(Pq, Ps, Pm, K, N))) return st;
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4)) return W4_ERR_MISALIGNED;
+    return W4_OK;
+}
+
+int w4g_matmul_kmajor(const float *x, int64_t M, int64_t K, const uint8_t *Pq, const float *Ps,
+                      const float *Pm, int64_t N, const float *bias, float *y, void *stream) {
+    int st = w4g_check_matmul_kmajor_args(x, M, K, Pq, Ps, Pm, N, bias, y);
+    if (st) return st;
+    if (M == 0 || N == 0) return W4_OK;
+    if ((st = device_check())) return st;
+    return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N), x, M, K, Pq, Ps, false, Pm,
+                                           N, bias, nullptr, W4_ACT_NONE, y, as_stream(stream),
+                                           true));
 }
 
 int i8_quantize_head(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q, float *hs,

@@ -109,10 +109,14 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // below 2^31 bytes).  CHECK clamps columns past N (ragged last workgroup);
 // without it every load is unconditional, so the compiler can start on
 // pass 0 while later passes are still in flight.
-template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP>
+// AFF: the group-64 affine variant, Ps = scales and Pz = minima, fp32
+// [N, K/64]: a lane's block is half a group, and its sum is
+// s * sum_k x q + m * sum_k x, with sum_k x formed once per lane and reused
+// by every pass (the codes enter as the same fp16 subnormals, unshifted).
+template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP, bool AFF = false>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, int M, int K, const uint8_t *__restrict__ Pq,
-    const void *__restrict__ Ps, const uint8_t *__restrict__ Pz, int N,
+    const void *__restrict__ Ps, const void *__restrict__ Pz, int N,
     const float *__restrict__ bias, const float *__restrict__ residual, int act,
     float *__restrict__ y, int G, int NBL) {
     extern __shared__ float red[];  // [MR][CC][NBL]
@@ -147,15 +151,18 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                     xr[r][4 * i + 3] = v.w;
                 }
             }
-            // codes, scale and zero point of this block, for each pass's column
+            // codes, scale and zero point (or minimum) of this block, for each
+            // pass's column
             u32x4_t w[P];
-            float s[P];
+            float s[P], mn[P];
             uint32_t zb[P];
             const int nf = n0 + g;  // this lane's column in pass 0
+            const int NS = AFF ? NB / 2 : NB;  // scales per column
+            const int bs = AFF ? (b >> 1) : b;
             uint32_t oq = (uint32_t)(nf * hk + 16 * b);
-            uint32_t os = (uint32_t)(nf * NB + b);
+            uint32_t os = (uint32_t)(nf * NS + bs);
             uint32_t oz = (uint32_t)(nf * (NB / 2) + (b >> 1));
-            const uint32_t sq = (uint32_t)(G * hk), ss = (uint32_t)(G * NB),
+            const uint32_t sq = (uint32_t)(G * hk), ss = (uint32_t)(G * NS),
                            sz = (uint32_t)(G * (NB / 2));
 #pragma unroll
             for (int p = 0; p < P; ++p) {
@@ -163,22 +170,37 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                 if (CHECK && n0 + p * G + g >= N) {  // past the last column: re-read it
                     const int nl = N - 1;
                     q_off = (uint32_t)(nl * hk + 16 * b);
-                    s_off = (uint32_t)(nl * NB + b);
+                    s_off = (uint32_t)(nl * NS + bs);
                     z_off = (uint32_t)(nl * (NB / 2) + (b >> 1));
                 }
                 w[p] = load_stream<u32x4_t>(Pq + q_off);
                 s[p] = H ? f16_bits_to_f32(static_cast<const uint16_t *>(Ps)[s_off])
                          : static_cast<const float *>(Ps)[s_off];
-                zb[p] = Pz[z_off];
+                if (AFF) {
+                    mn[p] = static_cast<const float *>(Pz)[s_off];
+                    zb[p] = 0;
+                } else {
+                    mn[p] = 0.0f;
+                    zb[p] = static_cast<const uint8_t *>(Pz)[z_off];
+                }
                 oq += sq;
                 os += ss;
                 oz += sz;
             }
             __builtin_amdgcn_sched_barrier(0);  // every load in flight before the arithmetic
+            float xs[MR];  // AFF: sum of the block's activations, per row
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                xs[r] = 0.0f;
+                if (AFF) {
+#pragma unroll
+                    for (int k = 0; k < kBlock; ++k) xs[r] += xr[r][k];
+                }
+            }
             const int zsh = (b & 1) * 4;
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                const uint32_t z = (zb[p] >> zsh) & 15;
+                const uint32_t z = AFF ? 0u : (zb[p] >> zsh) & 15;  // AFF: codes as they are
                 const half2_t zE = as_half2(z * 0x00010001u);
                 const half2_t zO = as_half2((z << 4) * 0x00010001u);
                 float accE[MR], accO[MR];
@@ -189,7 +211,10 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
 #pragma unroll
                 for (int r = 0; r < MR; ++r) {
                     const float t = __builtin_fmaf(accO[r], 1048576.0f, accE[r] * 16777216.0f);
-                    part[r][p] = __builtin_fmaf(s[p], t, part[r][p]);
+                    if (AFF)
+                        part[r][p] = __builtin_fmaf(s[p], t, __builtin_fmaf(mn[p], xs[r], part[r][p]));
+                    else
+                        part[r][p] = __builtin_fmaf(s[p], t, part[r][p]);
                 }
                 // Keep each pass's arithmetic here, in load order, so that it
                 // waits only for its own data: the partial sums are read only
@@ -266,7 +291,34 @@ __global__ __launch_bounds__(256) void k_epilogue_only(const float *__restrict__
         ep_store(bias ? bias[j] : 0.0f, act, residual, y, i);
 }
 
+// Group-64 affine variant: scales and minima [K/64, N] -> [N, K/64], one
+// thread per (column n, group c); consecutive threads take consecutive c.
+__global__ __launch_bounds__(256) void k_prepack_g64(const float *__restrict__ scales,
+                                                     const float *__restrict__ mins, int64_t K,
+                                                     int64_t N, float *__restrict__ Ps,
+                                                     float *__restrict__ Pm) {
+    const int64_t NG = K / 64;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= NG * N) return;
+    const int64_t n = t / NG, c = t - n * NG;
+    Ps[t] = scales[c * N + n];
+    Pm[t] = mins[c * N + n];
+}
+
 }  // namespace
+
+hipError_t launch_prepack_g64(const uint8_t *Wq, const float *scales, const float *mins,
+                              int64_t K, int64_t N, uint8_t *Pq, float *Ps, float *Pm,
+                              hipStream_t stream) {
+    const int64_t t1 = (K / 2) * (N / 2), t2 = (K / 64) * N;
+    if (t1 > 0)
+        hipLaunchKernelGGL(k_prepack_codes, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
+                           Wq, K, N, Pq);
+    if (t2 > 0)
+        hipLaunchKernelGGL(k_prepack_g64, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, stream,
+                           scales, mins, K, N, Ps, Pm);
+    return hipGetLastError();
+}
 
 hipError_t launch_epilogue_only(const float *bias, int64_t M, int64_t N, const float *residual,
                                 int act, float *y, hipStream_t stream) {
@@ -297,9 +349,9 @@ hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16
 }
 
 hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, int64_t K,
-                              const uint8_t *Pq, const void *Ps, bool f16, const uint8_t *Pz,
+                              const uint8_t *Pq, const void *Ps, bool f16, const void *Pz,
                               int64_t N, const float *bias, const float *residual, int act,
-                              float *y, hipStream_t stream) {
+                              float *y, hipStream_t stream, bool affine) {
     if (p.kind == KmajorPlan::kEmpty) return hipSuccess;
     if (p.kind == KmajorPlan::kBiasOnly) {
         if (act == W4_ACT_NONE && !residual) return launch_bias_fill(bias, M, N, y, stream);
@@ -312,7 +364,11 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const bool loop = p.lanes_per_col < K / kBlock;
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
-    if (f16)                                                                                    \
+    if (affine)                                                                                 \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true>), grid,            \
+                           dim3(p.threads), shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N,    \
+                           bias, residual, act, y, p.groups, p.lanes_per_col);                  \
+    else if (f16)                                                                               \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false>), grid, dim3(p.threads),  \
                            shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
                            act, y, p.groups, p.lanes_per_col);                                  \

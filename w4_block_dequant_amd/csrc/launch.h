@@ -32,9 +32,17 @@ hipError_t launch_prepack_kmajor(const uint8_t *Wq, const void *scales, bool f16
                                  const uint8_t *zeros, int64_t K, int64_t N, uint8_t *Pq, void *Ps,
                                  uint8_t *Pz, hipStream_t stream);
 hipError_t launch_gemv_kmajor(const KmajorPlan &plan, const float *x, int64_t M, int64_t K,
-                              const uint8_t *Pq, const void *Ps, bool f16, const uint8_t *Pz,
+                              const uint8_t *Pq, const void *Ps, bool f16, const void *Pz,
                               int64_t N, const float *bias, const float *residual, int act,
-                              float *y, hipStream_t stream);
+                              float *y, hipStream_t stream, bool affine = false);
+// Group-64 affine variant: quantize + pack, dequantize, K-major copy.
+hipError_t launch_g64_quantize_pack(const float *W, int64_t K, int64_t N, uint8_t *Wq,
+                                    float *scales, float *mins, int *d_status, hipStream_t stream);
+hipError_t launch_g64_dequantize(const uint8_t *Wq, const float *scales, const float *mins,
+                                 int64_t K, int64_t N, float *W_hat, hipStream_t stream);
+hipError_t launch_prepack_g64(const uint8_t *Wq, const float *scales, const float *mins,
+                              int64_t K, int64_t N, uint8_t *Pq, float *Ps, float *Pm,
+                              hipStream_t stream);
 // The fused epilogue alone (K = 0: the pre-activation values are the bias).
 hipError_t launch_epilogue_only(const float *bias, int64_t M, int64_t N, const float *residual,
                                 int act, float *y, hipStream_t stream);
