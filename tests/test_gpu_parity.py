@@ -744,3 +744,38 @@ def test_g64_special_inputs():
         y_ref, bound = ORC.w4g_matmul(x, Wq, s, m)
         y = host(w4.w4g_matmul_kmajor(dev(x), *P))
         assert_bound(y, y_ref, bound, f"g64 x={name}")
+
+
+def test_shared_workspace_growth_keeps_captured_graphs_valid():
+    """A graph captured with the shared scratch must stay correct after a later
+    call grows the scratch (the old buffer is kept, not freed and reused)."""
+    K, N = 3072, 768
+    W = mixed_weights(K, N, cfg=261)
+    Wq, s, z = w4.w4_quantize_pack(dev(W))
+    x = dev(synth.activations(1, K, cfg=261))
+    y = torch.empty((1, N), device=DEV)
+    need_small = w4.w4_matmul_workspace_bytes(1, K, N)
+    assert need_small > 0
+    ref = host(w4.w4_matmul(x, Wq, s, z))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w4.w4_matmul(x, Wq, s, z, out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.w4_matmul(x, Wq, s, z, out=y)
+    # a call needing far more scratch grows the pool
+    M2, K2, N2 = 64, 4096, 4096
+    assert w4.w4_matmul_workspace_bytes(M2, K2, N2) > 2 * need_small
+    W2 = synth.weights(K2, N2, cfg=262)
+    P2 = w4.w4_quantize_pack(dev(W2))
+    x2 = dev(synth.activations(M2, K2, cfg=262))
+    junk = [torch.full((1 << 22,), 7.0, device=DEV) for _ in range(4)]  # reuse pressure
+    w4.w4_matmul(x2, *P2)
+    del junk
+    for _ in range(3):
+        y.zero_()
+        g.replay()
+        assert_bits(host(y), ref, "graph replay after the scratch grew")

@@ -127,13 +127,18 @@ def _stream(device) -> int:
 
 
 class Workspace:
-    """Device scratch for the split-K partial sums, grown on demand.
+    """Device scratch for the split-K partial sums and the head's digit image,
+    grown on demand.
 
-    One buffer per device serves every call ordered on the same stream.
+    One buffer per device serves every call ordered on the same stream.  A
+    buffer that is outgrown is kept alive, not freed: a HIP graph captured
+    with it still names its address, and freeing it would let the caching
+    allocator hand that memory to another tensor under the graph.
     """
 
     def __init__(self):
         self._buf = {}
+        self._retired = []
         self._lock = threading.Lock()
 
     def get(self, device, nbytes: int):
@@ -143,7 +148,9 @@ class Workspace:
         with self._lock:
             buf = self._buf.get(key)
             if buf is None or buf.numel() < nbytes:
-                size = max(nbytes, 1 << 20)
+                if buf is not None:
+                    self._retired.append(buf)
+                size = max(nbytes, 1 << 20, 2 * (buf.numel() if buf is not None else 0))
                 buf = torch.empty(size, dtype=torch.uint8, device=device)
                 self._buf[key] = buf
         return buf, buf.numel()

@@ -180,11 +180,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits_mfma(const float *__
 }
 
 // Full-sequence logits, first launch: the digit image of x, built once.
-// One workgroup per group of 4 rows.  A-operand row 4 r + l of the group is
-// digit l of row r (each row has its own exponent e_r), laid out as the MFMA
-// reads it: img[group][j][4 r + l][kk] holds the digit of x[4 group + r,
-// 64 j + kk], so one 16-row x 64-byte block per K-step j.  erow[m] is e_m, or
-// INT_MIN for a row with a non-finite entry.  Rows past M are zero.
+// One workgroup per group of 4 rows.  A-operand row a = 4 r + l of the group
+// is digit l of row r (each row has its own exponent e_r), laid out in the
+// order the MFMA lanes read it: per K-step j one 1 KB block of 64 16-byte
+// elements, element 16 h + a holding the digits of x[4 group + r,
+// 64 j + 16 h .. 64 j + 16 h + 15] (lane l = 16 h + a reads element l, so a
+// wave's read is one contiguous kilobyte, free of LDS bank conflicts).
+// erow[m] is e_m, or INT_MIN for a row with a non-finite entry.  Rows past M
+// are zero.
 template <int XPT>
 __global__ __launch_bounds__(256) void k_head_digits(const float *__restrict__ x, int M, int K,
                                                      int8_t *__restrict__ img,
@@ -260,11 +263,11 @@ __global__ __launch_bounds__(256) void k_head_digits(const float *__restrict__ x
             const int v2 = (v1 - l1) >> 8;
             const int l2 = (int)(int8_t)(v2 & 0xFF);
             const int l3 = (v2 - l2) >> 8;
-            int8_t *d = dimg + ((k >> 6) * 16 + 4 * r) * 64 + (k & 63);
+            int8_t *d = dimg + (k >> 6) * 1024 + (((k & 63) >> 4) * 16 + 4 * r) * 16 + (k & 15);
             d[0] = (int8_t)l0;
-            d[64] = (int8_t)l1;
-            d[128] = (int8_t)l2;
-            d[192] = (int8_t)l3;
+            d[16] = (int8_t)l1;
+            d[32] = (int8_t)l2;
+            d[48] = (int8_t)l3;
         }
     }
     __syncthreads();
@@ -350,24 +353,40 @@ __global__ __launch_bounds__(256) void k_head_rows_mfma(const int8_t *__restrict
         if (rg0 + chunk < nrg) stage(rg0 + chunk, q ^ 1);
         const i32x4_t *cb = bufs[q];
         for (int r = 0; r < cnt; ++r) {
-            i32x4_t acc[TB];
+            // two accumulators per tile (even and odd K-steps): twice as many
+            // independent MFMA chains; int32 sums, so the order is exact
+            i32x4_t acc2[2][TB];
 #pragma unroll
-            for (int t = 0; t < TB; ++t) acc[t] = i32x4_t{0, 0, 0, 0};
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < TB; ++t) acc2[h][t] = i32x4_t{0, 0, 0, 0};
             // straight-line: steps past K read a valid block and multiply a
             // zero A operand (adds exactly 0), so the LDS reads can be issued
-            // ahead of the MFMAs
-            const i32x4_t *ap = cb + r * per_rg + c * 4 + g;
+            // ahead of the MFMAs; when K fills every step no select is needed
+            const i32x4_t *ap = cb + r * per_rg + lane;
             i32x4_t a[NJM];
 #pragma unroll
             for (int j = 0; j < NJM; ++j) a[j] = ap[min(j, NJ - 1) * 64];
+            if (NJ == NJM) {
 #pragma unroll
-            for (int j = 0; j < NJM; ++j) {
-                const i32x4_t aj = j < NJ ? a[j] : i32x4_t{0, 0, 0, 0};
+                for (int j = 0; j < NJM; ++j)
 #pragma unroll
-                for (int t = 0; t < TB; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        aj, __builtin_bit_cast(i32x4_t, b[t][j]), acc[t], 0, 0, 0);
+                    for (int t = 0; t < TB; ++t)
+                        acc2[j & 1][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            a[j], __builtin_bit_cast(i32x4_t, b[t][j]), acc2[j & 1][t], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJM; ++j) {
+                    const i32x4_t aj = j < NJ ? a[j] : i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                    for (int t = 0; t < TB; ++t)
+                        acc2[j & 1][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            aj, __builtin_bit_cast(i32x4_t, b[t][j]), acc2[j & 1][t], 0, 0, 0);
+                }
             }
+            i32x4_t acc[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) acc[t] = acc2[0][t] + acc2[1][t];
             const int m = 4 * (rg0 + r) + g;
             if (m < M) {
                 const int e = es[q][4 * r + g];
