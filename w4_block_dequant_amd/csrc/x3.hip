@@ -219,17 +219,18 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
                         acc[i][t][v] = __builtin_fmaf(sc[t], d[v], acc[i][t][v]);
                 }
             }
-            // Scale-accumulate here: the accumulators are only read by the
-            // guarded stores at the end, and the compiler would otherwise sink
-            // every block's FMAs there, keeping all MFMA results live.  An empty
-            // asm that reads and writes each accumulator pins them in place.
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(acc[i][t][v]));
         }
+        // Scale-accumulate here, once per quad: the accumulators are only read
+        // by the guarded stores at the end, and the compiler would otherwise
+        // sink every block's FMAs there, keeping all MFMA results live.  An
+        // empty asm that reads and writes each accumulator pins them in place;
+        // within the quad the four blocks' MFMA chains are free to overlap.
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(acc[i][t][v]));
     }
 
     // lane (g, c) holds D[4 g + v][c] of each (m-tile, column tile).  No lane
