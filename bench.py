@@ -52,6 +52,7 @@ GEMV_SOURCES = ("w4_block_dequant_amd/csrc/kmajor.hip", "w4_block_dequant_amd/cs
 PROFILE_DIR = "profiles"
 TRACE_SUMMARY = "k_gemv_kmajor_dense38_m1_kernel_trace.md"
 TRAFFIC_SUMMARY = "k_gemv_kmajor_dense38_m1_traffic.md"
+SECONDARY_SUMMARY = "secondary_workloads_kernel_trace.md"
 COPY_FLOATS = 1 << 26          # calibration copy: 256 MiB read, 256 MiB written
 PROFILE_COMMANDS = (
     "cd <repo root>; export TMPDIR=/tmp",
@@ -63,6 +64,9 @@ PROFILE_COMMANDS = (
     "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/w4prof/write "
     "-o run -- python bench.py --profile-run --steps 2",
     "python bench.py --json-out /tmp/w4prof/bench.json",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/w4prof/trace_all -o run "
+    "-- python bench.py --steps 10 --warmup 2 --skip-cpu "
+    "--json-out /tmp/w4prof/trace_all_bench.json",
     "python bench.py --summarize-profiles /tmp/w4prof --out profiles",
 )
 
@@ -672,6 +676,38 @@ def summarize_profiles(src: str, out_dir: str):
         f.write("\n".join(lines) + "\n")
     print(open(os.path.join(out_dir, TRACE_SUMMARY)).read())
     print(open(os.path.join(out_dir, TRAFFIC_SUMMARY)).read())
+
+    # ---- kernel trace of the whole bench, secondary workloads included
+    rows = []
+    for f in _csvs(os.path.join(src, "trace_all"), "kernel_trace.csv"):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        return
+    durs = {}
+    for r in rows:
+        durs.setdefault(r["Kernel_Name"], []).append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["# Kernel trace of the whole bench: the timed pass and every secondary workload",
+             "", "Made by:", "", cmds, "",
+             "Every dispatch of the traced run of the full bench (the secondary lines "
+             "included), by total time.  Template arguments name the instantiation: "
+             "`k_mm_x3<MT, NT, QPW, DQ, fp16 scales>` is the matrix-core matmul with MT "
+             "tiles of 16 rows (1 at M = 16, 4 at M = 58), `k_gemv_kmajor<rows, passes, "
+             "ragged, loop, fp16 scales, epilogue, affine>` the K-major GEMV, "
+             "`k_head_logits_mfma` the last-row head, `k_head_digits` + "
+             "`k_head_rows_mfma` the full-sequence head.", "",
+             "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:40]:
+        lines.append(f"| `{_short(k)}` | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                     f"{min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} | {sum(v) / 1e6:.3f} |")
+    if plain:  # tracing inflates graph replays: the untraced bench's lines
+        lines += ["", "Secondary lines of the untraced bench (`python bench.py --json-out "
+                  "<dir>/bench.json`, HIP events around graph replays):", ""]
+        for k, v in plain.get("secondary", {}).items():
+            lines.append(f"- {k}: {json.dumps(v)}")
+    with open(os.path.join(out_dir, SECONDARY_SUMMARY), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(os.path.join(out_dir, SECONDARY_SUMMARY)).read())
 
 
 if __name__ == "__main__":
