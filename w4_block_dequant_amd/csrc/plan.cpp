@@ -199,12 +199,23 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     p.kind = X3Plan::kRun;
     const int64_t rows = M < 64 ? M : 64;
     p.mt = (int)cdiv(rows, 16);
+    // Row tiles per workgroup.  Taller tiles convert each code once for more
+    // rows, but a small matrix then forms too few workgroups to fill the
+    // chip: with the workgroups that 64-row tiles allow (column groups x
+    // quads x row groups), measured best were 16-row tiles below 512 (every
+    // GPT-2 shape at M = 58 and 130), 32 rows below 2048 (3072 x 3072), 64
+    // rows above (the larger 3.8B shapes).
+    const int64_t w64 = cdiv(N, 64) * (K / 128) * cdiv(M, 64);
+    if (w64 < 512) p.mt = 1;
+    else if (w64 < 2048 && p.mt > 2) p.mt = 2;
+    static const int64_t env_mt = env_int("W4_X3_MT");
+    if (env_mt >= 1 && env_mt <= 4) p.mt = (int)(env_mt < cdiv(rows, 16) ? env_mt : cdiv(rows, 16));
     static const int64_t env_nt = env_int("W4_X3_NT");
     p.nt = (env_nt == 2 && p.mt <= 2) ? 2 : 1;
     p.dq = p.mt <= 2 ? 3 : 2;
     if (p.mt == 2 && p.nt == 2) p.dq = 2;
     p.col_wgs = cdiv(N, 64 * p.nt);
-    p.mgroups = cdiv(M, 64);
+    p.mgroups = cdiv(M, 16 * p.mt);
     p.npad = p.col_wgs * 64 * p.nt;
     const int64_t NQ = K / 128;
     // enough workgroups to fill the chip; larger row tiles carry more matrix

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
     const int g = lane >> 4, c = lane & 15;
     const int NB = K / kBlock, NQ = K / (4 * kBlock), hk = K / 2;
     const int split = blockIdx.y, splits = gridDim.y;
-    const int m0 = blockIdx.z * 64;
+    const int m0 = blockIdx.z * (16 * MT);  // this workgroup's group of 16 MT rows
     const int q_begin = split * QPW;
     const int nq = min(QPW, NQ - q_begin);  // quads of this workgroup (the last may have fewer)
     const int nw = blockIdx.x * (64 * NT) + wave * (16 * NT);
