@@ -23,7 +23,7 @@ Also reported on the same JSON line:
   * parity: GPU outputs of those layers against the oracle's, per output;
   * secondary: the GPT-2-small-shaped decode pass (48 matmuls with bias),
     the int8 head [768, 50257], the GPT-2 prefill pass at M = 58 plus the
-    last-row head, and the 3.8B pass at M = 16.
+    last-row head, and the 3.8B pass at M = 4 and M = 16.
 Inputs are seeded synthetic data of the workloads' shapes and distributions
 (see synth.py); nothing is read from disk.
 """
@@ -379,6 +379,19 @@ def main():
             "note": "SwiGLU fused into gate+up, residual add fused into out- and "
                     "down-projections; same weight bytes"}
         log(f"fused-epilogue pass: {secondary['dense38_m1_pass_fused_epilogues']}")
+
+        # 3.8B body at M = 4 (small-batch decode: the bf16 matrix cores from
+        # 3 rows on), same weights; HBM-bound (8 flops per 0.64-byte weight)
+        d4 = with_x(dense, synth.CFG_DENSE38, 4, outliers=True)
+        g4 = capture(lambda: run_pass(d4))
+        ms4, _ = time_graph(g4, 3, 1)
+        b4 = sum(m.bytes for m in d4)
+        secondary["dense38_m4_pass_kmajor"] = {
+            "ms": round(ms4, 4), "tokens_per_s": round(4e3 / ms4, 1),
+            "GB_s": round(b4 / (ms4 * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"M=4 pass: {secondary['dense38_m4_pass_kmajor']}")
+        del g4, d4
 
         # 3.8B body at M = 16 (batched decode), same weights
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)

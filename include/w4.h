@@ -143,9 +143,10 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
                       void *stream);
 
 /* y = x . w_hat + bias on the K-major layout: same result contract as
- * w4_matmul (fp32, same bound, deterministic).  Up to M = 4 rows (decode, small
- * batches) every workgroup owns whole columns and no workspace is used.  For
- * M > 4 with K % 128 == 0 the product runs on the bf16 matrix cores at fp32
+ * w4_matmul (fp32, same bound, deterministic).  For M <= 2 (decode), and
+ * for any M when K % 128 != 0, every workgroup owns whole columns and no
+ * workspace is used.  For M >= 3 with K % 128 == 0 (small batches, prefill)
+ * the product runs on the bf16 matrix cores at fp32
  * accuracy: (q - z) is exact in bf16 and each activation is split exactly
  * into three bf16 terms, so every product is exact and sums are fp32; each
  * block's scale is applied once per block.  That path may split K across

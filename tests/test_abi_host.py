@@ -140,7 +140,9 @@ def test_entry_points_reject_before_any_hip_call():
     assert km(A, 1, 128, A, A, A, 16, None, A, None, 0) == w4.W4_OK
     assert km(A, 1, 128, A + 8, A, A, 16, None, A, None, 0) == w4.W4_ERR_MISALIGNED
     assert km(None, 1, 128, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_NULL_PTR
-    # M > 4 on the matrix-core path: split-K needs a workspace for narrow N
+    # M >= 3 on the matrix-core path: split-K needs a workspace for narrow N
+    assert w4.w4_matmul_kmajor_workspace_bytes(2, 3072, 3072) == 0      # M = 2: the GEMV
+    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 3072) > 0       # M = 3: matrix cores
     need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072)
     assert need > 0
     assert w4.w4_matmul_kmajor_workspace_bytes(1, 3072, 3072) == 0

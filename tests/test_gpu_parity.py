@@ -465,9 +465,9 @@ X3_SHAPES = [(128, 16), (768, 768), (768, 2304), (3072, 768), (1024, 1008), (256
 
 
 @pytest.mark.parametrize("K,N", X3_SHAPES)
-@pytest.mark.parametrize("M", [5, 16, 17, 58, 64, 65, 130])
+@pytest.mark.parametrize("M", [3, 4, 5, 16, 17, 58, 64, 65, 130])
 def test_kmajor_matrix_cores(M, K, N):
-    """M > 4 on the bf16 matrix cores (split-K, ragged N, partial m-tiles)."""
+    """M >= 3 on the bf16 matrix cores (split-K, ragged N, partial m-tiles)."""
     note(f"kmajor x3 M={M} K={K} N={N} ws={w4.w4_matmul_kmajor_workspace_bytes(M, K, N)}")
     W = mixed_weights(K, N, cfg=232)
     x = synth.activations(M, K, cfg=232, slot=M, outliers=True)
@@ -599,11 +599,13 @@ def test_f16_matmul_kmajor(M, K, N):
 # fused epilogues (GELU, SwiGLU on interleaved gate/up columns, residual add)
 # --------------------------------------------------------------------------
 EP_CASES = [("none", True), ("gelu", False), ("gelu", True), ("swiglu", False), ("swiglu", True)]
-# (M, K, N): the decode GEMV (M <= 4), its row loop (M > 4 with K % 128 != 0),
-# the matrix cores with one split and with split-K, a ragged N, and K = 2048
-# (one column slot per workgroup: an odd column count is made even for SwiGLU)
+# (M, K, N): the decode GEMV (M <= 2, and M = 3 with K % 128 != 0), its row
+# loop (M > 4 with K % 128 != 0), the matrix cores from M = 3 with one split
+# and with split-K, a ragged N, and K = 2048 (one column slot per workgroup:
+# an odd column count is made even for SwiGLU)
 EP_SHAPES = [(1, 768, 2304), (1, 3072, 768), (3, 192, 530), (4, 2048, 768), (1, 2048, 768),
-             (7, 64, 96), (16, 768, 2304), (58, 768, 768), (16, 3072, 3072), (65, 256, 530)]
+             (2, 3072, 768), (7, 64, 96), (16, 768, 2304), (58, 768, 768), (16, 3072, 3072),
+             (65, 256, 530)]
 
 
 @pytest.mark.parametrize("M,K,N", EP_SHAPES)

@@ -195,7 +195,13 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
 
 X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     X3Plan p;
-    if (M <= 4 || K <= 0 || N <= 0 || K % 128 != 0) return p;
+    // From 3 rows on the matrix cores beat the GEMV, whose lanes then hold
+    // 4 rows of activations in registers (measured on the 3.8B shapes: 64
+    // against 116 us per layer at M = 3 and 4; at M = 2 the GEMV still wins
+    // on three shapes of four).
+    static const int64_t env_min = env_int("W4_X3_MIN_ROWS");
+    const int64_t min_rows = env_min >= 2 ? env_min : 3;
+    if (M < min_rows || K <= 0 || N <= 0 || K % 128 != 0) return p;
     p.kind = X3Plan::kRun;
     const int64_t rows = M < 64 ? M : 64;
     p.mt = (int)cdiv(rows, 16);

@@ -74,7 +74,7 @@ struct KmajorPlan {
 // that the SwiGLU epilogue's column pairs stay within one workgroup.
 KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols = false);
 
-// ---- M > 4 rows on the K-major layout: bf16 matrix cores, fp32 accuracy ------
+// ---- M >= 3 rows on the K-major layout: bf16 matrix cores, fp32 accuracy -----
 // Workgroup: 4 waves x nt tiles of 16 columns, the rows of one group of
 // 16 mt rows (mt tiles of 16, mt = 1..4), quads_per_wg quads of 4 K-blocks;
 // grid = col_wgs x splits x mgroups.  dq quads of loads in flight.  Needs

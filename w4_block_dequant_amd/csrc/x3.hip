@@ -1,4 +1,4 @@
-// Y = X . W_hat + bias for M > 4 rows on the K-major layout, on the bf16
+// Y = X . W_hat + bias for M >= 3 rows on the K-major layout, on the bf16
 // matrix cores with fp32 accuracy (page "ONNX export, quantization and the
 // browser runtime", section "Quantization", steps 1-2, and the runtime
 // paragraph after them: W_hat = (q - z) * scale, fp32 matmul).
