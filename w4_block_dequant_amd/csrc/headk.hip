@@ -302,12 +302,14 @@ __device__ __forceinline__ void copy_to_lds(const i32x4_t *__restrict__ src, i32
 // exactly as in the one-row kernel.  The table comes from HBM once; x only
 // through the small digit image.
 template <int TB, int NJM>
+// Arguments: those the prologue needs first, within the 14 preloaded
+// argument registers; the logits pointer last.
 __global__ __launch_bounds__(256) void k_head_rows_mfma(const int8_t *__restrict__ img,
-                                                        const int *__restrict__ erow, int M,
-                                                        int K, const int8_t *__restrict__ Qt,
-                                                        int ldt, const float *__restrict__ hs,
-                                                        int N, float *__restrict__ logits,
-                                                        int chunk) {
+                                                        const int *__restrict__ erow,
+                                                        const int8_t *__restrict__ Qt,
+                                                        const float *__restrict__ hs, int M,
+                                                        int K, int ldt, int N, int chunk,
+                                                        float *__restrict__ logits) {
     extern __shared__ i32x4_t abuf[];  // [2][chunk][K / 64][16][64] bytes
     __shared__ int es[2][kHeadRowsMaxChunk * 4];  // exponents of each buffer's rows
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -482,7 +484,7 @@ hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const i
 #define W4_HR(TBV, NJV)                                                                           \
     hipLaunchKernelGGL((k_head_rows_mfma<TBV, NJV>),                                             \
                        dim3((unsigned)((N + 64 * TBV - 1) / (64 * TBV))), dim3(256), shm, stream, \
-                       img, erow, (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits, (int)chunk)
+                       img, erow, Qt, hs, (int)M, (int)K, (int)ldt, (int)N, (int)chunk, logits)
     if (K <= 256) W4_HR(2, 4);
     else if (K <= 512) W4_HR(2, 8);
     else if (K <= 768) W4_HR(2, 12);

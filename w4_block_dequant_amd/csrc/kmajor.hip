@@ -103,7 +103,11 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 }
 
 // One workgroup: columns n0 .. n0 + CC - 1 (CC = G * P), MR rows of x
-// starting at row m0 = blockIdx.y * MR.  Lane L = (g, bl): column slot
+// starting at row m0 = blockIdx.y * MR.  The arguments that the first loads
+// depend on come first: they fit the 14 kernel-argument registers the
+// hardware fills at wave launch (the library is built with kernel-argument
+// preloading), so no wave waits for an argument load before its first
+// weight load; bias, residual, act and y are read only at the end.  Lane L = (g, bl): column slot
 // g = L / NBL and block bl, then bl + NBL, ... while < NB.  Pass p covers
 // column n0 + p * G + g.  Offsets are 32-bit (the host keeps every array
 // below 2^31 bytes).  CHECK clamps columns past N (ragged last workgroup);
@@ -115,10 +119,10 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // by every pass (the codes enter as the same fp16 subnormals, unshifted).
 template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP, bool AFF = false>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
-    const float *__restrict__ x, int M, int K, const uint8_t *__restrict__ Pq,
-    const void *__restrict__ Ps, const void *__restrict__ Pz, int N,
+    const float *__restrict__ x, const uint8_t *__restrict__ Pq, const void *__restrict__ Ps,
+    const void *__restrict__ Pz, int M, int K, int N, int G, int NBL,
     const float *__restrict__ bias, const float *__restrict__ residual, int act,
-    float *__restrict__ y, int G, int NBL) {
+    float *__restrict__ y) {
     extern __shared__ float red[];  // [MR][CC][NBL]
     const int L = threadIdx.x;
     const int g = L / NBL, bl = L - g * NBL;
@@ -363,23 +367,21 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const bool check = (N % C) != 0;
     const bool loop = p.lanes_per_col < K / kBlock;
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
+#define W4_KM_ARGS                                                                              \
+    x, Pq, Ps, Pz, (int)M, (int)K, (int)N, p.groups, p.lanes_per_col, bias, residual, act, y
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
     if (affine)                                                                                 \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true>), grid,            \
-                           dim3(p.threads), shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N,    \
-                           bias, residual, act, y, p.groups, p.lanes_per_col);                  \
+                           dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else if (f16)                                                                               \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false>), grid, dim3(p.threads),  \
-                           shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
-                           act, y, p.groups, p.lanes_per_col);                                  \
+                           shm, stream, W4_KM_ARGS);                                            \
     else if (ep)                                                                                \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true>), grid, dim3(p.threads),  \
-                           shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
-                           act, y, p.groups, p.lanes_per_col);                                  \
+                           shm, stream, W4_KM_ARGS);                                            \
     else                                                                                        \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false>), grid, dim3(p.threads), \
-                           shm, stream, x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual,    \
-                           act, y, p.groups, p.lanes_per_col)
+                           shm, stream, W4_KM_ARGS)
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
         if (check) {                                                                            \
@@ -395,6 +397,7 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     W4_KM_CASE(1, 6) W4_KM_CASE(1, 8) W4_KM_CASE(1, 12) W4_KM_CASE(1, 16)
     W4_KM_CASE(2, 1) W4_KM_CASE(2, 2) W4_KM_CASE(2, 4)
     W4_KM_CASE(4, 1) W4_KM_CASE(4, 2)
+#undef W4_KM_ARGS
 #undef W4_KM_LAUNCH
 #undef W4_KM_CASE
     return hipErrorInvalidValue;
