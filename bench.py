@@ -135,7 +135,7 @@ def main():
         summarize_profiles(args.summarize_profiles, args.out)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding or collectives).", file=sys.stderr)
         sys.exit(2)
 
