@@ -231,6 +231,11 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     // on the 3.8B shapes (the extra split-K partials cost less than idle CUs)
     const int64_t target = env_wgs > 0 ? env_wgs : 1024;
     int64_t splits = cdiv(target, p.col_wgs * p.mgroups);
+    // No split when the matrix already forms half a chip of workgroups and
+    // each one's K loop is short (K <= 1024): the split-K reduce is a second
+    // launch, which costs more there than the idle compute units (GPT-2
+    // 768 x 2304 and 768 x 3072 at M = 58: 9.5 -> 8.1 and 10.2 -> 8.0 us)
+    if (env_wgs <= 0 && p.col_wgs * p.mgroups >= 128 && NQ <= 8) splits = 1;
     if (splits > NQ) splits = NQ;
     if (splits < 1) splits = 1;
     const int64_t want = cdiv(NQ, splits);  // quads per workgroup, then the largest
