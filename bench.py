@@ -705,7 +705,7 @@ def summarize_profiles(src: str, out_dir: str):
              "Every dispatch of the traced run of the full bench (the secondary lines "
              "included), by total time.  Template arguments name the instantiation: "
              "`k_mm_x3<MT, NT, QPW, DQ, fp16 scales>` is the matrix-core matmul with MT "
-             "tiles of 16 rows (1 at M = 16, 4 at M = 58), `k_gemv_kmajor<rows, passes, "
+             "tiles of 16 rows (1 for every workload here: M = 4 and 16, and the small GPT-2 matrices at M = 58), `k_gemv_kmajor<rows, passes, "
              "ragged, loop, fp16 scales, epilogue, affine>` the K-major GEMV, "
              "`k_head_logits_mfma` the last-row head, `k_head_digits` + "
              "`k_head_rows_mfma` the full-sequence head.", "",
