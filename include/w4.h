@@ -4,13 +4,15 @@
  *
  * The method (page "ONNX export, quantization and the browser runtime",
  * section "Quantization (train/quantize.py)"):
- *   step 1  every body weight is a plain [K, N] constant followed by a bias Add;
- *   step 2  it is stored 4-bit: asymmetric, blocks of 32 along K, one fp32
- *           scale and one uint4 zero point per block, as packed UINT4, and a
- *           blocked DequantizeLinear gives w_hat = (q - z) * scale;
- *   step 3  the tied embedding / LM head is one int8 table [768, 50257] with
- *           one scale per token; the token lookup gathers its columns;
- *   step 4  the head is applied to the last position only.
+ *   step 1  each linear layer of the body is a [K, N] weight matrix and a bias;
+ *   step 2  the matrix is kept in 4 bits: in every column, each run of 32
+ *           rows is quantized asymmetrically with its own scale (fp32) and
+ *           zero point (uint4), codes are packed two to a byte, and
+ *           dequantization restores w_hat = (q - z) * scale in fp32;
+ *   step 3  the embedding and the LM head share one int8 [768, 50257] table
+ *           with an fp32 scale for each token; a token's embedding is its
+ *           column of the table;
+ *   step 4  logits are needed for the final position alone.
  * The paragraph after the steps: the runtime folds the dequantization and
  * runs fp32 kernels, so every matmul here computes x . w_hat in fp32.
  *
@@ -21,7 +23,7 @@
  *   zeros   uint8 [K/32, N/2]  packed like Wq: z[b, 2j] low nibble, z[b, 2j+1] high
  *   bias    fp32  [N]          may be NULL
  *   y       fp32  [M, N]
- *   Q       int8  [K, ldq]     head table, ldq >= N; hs fp32 [N] one scale per token
+ *   Q       int8  [K, ldq]     head table, ldq >= N; hs fp32 [N] a scale for each token
  * The pairing of nibbles along N (flat row-major UINT4 packing of the [K, N]
  * code tensor, element 2i in the low nibble) is a reading: the page says
  * only "raw packed UINT4"; low nibble first is fixed.

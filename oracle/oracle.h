@@ -8,13 +8,14 @@
  *
  * Source of the method: the page "ONNX export, quantization and the browser
  * runtime", section "Quantization (train/quantize.py)", steps 1-4:
- *   - every body weight is a plain [K, N] constant followed by a bias Add;
- *   - it is stored 4-bit, asymmetric, in blocks of 32 along K, with one fp32
- *     scale and one uint4 zero point per block, as packed UINT4 tensors, and a
- *     blocked DequantizeLinear restores fp32;
- *   - the tied embedding / LM head is stored once as int8 with one scale per
- *     token, in the head's [768, 50257] layout;
- *   - the head is applied to the last position only.
+ *   - each linear layer of the body is a [K, N] weight matrix and a bias;
+ *   - the matrix is kept in 4 bits: in every column each run of 32 rows is
+ *     quantized asymmetrically with its own scale (fp32) and zero point
+ *     (uint4), the codes are packed two to a byte, and dequantization gives
+ *     back fp32 values;
+ *   - the embedding and the LM head share a single int8 table laid out as
+ *     [768, 50257], with an fp32 scale for each token;
+ *   - logits are needed for the final position alone.
  * The same page, paragraph after the steps: the runtime folds the dequantize
  * nodes and runs plain fp32 kernels, so the matmul computes x . W_hat with
  * W_hat the fp32 output of the dequantization.

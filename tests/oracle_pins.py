@@ -17,7 +17,7 @@ different route to the same fact.
   * dequantization: every (q, z) pair against the exactly rounded rational
     product;
   * matmul: exact rational sums on tiny shapes, one-hot rows, constant-0.5
-    weights ("halved row sums"), zero activations;
+    weights (every output half the sum of its row of x), zero activations;
   * head: one-hot rows, sign symmetry, full use of [-127, 127], the
     round-trip bound, exact rational logits;
   * embedding lookup: rows of the dequantized table;
