@@ -31,6 +31,9 @@ FLAGS = [
     # arguments arrive in SGPRs at wave launch instead of through a scalar
     # load (the short decode launches save one memory round trip each)
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
+    # MFMA results in ordinary VGPRs (gfx950 allows it): no accumulation-
+    # register copies before the fp32 epilogue arithmetic, fewer registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -109,23 +109,26 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
         const uint32_t q = (uint32_t)(q_begin + min(j, nq - 1));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            R.w[t] = load_stream<u32x4_t>(Pq + oq[t] + 64u * q);  // block 4 q + g
+            // offsets summed in 32 bits first: one unsigned offset from a uniform
+            // base lets each load take the scalar-base form (no 64-bit address math)
+            R.w[t] = load_stream<u32x4_t>(Pq + (oq[t] + 64u * q));  // block 4 q + g
             if (H) {  // four binary16 scales
                 const u32x2_t h = *reinterpret_cast<const u32x2_t *>(
-                    static_cast<const uint16_t *>(Ps) + os[t] + 4u * q);
+                    static_cast<const char *>(Ps) + 2u * (os[t] + 4u * q));
                 R.s[t] = f32x4_t{f16_bits_to_f32((uint16_t)h.x), f16_bits_to_f32((uint16_t)(h.x >> 16)),
                                  f16_bits_to_f32((uint16_t)h.y), f16_bits_to_f32((uint16_t)(h.y >> 16))};
             } else {
-                R.s[t] = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(Ps) + os[t] +
-                                                            4u * q);
+                R.s[t] = *reinterpret_cast<const f32x4_t *>(static_cast<const char *>(Ps) +
+                                                            4u * (os[t] + 4u * q));
             }
-            R.z[t] = *reinterpret_cast<const uint16_t *>(Pz + oz[t] + 2u * q);
+            R.z[t] = *reinterpret_cast<const uint16_t *>(Pz + (oz[t] + 2u * q));
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                R.xv[i][b] = *reinterpret_cast<const float2 *>(x + ox[i] + 32u * (4u * q + b));
+                R.xv[i][b] = *reinterpret_cast<const float2 *>(
+                    reinterpret_cast<const char *>(x) + 4u * (ox[i] + 32u * (4u * q + b)));
     };
 
     f32x4v acc[MT][NT];
