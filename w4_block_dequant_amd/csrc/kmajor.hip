@@ -121,8 +121,7 @@ template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP, bool AFF = fals
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, const uint8_t *__restrict__ Pq, const void *__restrict__ Ps,
     const void *__restrict__ Pz, int M, int K, int N, int G, int NBL,
-    const float *__restrict__ bias, const float *__restrict__ residual, int act,
-    float *__restrict__ y) {
+    const float *__restrict__ bias, const float *residual, int act, float *y) {
     extern __shared__ float red[];  // [MR][CC][NBL]
     const int L = threadIdx.x;
     const int g = L / NBL, bl = L - g * NBL;
@@ -283,8 +282,8 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
 // one thread per output.
 __global__ __launch_bounds__(256) void k_epilogue_only(const float *__restrict__ bias, int64_t M,
                                                        int64_t N,
-                                                       const float *__restrict__ residual,
-                                                       int act, float *__restrict__ y) {
+                                                       const float *residual, int act,
+                                                       float *y) {
     const int64_t nout = act == W4_ACT_SWIGLU ? N / 2 : N;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= M * nout) return;

@@ -18,8 +18,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
                                                        const float *__restrict__ bias,
                                                        const float *__restrict__ col_scale,
                                                        float unit,
-                                                       const float *__restrict__ residual,
-                                                       int act, float *__restrict__ y) {
+                                                       const float *residual, int act,
+                                                       float *y) {
     const int n0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
     if (n0 >= N) return;
     const int64_t plane = rows * npad;

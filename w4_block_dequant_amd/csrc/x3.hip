@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
                                                const void *__restrict__ Ps,
                                                const uint8_t *__restrict__ Pz, int N,
                                                const float *__restrict__ bias,
-                                               const float *__restrict__ residual, int act,
-                                               float *__restrict__ y, int npad,
+                                               const float *residual, int act,
+                                               float *y, int npad,
                                                float *__restrict__ part) {
     // A operands of a quad: [buffer][block][m-tile][part][lane]; two buffers
     // (one barrier per quad) while they fit, else one (two barriers per quad)
