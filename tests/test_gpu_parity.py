@@ -489,7 +489,11 @@ def test_kmajor_matrix_cores_special_inputs():
              "one-hot rows": np.eye(M, K, 5, dtype=np.float32),
              "tiny": base * np.float32(1e-30),
              "huge": base * np.float32(1e30),
-             "spread": base * np.where(np.arange(K) % 3 == 0, 1e3, 1e-3).astype(np.float32)}
+             "spread": base * np.where(np.arange(K) % 3 == 0, 1e3, 1e-3).astype(np.float32),
+             # rows 10^-30 .. 10^30 apart in one 16-row tile: each row keeps
+             # its own scale on the M <= 16 path
+             "row magnitudes": base * np.logspace(-30, 30, M, dtype=np.float64)
+                                        .astype(np.float32)[:, None]}
     for name, x in cases.items():
         y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
         y = host(w4.w4_matmul_kmajor(dev(x), *P))

@@ -244,12 +244,18 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     p.mgroups = cdiv(M, 16 * p.mt);
     p.npad = p.col_wgs * 64 * p.nt;
     const int64_t NQ = K / 128;
+    // M <= 16 (one 16-row tile): the fp16 kernel, which builds all of its A
+    // operands before the first quad (3.8B layer at M = 4: 62 -> 55 us; at
+    // M = 16: 70 -> 62 us; at M = 58 the bf16 kernel stays ahead)
+    static const int64_t env_bf16 = env_int("W4_X3_BF16");
+    p.h3 = p.mt == 1 && p.nt == 1 && p.mgroups == 1 && env_bf16 != 1;
     // enough workgroups to fill the chip; larger row tiles carry more matrix
     // work per weight byte, so fewer (and less split-K partial traffic)
     static const int64_t env_wgs = env_int("W4_X3_TARGET_WGS");
-    // about four workgroups per compute unit: measured best at M = 16 and 58
-    // on the 3.8B shapes (the extra split-K partials cost less than idle CUs)
-    const int64_t target = env_wgs > 0 ? env_wgs : 1024;
+    // bf16: about four workgroups per compute unit, measured best at M = 16
+    // and 58 on the 3.8B shapes (the extra split-K partials cost less than
+    // idle CUs); fp16 (its workgroups hold up to 52 KB of LDS): about two
+    const int64_t target = env_wgs > 0 ? env_wgs : (p.h3 ? 512 : 1024);
     int64_t splits = cdiv(target, p.col_wgs * p.mgroups);
     // No split when the matrix already forms half a chip of workgroups and
     // each one's K loop is short (K <= 1024): the split-K reduce is a second
@@ -258,11 +264,12 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     if (env_wgs <= 0 && p.col_wgs * p.mgroups >= 128 && NQ <= 8) splits = 1;
     if (splits > NQ) splits = NQ;
     if (splits < 1) splits = 1;
+    const int64_t qmax = p.h3 ? 4 : 12;
     const int64_t want = cdiv(NQ, splits);  // quads per workgroup, then the largest
     static const int allowed[] = {12, 8, 6, 4, 3, 2, 1};  // instantiated count <= want
     p.quads_per_wg = 1;
     for (int a : allowed)
-        if (a <= want) {
+        if (a <= want && a <= qmax) {
             p.quads_per_wg = a;
             break;
         }

@@ -74,14 +74,15 @@ struct KmajorPlan {
 // that the SwiGLU epilogue's column pairs stay within one workgroup.
 KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols = false);
 
-// ---- M >= 3 rows on the K-major layout: bf16 matrix cores, fp32 accuracy -----
+// ---- M >= 3 rows on the K-major layout: matrix cores, fp32 accuracy -----------
 // Workgroup: 4 waves x nt tiles of 16 columns, the rows of one group of
 // 16 mt rows (mt tiles of 16, mt = 1..4), quads_per_wg quads of 4 K-blocks;
 // grid = col_wgs x splits x mgroups.  dq quads of loads in flight.  Needs
-// K % 128 == 0.
+// K % 128 == 0.  h3: one 16-row tile (M <= 16) on the fp16 matrix cores.
 struct X3Plan {
     enum Kind { kNone = 0, kRun = 1 } kind = kNone;
     int mt = 1, nt = 1, dq = 2;
+    bool h3 = false;  // M <= 16: the fp16 form (k_mm_h3), quads_per_wg <= 4
     int64_t col_wgs = 0, mgroups = 0, splits = 1, quads_per_wg = 0, npad = 0;
     size_t workspace = 0;
 };
