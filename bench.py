@@ -69,7 +69,8 @@ PROFILE_COMMANDS = (
     "-- python bench.py --steps 10 --warmup 2 --skip-cpu "
     "--json-out /tmp/w4prof/trace_all_bench.json",
     "timeout -s KILL 300 rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 "
-    "SQ_INSTS_VALU_MFMA_MOPS_F32 --output-format csv -d /tmp/w4prof/mfma -o run "
+    "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_F32 --output-format csv "
+    "-d /tmp/w4prof/mfma -o run "
     "-- python bench.py --profile-run-mfma --steps 2",
     "python bench.py --summarize-profiles /tmp/w4prof --out profiles",
 )
@@ -287,8 +288,9 @@ def main():
         return
 
     if args.profile_run_mfma:
-        # eager passes on the matrix-core paths: 3.8B body at M = 16 (prepacked
-        # bf16 x3 and canonical fp32 MFMA), GPT-2 body at M = 58 (prepacked)
+        # eager passes on the matrix-core paths: 3.8B body at M = 16 (prepacked:
+        # the fp16 kernel; canonical: fp32 MFMA), GPT-2 body at M = 58
+        # (prepacked: the bf16 kernel)
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
         gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)
         pre = with_x(gpt2, synth.CFG_GPT2_PREFILL, synth.GPT2_PROMPT, outliers=False)
@@ -405,8 +407,8 @@ def main():
                     "down-projections; same weight bytes"}
         log(f"fused-epilogue pass: {secondary['dense38_m1_pass_fused_epilogues']}")
 
-        # 3.8B body at M = 4 (small-batch decode: the bf16 matrix cores from
-        # 3 rows on), same weights; HBM-bound (8 flops per 0.64-byte weight)
+        # 3.8B body at M = 4 (small-batch decode: the matrix cores from 3 rows
+        # on), same weights; HBM-bound (8 flops per 0.64-byte weight)
         d4 = with_x(dense, synth.CFG_DENSE38, 4, outliers=True)
         g4 = capture(lambda: run_pass(d4))
         ms4, _ = time_graph(g4, 3, 1)
@@ -421,7 +423,7 @@ def main():
         # 3.8B body at M = 16 (batched decode), same weights
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
         fl16 = sum(m.flops for m in d16)
-        for layout, name in (("kmajor", "dense38_m16_pass_kmajor_bf16x3_mfma"),
+        for layout, name in (("kmajor", "dense38_m16_pass_kmajor_mfma"),
                              ("canonical", "dense38_m16_pass_canonical_fp32_mfma")):
             g16 = capture(lambda: run_pass(d16, layout=layout))
             ms16, _ = time_graph(g16, 3, 1)
@@ -729,8 +731,9 @@ def summarize_profiles(src: str, out_dir: str):
              "", "Made by:", "", cmds, "",
              "Every dispatch of the traced run of the full bench (the secondary lines "
              "included), by total time.  Template arguments name the instantiation: "
-             "`k_mm_x3<MT, NT, QPW, DQ, fp16 scales>` is the matrix-core matmul with MT "
-             "tiles of 16 rows (1 for every workload here: M = 4 and 16, and the small GPT-2 matrices at M = 58), `k_gemv_kmajor<rows, passes, "
+             "`k_mm_h3<MT, NT, QPW, DQ, fp16 scales>` is the fp16 matrix-core matmul for one "
+             "16-row tile (M = 4 and 16 here), `k_mm_x3<...>` the bf16 one for M > 16 with MT "
+             "tiles of 16 rows (1 for the small GPT-2 matrices at M = 58), `k_gemv_kmajor<rows, passes, "
              "ragged, loop, fp16 scales, epilogue, affine>` the K-major GEMV, "
              "`k_head_logits_mfma` the last-row head, `k_head_digits` + "
              "`k_head_rows_mfma` the full-sequence head.", "",
@@ -768,21 +771,24 @@ def summarize_profiles(src: str, out_dir: str):
              "prepacked).  `MfmaUtil` is rocprofv3's derived metric: MFMA-busy cycles over "
              "active cycles times SIMDs, in percent.  MFMA FLOP/s count the matrix-core "
              "operations the kernel issued (MOPS x 512 over the dispatch's duration under "
-             "counter collection): `k_mm_x3` issues three bf16 MFMAs per fp32 product "
-             "(exact splits of each activation), so its useful fp32 rate is a third of its "
-             "bf16 rate; `k_mm_mfma` runs fp32 MFMA.  Peaks: bf16 2.5 PFLOP/s, fp32 "
-             "157.3 TFLOP/s (dense).", "",
-             "| kernel | dispatches | MfmaUtil % (mean) | bf16 MFMA TFLOP/s | fp32 MFMA TFLOP/s | avg us |",
-             "|---|---|---|---|---|---|"]
+             "counter collection): `k_mm_h3` (M <= 16) and `k_mm_x3` (M > 16) issue three "
+             "fp16 or bf16 MFMAs per fp32 product (three-part splits of each activation), "
+             "so their useful fp32 rate is a third of their fp16/bf16 rate; `k_mm_mfma` "
+             "runs fp32 MFMA.  Peaks: fp16 and bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s "
+             "(dense).", "",
+             "| kernel | dispatches | MfmaUtil % (mean) | fp16 MFMA TFLOP/s | "
+             "bf16 MFMA TFLOP/s | fp32 MFMA TFLOP/s | avg us |",
+             "|---|---|---|---|---|---|---|"]
     for k, ds in sorted(kern.items(), key=lambda kv: -sum(d["ns"] for d in kv[1])):
         util = statistics.mean(d["c"]["MfmaUtil"] for d in ds)
         ns = sum(d["ns"] for d in ds)
+        h16 = sum(d["c"].get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) for d in ds) * 512
         bf = sum(d["c"].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in ds) * 512
         f32 = sum(d["c"].get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) for d in ds) * 512
-        if bf == 0 and f32 == 0:
+        if h16 == 0 and bf == 0 and f32 == 0:
             continue
-        lines.append(f"| `{_short(k)}` | {len(ds)} | {util:.1f} | {bf / ns / 1e3:.1f} | "
-                     f"{f32 / ns / 1e3:.1f} | {ns / len(ds) / 1e3:.2f} |")
+        lines.append(f"| `{_short(k)}` | {len(ds)} | {util:.1f} | {h16 / ns / 1e3:.1f} | "
+                     f"{bf / ns / 1e3:.1f} | {f32 / ns / 1e3:.1f} | {ns / len(ds) / 1e3:.2f} |")
     with open(os.path.join(out_dir, MFMA_SUMMARY), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(open(os.path.join(out_dir, MFMA_SUMMARY)).read())

@@ -148,10 +148,16 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
  * w4_matmul (fp32, same bound, deterministic).  For M <= 2 (decode), and
  * for any M when K % 128 != 0, every workgroup owns whole columns and no
  * workspace is used.  For M >= 3 with K % 128 == 0 (small batches, prefill)
- * the product runs on the bf16 matrix cores at fp32
- * accuracy: (q - z) is exact in bf16 and each activation is split exactly
- * into three bf16 terms, so every product is exact and sums are fp32; each
- * block's scale is applied once per block.  That path may split K across
+ * the product runs on the matrix cores at fp32 accuracy, each block's scale
+ * applied once per block and the block sums fp32.  M > 16: (q - z) is exact
+ * in bf16 and each activation is split exactly into three bf16 terms, so
+ * every product is exact.  3 <= M <= 16: (q - z) is exact in fp16 and each
+ * row of x, scaled by its own power of two over every K range of at most
+ * 512, is split into three fp16 terms that carry it to within
+ * 2^-33 |x| + 2^-39 max|x| (max over that row and range): inside the bound
+ * unless a row's largest activation in a range exceeds about 5 * 10^6 times
+ * the row's |w|-weighted average there.  Non-finite x gives NaN outputs on
+ * both.  That path may split K across
  * workgroups and then needs a workspace of
  * w4_matmul_kmajor_workspace_bytes(M, K, N) bytes (0 when it does not):
  * device memory, 256-byte aligned, any contents, not shared with a call in
