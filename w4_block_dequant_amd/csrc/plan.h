@@ -68,6 +68,7 @@ SmallMPlan plan_small_m(int64_t M, int64_t K, int64_t N);
 struct KmajorPlan {
     enum Kind { kEmpty = 0, kBiasOnly = 1, kRun = 2 } kind;
     int rows = 1, passes = 1, groups = 1, lanes_per_col = 64, threads = 64;
+    bool xc = true;  // activations in whole runs through LDS where the geometry allows
 };
 
 // even_cols: a workgroup's column count (groups * passes) must be even, so

@@ -9,10 +9,12 @@
 namespace w4 {
 namespace {
 
-// Grid: x over groups of 4 columns, y strides over rows (no index division).  Each
-// thread adds 4 adjacent outputs with 16-byte reads of every plane (npad is
-// a multiple of 4 and the planes are 256-byte aligned), in split order.
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ part,
+// Grid: x over groups of 4 columns (64 threads per workgroup, so that even a
+// one-row reduce spreads over many compute units), y strides over rows (no
+// index division).  Each thread adds 4 adjacent outputs with 16-byte reads of
+// every plane (npad is a multiple of 4 and the planes are 256-byte aligned),
+// in split order.
+__global__ __launch_bounds__(64) void k_splitk_reduce(const float *__restrict__ part,
                                                        int splits, int64_t rows, int N,
                                                        int64_t npad,
                                                        const float *__restrict__ bias,
@@ -36,17 +38,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
             for (int j = 0; j < 4; ++j) cj[j] = col_scale[min(n0 + j, N - 1)];
         }
         const float *p = part + m * npad + n0;
-        // eight planes' loads in flight at a time (addresses clamped to the
+        // sixteen planes' loads in flight at a time (addresses clamped to the
         // last plane), then added in split order: the same sums as one plane
-        // at a time, with a quarter of the dependent round trips at 8 splits
+        // at a time, with one dependent round trip up to 16 splits
         f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int s0 = 0; s0 < splits; s0 += 8) {
-            f32x4_t r[8];
+        for (int s0 = 0; s0 < splits; s0 += 16) {
+            f32x4_t r[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                r[j] = *reinterpret_cast<const f32x4_t *>(p + min(s0 + j, splits - 1) * plane);
+            for (int j = 0; j < 16; ++j)
+                r[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(
+                    p + min(s0 + j, splits - 1) * plane));
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 16; ++j)
                 if (s0 + j < splits) v += r[j];
         }
         float t[4];
@@ -78,8 +81,8 @@ hipError_t launch_splitk_reduce(const float *part, int64_t splits, int64_t rows,
                                 int act) {
     if (rows == 0 || N == 0) return hipSuccess;
     const int64_t groups = (N + 3) / 4;
-    const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
-    hipLaunchKernelGGL(k_splitk_reduce, grid, dim3(256), 0, stream, part, (int)splits, rows,
+    const dim3 grid((unsigned)((groups + 63) / 64), (unsigned)(rows < 65535 ? rows : 65535));
+    hipLaunchKernelGGL(k_splitk_reduce, grid, dim3(64), 0, stream, part, (int)splits, rows,
                        (int)N, npad, bias, col_scale, unit, residual, act, y);
     return hipGetLastError();
 }
