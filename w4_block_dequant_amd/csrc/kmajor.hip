@@ -414,22 +414,25 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_ARGS                                                                              \
     x, Pq, Ps, Pz, (int)M, (int)K, (int)N, p.groups, p.lanes_per_col, bias, residual, act, y
-#define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
+#define W4_KM_LAUNCH2(MRV, PV, CV, LV, XCV)                                                     \
     if (affine)                                                                                 \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true>), grid,            \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true, XCV>), grid,       \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else if (f16)                                                                               \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false>), grid, dim3(p.threads),  \
-                           shm, stream, W4_KM_ARGS);                                            \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false, false, XCV>), grid,       \
+                           dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else if (ep)                                                                                \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true>), grid, dim3(p.threads),  \
-                           shm, stream, W4_KM_ARGS);                                            \
-    else if (xc && MRV == 1 && !LV)                                                             \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, MRV == 1 && !LV>), \
-                           grid, dim3(p.threads), shm, stream, W4_KM_ARGS);                     \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true, false, XCV>), grid,       \
+                           dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else                                                                                        \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false>), grid, dim3(p.threads), \
-                           shm, stream, W4_KM_ARGS)
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV>), grid,      \
+                           dim3(p.threads), shm, stream, W4_KM_ARGS)
+#define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
+    if (MRV == 1 && !LV && xc) {                                                                \
+        W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV == 1 && !LV);                                        \
+    } else {                                                                                    \
+        W4_KM_LAUNCH2(MRV, PV, CV, LV, false);                                                  \
+    }
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
         if (check) {                                                                            \
@@ -447,6 +450,7 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     W4_KM_CASE(4, 1) W4_KM_CASE(4, 2)
 #undef W4_KM_ARGS
 #undef W4_KM_LAUNCH
+#undef W4_KM_LAUNCH2
 #undef W4_KM_CASE
     return hipErrorInvalidValue;
 }

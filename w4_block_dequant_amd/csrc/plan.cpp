@@ -210,12 +210,16 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
         p.passes = 2;
     // an odd column count only arises with one column slot and 1 or 3 passes
     if (even_cols && (p.groups * p.passes) % 2 != 0) p.passes = p.passes == 3 ? 4 : 2;
-    // Activations in whole 1 KB runs through LDS wherever the lane layout
-    // allows it (one row, one block per lane): 3.8B M=1 pass 0.905 -> 0.838 ms
-    // (3072 x 9216: 7.09 -> 6.40 us, 3072 x 16384: 8.86 -> 8.38, 8192 x 3072:
-    // 6.75 -> 6.21, 3072 x 3072 unchanged).  W4_KMAJOR_XC=2 turns it off.
+    // Activations in whole 1 KB runs through LDS where the lane layout allows
+    // it (one row, one block per lane) and the matrix fills the chip with
+    // workgroups: 3.8B M=1 pass 0.905 -> 0.838 ms (3072 x 9216: 7.09 -> 6.40
+    // us, 3072 x 16384: 8.86 -> 8.38, 8192 x 3072: 6.75 -> 6.21, 3072 x 3072
+    // unchanged); the GPT-2 matrices (48-144 workgroups, 3.2-3.4 us, bound by
+    // launch latency) lose 0.05-0.15 us to the extra LDS round trip.
+    // W4_KMAJOR_XC=1 forces it on, 2 off.
     static const int64_t env_xc = env_int("W4_KMAJOR_XC");
-    p.xc = env_xc != 2;
+    const int64_t wgs = cdiv(N, (int64_t)p.groups * p.passes) * cdiv(M, p.rows);
+    p.xc = env_xc == 1 || (env_xc != 2 && wgs >= 256);
     return p;
 }
 
