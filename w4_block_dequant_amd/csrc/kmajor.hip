@@ -117,8 +117,8 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // [N, K/64]: a lane's block is half a group, and its sum is
 // s * sum_k x q + m * sum_k x, with sum_k x formed once per lane and reused
 // by every pass (the codes enter as the same fp16 subnormals, unshifted).
-// XC (one row, NBL == NB so every lane owns exactly one block, NBL % 8 == 0,
-// every lane in a column slot): the activations are read
+// XC (one or two rows, NBL == NB so every lane owns exactly one block,
+// NBL % 8 == 0, every lane in a column slot): the activations are read
 // in whole 1 KB runs, eight consecutive blocks per load instruction (lane l
 // takes 16 bytes of block l / 8 of its 8-lane group's run), and handed to
 // the lanes that own each block through wave-private LDS (144-byte block
@@ -150,18 +150,21 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         for (int b = bl; LOOP ? b < NB : (b == bl && b < NB); b += NBL) {
             // activations of this block, for each of the MR rows
             float xr[MR][kBlock];
-            f32x4_t xg[XC ? kBlock / 4 : 1];  // XC: 16 bytes of each of 8 runs
+            f32x4_t xg[XC ? MR : 1][XC ? kBlock / 4 : 1];  // XC: 16 bytes of each of 8 runs
             const int lw = L & 63;
             if (XC) {
                 // run i: the 8 blocks of lane group i of this wave, from block
                 // bl(8 i); this lane takes block lw / 8 of it, bytes 16 (lw % 8)
-                const float *xrow = x + (size_t)m0 * K;
 #pragma unroll
-                for (int i = 0; i < kBlock / 4; ++i) {
-                    const int li = (L & ~63) + 8 * i;
-                    const int bi = li - (li / NBL) * NBL;
-                    xg[i] = *reinterpret_cast<const f32x4_t *>(xrow + kBlock * (bi + (lw >> 3)) +
-                                                               4 * (lw & 7));
+                for (int r = 0; r < MR; ++r) {
+                    const float *xrow = x + (size_t)min(m0 + r, M - 1) * K;
+#pragma unroll
+                    for (int i = 0; i < kBlock / 4; ++i) {
+                        const int li = (L & ~63) + 8 * i;
+                        const int bi = li - (li / NBL) * NBL;
+                        xg[r][i] = *reinterpret_cast<const f32x4_t *>(
+                            xrow + kBlock * (bi + (lw >> 3)) + 4 * (lw & 7));
+                    }
                 }
             }
 #pragma unroll
@@ -217,19 +220,25 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
             if (XC) {
                 // run i's pieces to block slot 8 i + lw / 8 of this wave's
                 // staging area; then this lane's own block is slot lw
-                float *xs = red + MR * CC * NBL + (L & ~63) * 36;
+                float *xs = red + MR * CC * NBL + (L & ~63) * (36 * MR);
 #pragma unroll
-                for (int i = 0; i < kBlock / 4; ++i)
-                    *reinterpret_cast<f32x4_t *>(xs + 36 * (8 * i + (lw >> 3)) + 4 * (lw & 7)) = xg[i];
+                for (int r = 0; r < MR; ++r)
+#pragma unroll
+                    for (int i = 0; i < kBlock / 4; ++i)
+                        *reinterpret_cast<f32x4_t *>(xs + 36 * (64 * r + 8 * i + (lw >> 3)) +
+                                                     4 * (lw & 7)) = xg[r][i];
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int i = 0; i < kBlock / 4; ++i) {
-                    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(xs + 36 * lw + 4 * i);
-                    xr[0][4 * i + 0] = v.x;
-                    xr[0][4 * i + 1] = v.y;
-                    xr[0][4 * i + 2] = v.z;
-                    xr[0][4 * i + 3] = v.w;
-                }
+                for (int r = 0; r < MR; ++r)
+#pragma unroll
+                    for (int i = 0; i < kBlock / 4; ++i) {
+                        const f32x4_t v =
+                            *reinterpret_cast<const f32x4_t *>(xs + 36 * (64 * r + lw) + 4 * i);
+                        xr[r][4 * i + 0] = v.x;
+                        xr[r][4 * i + 1] = v.y;
+                        xr[r][4 * i + 2] = v.z;
+                        xr[r][4 * i + 3] = v.w;
+                    }
             }
             float xs[MR];  // AFF: sum of the block's activations, per row
 #pragma unroll
@@ -404,13 +413,13 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const dim3 grid((unsigned)((N + C - 1) / C), (unsigned)((M + p.rows - 1) / p.rows));
     const bool check = (N % C) != 0;
     const bool loop = p.lanes_per_col < K / kBlock;
-    // whole-run activation loads: one row and exactly one block per lane (no
+    // whole-run activation loads: one or two rows, exactly one block per lane (no
     // idle lanes: every lane of a wave takes part in the runs' loads), 8-lane
     // groups inside one column slot
-    const bool xc = p.xc && p.rows == 1 && p.lanes_per_col == K / kBlock &&
+    const bool xc = p.xc && p.rows <= 2 && p.lanes_per_col == K / kBlock &&
                     p.lanes_per_col % 8 == 0 && (int64_t)p.groups * p.lanes_per_col == p.threads;
     const size_t shm = (size_t)p.rows * C * p.lanes_per_col * sizeof(float) +
-                       (xc ? (size_t)p.threads * 36 * sizeof(float) : 0);
+                       (xc ? (size_t)p.threads * 36 * p.rows * sizeof(float) : 0);
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_ARGS                                                                              \
     x, Pq, Ps, Pz, (int)M, (int)K, (int)N, p.groups, p.lanes_per_col, bias, residual, act, y
@@ -428,8 +437,8 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV>), grid,      \
                            dim3(p.threads), shm, stream, W4_KM_ARGS)
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
-    if (MRV == 1 && !LV && xc) {                                                                \
-        W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV == 1 && !LV);                                        \
+    if (MRV <= 2 && !LV && xc) {                                                                \
+        W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && !LV);                                        \
     } else {                                                                                    \
         W4_KM_LAUNCH2(MRV, PV, CV, LV, false);                                                  \
     }
