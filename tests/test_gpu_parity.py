@@ -442,8 +442,11 @@ def test_prepack_kmajor_bit_exact(K, N):
         assert_bits(host(a), b, f"{name} {K}x{N}")
 
 
+# (3072, 3080): every lane owns one block and the matrix fills the chip, so
+# M = 1 and 2 take the whole-run activation loads, with a ragged last
+# workgroup (3080 is not a multiple of the 12 columns per workgroup)
 KMAJOR_SHAPES = [(64, 16), (768, 768), (768, 2304), (3072, 768), (1024, 1008), (192, 530),
-                 (8192, 512), (128, 2), (4096, 4112), (320, 96)]
+                 (8192, 512), (128, 2), (4096, 4112), (320, 96), (3072, 3080)]
 
 
 @pytest.mark.parametrize("K,N", KMAJOR_SHAPES)
