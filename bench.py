@@ -601,6 +601,12 @@ def _csvs(root: str, suffix: str):
     return sorted(out)
 
 
+def _pct(v, q):
+    """Percentile q (0-100) of the values v, nearest-rank."""
+    w = sorted(v)
+    return w[min(len(w) - 1, max(0, int(round(q / 100.0 * (len(w) - 1)))))]
+
+
 def _short(name: str) -> str:
     name = name.replace("void ", "").replace("(anonymous namespace)::", "")
     name = name.split("(")[0]
@@ -645,9 +651,11 @@ def summarize_profiles(src: str, out_dir: str):
              "is over all K-major GEMV dispatches; the untraced bench's figure is the "
              "timed pass over its launches (`python bench.py --json-out <dir>/bench.json`).",
              ""]
-    lines += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    lines += ["| kernel | calls | avg us | p10 us | median us | p90 us | min us | max us |",
+              "|---|---|---|---|---|---|---|---|"]
     for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:12]:
         lines.append(f"| `{_short(k)}` | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                     f"{_pct(v, 10) / 1e3:.3f} | {_pct(v, 50) / 1e3:.3f} | {_pct(v, 90) / 1e3:.3f} | "
                      f"{min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} |")
     avg_gemv_us = statistics.mean(gemv) / 1e3 if gemv else float("nan")
     lines += ["", f"- gemv_dispatches: {len(gemv)}",
@@ -737,9 +745,11 @@ def summarize_profiles(src: str, out_dir: str):
              "ragged, loop, fp16 scales, epilogue, affine>` the K-major GEMV, "
              "`k_head_logits_mfma` the last-row head, `k_head_digits` + "
              "`k_head_rows_mfma` the full-sequence head.", "",
-             "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | p10 us | median us | p90 us | min us | max us | total ms |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:40]:
         lines.append(f"| `{_short(k)}` | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                     f"{_pct(v, 10) / 1e3:.3f} | {_pct(v, 50) / 1e3:.3f} | {_pct(v, 90) / 1e3:.3f} | "
                      f"{min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} | {sum(v) / 1e6:.3f} |")
     if plain:  # tracing inflates graph replays: the untraced bench's lines
         lines += ["", "Secondary lines of the untraced bench (`python bench.py --json-out "
