@@ -119,12 +119,12 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // by every pass (the codes enter as the same fp16 subnormals, unshifted).
 // XC (one or two rows, NBL == NB so every lane owns exactly one block,
 // NBL % 8 == 0, every lane in a column slot): the activations are read
-// in whole 1 KB runs, eight consecutive blocks per load instruction (lane l
-// takes 16 bytes of block l / 8 of its 8-lane group's run), and handed to
-// the lanes that own each block through wave-private LDS (144-byte block
-// slots, so the 16-byte reads of one block per lane do not collide).  A
-// lane's own block's 128 bytes would otherwise come from 8 loads that each
-// touch 64 different cache lines.
+// in whole 1 KB runs: load instruction i reads the 8 consecutive blocks that
+// lane group i of the wave owns, lane l taking bytes 16 (l % 8) of the run's
+// block l / 8; wave-private LDS (144-byte block slots, so the 16-byte reads
+// of one block per lane do not collide) then hands every lane its own
+// block.  A lane's own block's 128 bytes would otherwise come from 8 loads
+// that each touch 64 different cache lines.
 template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP, bool AFF = false,
           bool XC = false>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
@@ -220,12 +220,12 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
             if (XC) {
                 // run i's pieces to block slot 8 i + lw / 8 of this wave's
                 // staging area; then this lane's own block is slot lw
-                float *xs = red + MR * CC * NBL + (L & ~63) * (36 * MR);
+                float *xstage = red + MR * CC * NBL + (L & ~63) * (36 * MR);
 #pragma unroll
                 for (int r = 0; r < MR; ++r)
 #pragma unroll
                     for (int i = 0; i < kBlock / 4; ++i)
-                        *reinterpret_cast<f32x4_t *>(xs + 36 * (64 * r + 8 * i + (lw >> 3)) +
+                        *reinterpret_cast<f32x4_t *>(xstage + 36 * (64 * r + 8 * i + (lw >> 3)) +
                                                      4 * (lw & 7)) = xg[r][i];
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
 #pragma unroll
                     for (int i = 0; i < kBlock / 4; ++i) {
                         const f32x4_t v =
-                            *reinterpret_cast<const f32x4_t *>(xs + 36 * (64 * r + lw) + 4 * i);
+                            *reinterpret_cast<const f32x4_t *>(xstage + 36 * (64 * r + lw) + 4 * i);
                         xr[r][4 * i + 0] = v.x;
                         xr[r][4 * i + 1] = v.y;
                         xr[r][4 * i + 2] = v.z;
