@@ -478,6 +478,38 @@ def main():
                 "note": "55 MB body: resident in the 256 MB Infinity Cache across passes"}
             del gg
 
+        # the same pass cold: 20 copies of the prepacked body (1.1 GB, over
+        # four times the Infinity Cache) read in turn, one pass per copy
+        copies = [[tuple(t.clone() for t in m.P) for m in gpt2] for _ in range(20)]
+
+        def run_cold():
+            for cp in copies:
+                for m, P in zip(gpt2, cp):
+                    w4.w4_matmul_kmajor(m.x, *P, bias=m.b, out=m.y)
+
+        gc = capture(run_cold)
+        msc, _ = time_graph(gc, 5, 1)
+        del gc, copies
+        msc /= 20
+        secondary["gpt2_decode_pass_kmajor_cold"] = {
+            "ms": round(msc, 5), "tokens_per_s": round(1e3 / msc, 1),
+            "GB_s": round(gb / (msc * 1e-3) / 1e9, 1),
+            "note": "20 copies of the 55 MB body read in turn: weights from HBM"}
+        # one 768 x 768 matmul cold: 2,800 copies (1.06 GB) in turn
+        m0 = gpt2[1]
+        assert (m0.K, m0.N) == (768, 768)
+        one = [tuple(t.clone() for t in m0.P) for _ in range(2800)]
+        g1 = capture(lambda: [w4.w4_matmul_kmajor(m0.x, *P, bias=m0.b, out=m0.y) for P in one])
+        ms1, _ = time_graph(g1, 3, 1)
+        del g1, one
+        us1 = 1e3 * ms1 / 2800
+        secondary["gpt2_768x768_cold"] = {
+            "us": round(us1, 3), "GB_s": round(m0.bytes / (us1 * 1e-6) / 1e9, 1),
+            "note": "2,800 copies read in turn; latency-bound (384 KB per launch)"}
+        log(f"GPT-2 cold: {secondary['gpt2_decode_pass_kmajor_cold']}, "
+            f"{secondary['gpt2_768x768_cold']}")
+        torch.cuda.empty_cache()
+
         # int8 head [768, 50257]: 8 copies of each table (> the 256 MB Infinity
         # Cache) are read in turn, 24 launches per graph replay, so every launch
         # streams its table from HBM and graph launch costs are amortized
