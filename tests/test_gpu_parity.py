@@ -482,6 +482,34 @@ def test_kmajor_matrix_cores(M, K, N):
     assert_bound(y, y_ref, bound, f"kmajor x3 M={M} {K}x{N}")
 
 
+# seeded draws over the K-major plan's corners: K a multiple of 64 (the GEMV,
+# whole-run activation loads or not, one or several blocks per lane) or of
+# 128 (the matrix cores: the fp16 kernel up to 16 rows, bf16 beyond, with and
+# without split-K), N even and ragged, M from 1 to 70
+def _random_kmajor_cases(n, seed=2024):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        K = int(g.choice([64, 128, 192, 256, 384, 640, 768, 1024, 1536, 2048, 3072, 4096]))
+        N = 2 * int(g.integers(1, 2600))
+        M = int(g.choice([1, 1, 2, 2, 3, 4, 5, 8, 12, 16, 17, 33, 70]))
+        out.append((M, K, N))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N", _random_kmajor_cases(24))
+def test_kmajor_random_shapes(M, K, N):
+    note(f"kmajor random M={M} K={K} N={N}")
+    W = mixed_weights(K, N, cfg=236)
+    x = synth.activations(M, K, cfg=236, slot=M, outliers=True)
+    b = synth.bias(N, cfg=236)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z, b)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y, y_ref, bound, f"kmajor random M={M} {K}x{N}")
+
+
 def test_kmajor_matrix_cores_special_inputs():
     K, N, M = 768, 2304, 16
     W = mixed_weights(K, N, cfg=233)
