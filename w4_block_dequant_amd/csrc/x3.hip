@@ -121,15 +121,14 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
             // base lets each load take the scalar-base form (no 64-bit address math)
             R.w[t] = load_stream<u32x4_t>(Pq + (oq[t] + 64u * q));  // block 4 q + g
             if (H) {  // four binary16 scales
-                const u32x2_t h = *reinterpret_cast<const u32x2_t *>(
-                    static_cast<const char *>(Ps) + 2u * (os[t] + 4u * q));
+                const u32x2_t h =
+                    load_stream<u32x2_t>(static_cast<const char *>(Ps) + 2u * (os[t] + 4u * q));
                 R.s[t] = f32x4_t{f16_bits_to_f32((uint16_t)h.x), f16_bits_to_f32((uint16_t)(h.x >> 16)),
                                  f16_bits_to_f32((uint16_t)h.y), f16_bits_to_f32((uint16_t)(h.y >> 16))};
             } else {
-                R.s[t] = *reinterpret_cast<const f32x4_t *>(static_cast<const char *>(Ps) +
-                                                            4u * (os[t] + 4u * q));
+                R.s[t] = load_stream<f32x4_t>(static_cast<const char *>(Ps) + 4u * (os[t] + 4u * q));
             }
-            R.z[t] = *reinterpret_cast<const uint16_t *>(Pz + (oz[t] + 2u * q));
+            R.z[t] = load_stream<uint16_t>(Pz + (oz[t] + 2u * q));
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -380,15 +379,14 @@ __global__ __launch_bounds__(256) void k_mm_h3(const float *__restrict__ x, int 
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if (H) {
-                const u32x2_t h = *reinterpret_cast<const u32x2_t *>(
-                    static_cast<const char *>(Ps) + 2u * (os[t] + 4u * q));
+                const u32x2_t h =
+                    load_stream<u32x2_t>(static_cast<const char *>(Ps) + 2u * (os[t] + 4u * q));
                 sv[t] = f32x4_t{f16_bits_to_f32((uint16_t)h.x), f16_bits_to_f32((uint16_t)(h.x >> 16)),
                                 f16_bits_to_f32((uint16_t)h.y), f16_bits_to_f32((uint16_t)(h.y >> 16))};
             } else {
-                sv[t] = *reinterpret_cast<const f32x4_t *>(static_cast<const char *>(Ps) +
-                                                           4u * (os[t] + 4u * q));
+                sv[t] = load_stream<f32x4_t>(static_cast<const char *>(Ps) + 4u * (os[t] + 4u * q));
             }
-            zv[t] = *reinterpret_cast<const uint16_t *>(Pz + (oz[t] + 2u * q));
+            zv[t] = load_stream<uint16_t>(Pz + (oz[t] + 2u * q));
         }
     }
     Loads L[QPW];
