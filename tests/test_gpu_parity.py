@@ -510,6 +510,29 @@ def test_kmajor_random_shapes(M, K, N):
     assert_bound(y, y_ref, bound, f"kmajor random M={M} {K}x{N}")
 
 
+def _random_epilogue_cases(n, seed=777):
+    acts = ("none", "gelu", "swiglu")
+    return [(M, K, N, acts[i % 3], (i // 3) % 2 == 1)
+            for i, (M, K, N) in enumerate(_random_kmajor_cases(n, seed=seed))]
+
+
+@pytest.mark.parametrize("M,K,N,act,res", _random_epilogue_cases(48))
+def test_kmajor_random_shapes_epilogue(M, K, N, act, res):
+    note(f"kmajor random epilogue M={M} K={K} N={N} act={act} residual={res}")
+    W = mixed_weights(K, N, cfg=237)
+    x = synth.activations(M, K, cfg=237, slot=M, outliers=True)
+    b = synth.bias(N, cfg=237)
+    nout = N // 2 if act == "swiglu" else N
+    r = synth.activations(M, nout, cfg=238, slot=M) if res else None
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, b, r, act=act)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b), act=act,
+                                 residual=None if r is None else dev(r)))
+    assert y.shape == (M, nout)
+    assert_bound(y, y_ref, bound, f"kmajor random epilogue {act} M={M} {K}x{N}")
+
+
 def test_kmajor_matrix_cores_special_inputs():
     K, N, M = 768, 2304, 16
     W = mixed_weights(K, N, cfg=233)
