@@ -693,6 +693,115 @@ def pin_epilogue_matmul(orc):
             None, 0, K, None, None, None, N, None, None, 7, None, None))
 
 
+def _gelu64(v: float) -> float:
+    import math
+    return 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))
+
+
+def _silu64(v: float) -> float:
+    import math
+    return v / (1.0 + math.exp(-v))
+
+
+def _slope_max(f, lo, hi, step=1e-4):
+    """Largest |f'| on [lo, hi], from central differences on a fine grid."""
+    v = np.arange(lo, hi, step)
+    h = 1e-6
+    return max(abs(f(a + h) - f(a - h)) / (2 * h) for a in v)
+
+
+def _targeted_epilogue_case(orc, targets, seed):
+    """x, W_hat and exact pre-activations t[m, n] = sum_k x W_hat + b, with t
+    steered close to targets[m, n] and sum_k |x W_hat| large (so the matmul
+    bound dominates the activation's own rounding allowance).  Column n of W
+    is nonzero on rows 8n .. 8n + 7 only, so each column's activations can be
+    chosen on their own."""
+    g = np.random.default_rng(seed)
+    M, N = targets.shape
+    K = (8 * N + 31) // 32 * 32
+    W = np.zeros((K, N), np.float32)
+    for n in range(N):
+        W[8 * n:8 * n + 8, n] = g.standard_normal(8).astype(np.float32)
+    Wq, sc, zp = orc.quantize_pack(W)
+    What = orc.dequantize(Wq, sc, zp, K, N)
+    b = (g.standard_normal(N) * 0.5).astype(np.float32)
+    x = (g.standard_normal((M, K)) * 60.0).astype(np.float32)
+    for m in range(M):
+        for n in range(N):
+            w = What[8 * n:8 * n + 8, n].astype(np.float64)
+            j = int(np.argmax(np.abs(w)))
+            rest = sum(float(x[m, 8 * n + i]) * w[i] for i in range(8) if i != j)
+            x[m, 8 * n + j] = np.float32((targets[m, n] - float(b[n]) - rest) / w[j])
+    t = np.empty((M, N))
+    tb = np.empty((M, N))
+    for m in range(M):
+        for n in range(N):
+            tt = sum((F(x[m, k]) * F(What[k, n]) for k in range(K)), F(b[n]))
+            ab = sum((abs(F(x[m, k]) * F(What[k, n])) for k in range(K)), abs(F(b[n])))
+            t[m, n] = float(tt)
+            tb[m, n] = 1e-5 * float(ab) + 1e-6    # the matmul's stated tolerance
+    return x, Wq, sc, zp, b, t, tb
+
+
+def pin_epilogue_bound(orc):
+    """The fused epilogue's tolerance, checked against the activations
+    themselves: every pre-activation value the matmul bound admits must map
+    inside the bound (sufficiency), and where the activation is steepest the
+    bound may not exceed the worst such deviation by more than 5% (tightness).
+    t is exact (rationals); the activations are evaluated in fp64 here, from
+    their formulas, at many points of the admitted interval."""
+    eval_allow = lambda *a: 2.0 ** -21 * sum(abs(v) for v in a)   # fp32 evaluation slack
+    # slopes measured, not assumed: GELU (tanh form) and SiLU
+    sg = _slope_max(_gelu64, -8.0, 8.0)
+    ss = _slope_max(_silu64, -12.0, 12.0)
+    assert 1.12 < sg < 1.13 and 1.09 < ss < 1.1, (sg, ss)
+    v_steep = max(np.arange(0.0, 4.0, 1e-3), key=lambda a: abs(_gelu64(a + 1e-6) - _gelu64(a - 1e-6)))
+    # ---- GELU: rows steered to the steepest point and across [-6, 6]
+    M, N = 12, 6
+    targets = np.empty((M, N))
+    targets[:4] = v_steep
+    targets[4:] = np.linspace(-6.0, 6.0, 8 * N).reshape(8, N)
+    x, Wq, sc, zp, b, t, tb = _targeted_epilogue_case(orc, targets, seed=71)
+    y, bound = orc.w4_matmul_ep(x, Wq, sc, zp, b, None, act="gelu")
+    tight = 0
+    for m in range(M):
+        for n in range(N):
+            o = _gelu64(t[m, n])
+            dev_max = max(abs(_gelu64(tp) - o) for tp in np.linspace(t[m, n] - tb[m, n],
+                                                                     t[m, n] + tb[m, n], 41))
+            need = dev_max + eval_allow(t[m, n], o)
+            assert bound[m, n] >= need, ("gelu bound too small", m, n, bound[m, n], need)
+            if m < 4 and tb[m, n] > 2.0 ** -13 * (abs(t[m, n]) + abs(o)):
+                assert bound[m, n] <= 1.05 * dev_max + 2.0 ** -17 * (abs(t[m, n]) + abs(o)), \
+                    ("gelu bound too loose", m, n, bound[m, n], dev_max)
+                tight += 1
+    assert tight >= 12  # the steep-point rows were reached
+    # ---- SwiGLU: gate near SiLU's steepest point, large up values; and spread
+    v_ss = max(np.arange(0.0, 6.0, 1e-3), key=lambda a: abs(_silu64(a + 1e-6) - _silu64(a - 1e-6)))
+    M, N = 12, 8
+    targets = np.empty((M, N))
+    targets[:, 0::2] = v_ss
+    targets[:, 1::2] = np.where(np.arange(M)[:, None] % 2 == 0, 12.0, -9.0)
+    targets[6:, 0::2] = np.linspace(-8.0, 8.0, 6 * (N // 2)).reshape(6, N // 2)
+    x, Wq, sc, zp, b, t, tb = _targeted_epilogue_case(orc, targets, seed=72)
+    y, bound = orc.w4_matmul_ep(x, Wq, sc, zp, b, None, act="swiglu")
+    tight = 0
+    for m in range(M):
+        for i in range(N // 2):
+            gt, ut, gb, ub = t[m, 2 * i], t[m, 2 * i + 1], tb[m, 2 * i], tb[m, 2 * i + 1]
+            o = _silu64(gt) * ut
+            dev_max = max(abs(_silu64(gp) * up - o)
+                          for gp in np.linspace(gt - gb, gt + gb, 17)
+                          for up in np.linspace(ut - ub, ut + ub, 9))
+            need = dev_max + eval_allow(gt * ut, o)
+            assert bound[m, i] >= need, ("swiglu bound too small", m, i, bound[m, i], need)
+            if m < 6 and gb * abs(ut) > 2.0 ** -13 * (abs(gt * ut) + abs(o)):
+                assert bound[m, i] <= 1.05 * dev_max + 2.0 ** -17 * (abs(gt * ut) + abs(o)), \
+                    ("swiglu bound too loose", m, i, bound[m, i], dev_max)
+                tight += 1
+    assert tight >= 12
+
+
 # --------------------------------------------------------------------------
 # group-64 affine variant
 # --------------------------------------------------------------------------
@@ -815,6 +924,7 @@ ALL_PINS = [
     pin_g64_dequant_and_matmul,
     pin_activations,
     pin_epilogue_matmul,
+    pin_epilogue_bound,
     pin_f16_conversion,
     pin_f16_quantizer,
     pin_f16_degenerate_and_errors,

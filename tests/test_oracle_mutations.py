@@ -48,6 +48,18 @@ MUTATIONS = {
     "swiglu_pair_swapped": (
         "const double g = t[2 * i], u = t[2 * i + 1], sg = orc_silu(g);",
         "const double g = t[2 * i + 1], u = t[2 * i], sg = orc_silu(g);"),
+    "gelu_bound_slope_loose": (
+        "b = 1.13 * tb[i] + ldexp(fabs(t[i]) + fabs(o), -20);",
+        "b = 11.3 * tb[i] + ldexp(fabs(t[i]) + fabs(o), -20);"),
+    "gelu_bound_slope_too_small": (
+        "b = 1.13 * tb[i] + ldexp(fabs(t[i]) + fabs(o), -20);",
+        "b = 0.9 * tb[i] + ldexp(fabs(t[i]) + fabs(o), -20);"),
+    "swiglu_bound_drops_gate_error": (
+        "b = 1.1 * fabs(u) * tb[2 * i] + fabs(sg) * tb[2 * i + 1] +",
+        "b = fabs(sg) * tb[2 * i + 1] +"),
+    "swiglu_bound_slope_loose": (
+        "b = 1.1 * fabs(u) * tb[2 * i] + fabs(sg) * tb[2 * i + 1] +",
+        "b = 11.0 * fabs(u) * tb[2 * i] + fabs(sg) * tb[2 * i + 1] +"),
     "epilogue_residual_before_act": (
         "                o = orc_gelu(t[i]);",
         "                o = orc_gelu(t[i] + (residual ? (double)residual[m * nout + i] : 0.0));"),
