@@ -34,9 +34,12 @@
  *     enqueues nothing.  W4_ERR_LAUNCH carries the HIP error of the launch.
  *   - Sizes are int64_t.  Empty sizes are valid: M == 0 or N == 0 enqueue
  *     nothing; K == 0 makes every output equal to the bias (or 0).
- *   - Pointers are device pointers (16-byte aligned for Wq, scales, zeros and
- *     the head table Q; 4-byte aligned for fp32 arrays).  A pointer may be NULL
- *     only when the buffer it names is empty, or where marked "may be NULL".
+ *   - Pointers are device pointers: 16-byte aligned for Wq, scales, zeros,
+ *     the head tables Q and Qt and the activations x of every matmul (read
+ *     in 16-byte pieces); 4-byte aligned for the other fp32 arrays (bias, y,
+ *     residual, hs, logits).  Each head call states its own rule for x.  A
+ *     pointer may be NULL only when the buffer it names is empty, or where
+ *     marked "may be NULL".
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Calls only enqueue work on it: they never synchronize, and never
  *     allocate device memory.  Scratch memory is the caller's `workspace`.
@@ -147,18 +150,14 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
 /* y = x . w_hat + bias on the K-major layout: same result contract as
  * w4_matmul (fp32, same bound, deterministic).  For M <= 2 (decode), and
  * for any M when K % 128 != 0, every workgroup owns whole columns and no
- * workspace is used.  For M >= 3 with K % 128 == 0 (small batches, prefill)
- * the product runs on the matrix cores at fp32 accuracy, each block's scale
- * applied once per block and the block sums fp32.  M > 16: (q - z) is exact
- * in bf16 and each activation is split exactly into three bf16 terms, so
- * every product is exact.  3 <= M <= 16: (q - z) is exact in fp16 and each
- * row of x, scaled by its own power of two over every K range of at most
- * 512, is split into three fp16 terms that carry it to within
- * 2^-33 |x| + 2^-39 max|x| (max over that row and range): inside the bound
- * unless a row's largest activation in a range exceeds about 5 * 10^6 times
- * the row's |w|-weighted average there.  Non-finite x gives NaN outputs on
- * both.  That path may split K across
- * workgroups and then needs a workspace of
+ * workspace is used.  For M >= 3 with K % 128 == 0 and K < 2^22 (small
+ * batches, prefill) the product runs on the matrix cores at fp32 accuracy
+ * with exact operands: within a block the scale factors out, (q - z) is
+ * exact in bf16, and each activation is split exactly into three bf16
+ * terms, so every product is exact and only the fp32 accumulation rounds;
+ * the block's scale is applied once per block and column.  This holds for
+ * any finite x, whatever its range.  Non-finite x gives NaN outputs on this
+ * path.  It may split K across workgroups and then needs a workspace of
  * w4_matmul_kmajor_workspace_bytes(M, K, N) bytes (0 when it does not):
  * device memory, 256-byte aligned, any contents, not shared with a call in
  * flight on another stream.  Indexing is 32-bit: K * N, M * K and M * N must
@@ -314,27 +313,22 @@ int i8_check_head_logits_kmajor_args(const float *x_last, int64_t K, const int8_
                                      int64_t ldt, const float *hs, int64_t N,
                                      const float *logits);
 
-/* Last-token logits on the integer matrix cores, one launch, no workspace:
- * logits[n] = hs[n] * sum_k x_last[k] * Qt[n, k].  K % 64 == 0, K <= 8192.
- * The table products are exact; x_last enters as a 31-bit fixed-point value
- * relative to 2^e, e the exponent of max|x_last|, so each activation carries
- * an absolute error of at most 2^-30 max|x_last| and the result is within the
- * bound of w4_matmul for activations whose largest entry is not more than
- * about 10^4 times their |Q|-weighted average.  Non-finite x_last gives NaN
- * logits.  x_last, Qt 16-byte aligned; hs, logits 4-byte aligned.           */
+/* Last-token logits: logits[n] = hs[n] * sum_k x_last[k] * Qt[n, k], one
+ * launch, no workspace.  K % 16 == 0, 16 <= K <= 8192.  fp32 arithmetic with
+ * every product formed exactly from the int8 code and the fp32 activation, so
+ * every logit is within the bound of w4_matmul for any finite x_last (nothing
+ * of x is quantized).  A non-finite entry of x_last gives NaN logits.
+ * x_last, Qt 16-byte aligned; hs, logits 4-byte aligned.                   */
 int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int64_t ldt,
                           const float *hs, int64_t N, float *logits, void *stream);
 
 /* Full-sequence logits (the page's export before the last-position slice of
  * step 4): logits[m, n] = hs[n] * sum_k x[m, k] * Qt[n, k] for every row m of
- * x [M, K] (fp32, row-major, 4-byte aligned), logits [M, N] fp32.  Same
- * arithmetic and precision condition as i8_head_logits_kmajor, with one
- * exponent per row.  K % 64 == 0, K <= 2048; N * ldt < 2^31.  Two launches:
- * the int8 digit image of x is written once to the workspace (caller-owned,
- * device memory, 256-byte aligned, at least i8_head_rows_workspace_bytes(M,
- * K) bytes: 16 K bytes per group of 4 rows plus 4 bytes per row; contents on
- * entry do not matter and are overwritten), then the table is streamed once
- * past all rows.  Missing or short workspace: W4_ERR_WORKSPACE.            */
+ * x [M, K] (fp32, row-major, 16-byte aligned), logits [M, N] fp32.  Same
+ * arithmetic and bound as i8_head_logits_kmajor (a row with a non-finite
+ * entry gives NaN logits for that row only).  K % 16 == 0, 16 <= K <= 8192;
+ * N * ldt < 2^31.  One launch; no workspace is needed:
+ * i8_head_rows_workspace_bytes returns 0 and `workspace` may be NULL.      */
 size_t i8_head_rows_workspace_bytes(int64_t M, int64_t K);
 
 int i8_check_head_logits_rows_args(const float *x, int64_t M, int64_t K, const int8_t *Qt,

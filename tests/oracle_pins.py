@@ -724,6 +724,7 @@ def _targeted_epilogue_case(orc, targets, seed):
         W[8 * n:8 * n + 8, n] = g.standard_normal(8).astype(np.float32)
     Wq, sc, zp = orc.quantize_pack(W)
     What = orc.dequantize(Wq, sc, zp, K, N)
+    assert np.all(np.isfinite(What)) and all(np.any(What[8 * n:8 * n + 8, n]) for n in range(N))
     b = (g.standard_normal(N) * 0.5).astype(np.float32)
     x = (g.standard_normal((M, K)) * 60.0).astype(np.float32)
     for m in range(M):
@@ -732,6 +733,7 @@ def _targeted_epilogue_case(orc, targets, seed):
             j = int(np.argmax(np.abs(w)))
             rest = sum(float(x[m, 8 * n + i]) * w[i] for i in range(8) if i != j)
             x[m, 8 * n + j] = np.float32((targets[m, n] - float(b[n]) - rest) / w[j])
+    assert np.all(np.isfinite(x))
     t = np.empty((M, N))
     tb = np.empty((M, N))
     for m in range(M):

@@ -167,7 +167,9 @@ def test_head_kmajor_checks():
     assert check_headk(768, 50257) == w4.W4_OK
     assert check_headk(768, 50257, ldt=784) == w4.W4_OK
     assert check_headk(8192, 1000) == w4.W4_OK
-    assert check_headk(800, 10) == w4.W4_ERR_BAD_SHAPE          # K % 64 != 0
+    assert check_headk(808, 10) == w4.W4_ERR_BAD_SHAPE          # K % 16 != 0
+    assert check_headk(800, 10, ldt=800) == w4.W4_OK            # K % 16 == 0 is enough
+    assert check_headk(0, 10) == w4.W4_ERR_BAD_SHAPE
     assert check_headk(8256, 10) == w4.W4_ERR_BAD_SHAPE         # K > 8192
     assert check_headk(768, 10, ldt=776) == w4.W4_ERR_BAD_SHAPE  # ldt % 16 != 0
     assert check_headk(768, 10, ldt=704) == w4.W4_ERR_BAD_SHAPE  # ldt < K
@@ -190,24 +192,21 @@ def test_head_kmajor_checks():
 def test_head_rows_checks():
     lib = w4.library()
     chk = lib.i8_check_head_logits_rows_args
-    need = lib.i8_head_rows_workspace_bytes(58, 768)
-    # 15 groups of 4 rows x 16 K bytes, rounded to 256, then one int per row
-    assert need == (15 * 16 * 768 + 255) // 256 * 256 + 4 * 58
+    # the full-sequence head needs no workspace
+    assert lib.i8_head_rows_workspace_bytes(58, 768) == 0
     assert lib.i8_head_rows_workspace_bytes(0, 768) == 0
-    W = A
-    assert chk(A, 58, 768, A, 768, A, 50257, A, W, need) == w4.W4_OK
-    assert chk(A, 58, 768, A, 768, A, 50257, A, W, need - 1) == w4.W4_ERR_WORKSPACE
-    assert chk(A, 58, 768, A, 768, A, 50257, A, None, need) == w4.W4_ERR_WORKSPACE
-    assert chk(A, 58, 768, A, 768, A, 50257, A, W + 16, need) == w4.W4_ERR_MISALIGNED
-    assert chk(A, 58, 4096, A, 4096, A, 100, A, W, 1 << 30) == w4.W4_ERR_BAD_SHAPE  # K > 2048
-    assert chk(A, 58, 800, A, 800, A, 100, A, W, 1 << 30) == w4.W4_ERR_BAD_SHAPE    # K % 64 != 0
-    assert chk(A, -1, 768, A, 768, A, 100, A, W, 1 << 30) == w4.W4_ERR_BAD_SHAPE
+    assert chk(A, 58, 768, A, 768, A, 50257, A, None, 0) == w4.W4_OK
+    assert chk(A, 58, 768, A, 768, A, 50257, A, A, 12345) == w4.W4_OK  # a workspace is ignored
+    assert chk(A, 58, 8192, A, 8192, A, 100, A, None, 0) == w4.W4_OK
+    assert chk(A, 58, 8208, A, 8208, A, 100, A, None, 0) == w4.W4_ERR_BAD_SHAPE  # K > 8192
+    assert chk(A, 58, 808, A, 816, A, 100, A, None, 0) == w4.W4_ERR_BAD_SHAPE    # K % 16 != 0
+    assert chk(A, -1, 768, A, 768, A, 100, A, None, 0) == w4.W4_ERR_BAD_SHAPE
     assert chk(None, 0, 768, None, 768, None, 100, None, None, 0) == w4.W4_OK
-    assert chk(A, 2, 768, None, 768, A, 100, A, W, need) == w4.W4_ERR_NULL_PTR
-    assert chk(A + 2, 2, 768, A, 768, A, 100, A, W, need) == w4.W4_ERR_MISALIGNED
-    assert chk(A, 2, 768, A + 8, 768, A, 100, A, W, need) == w4.W4_ERR_MISALIGNED
+    assert chk(A, 2, 768, None, 768, A, 100, A, None, 0) == w4.W4_ERR_NULL_PTR
+    assert chk(A + 4, 2, 768, A, 768, A, 100, A, None, 0) == w4.W4_ERR_MISALIGNED  # x 16-byte
+    assert chk(A, 2, 768, A + 8, 768, A, 100, A, None, 0) == w4.W4_ERR_MISALIGNED
     if NO_GPU:
-        assert lib.i8_head_logits_rows(A, 2, 768, A, 768, A, 100, A, W, need, None) == \
+        assert lib.i8_head_logits_rows(A, 2, 768, A, 768, A, 100, A, None, 0, None) == \
             w4.W4_ERR_DEVICE
 
 

@@ -343,7 +343,8 @@ def head_kmajor_case(K, N, ldt, x, label):
 
 @pytest.mark.parametrize("K,N,ldt", [(768, 50257, 768), (768, 50257, 784), (64, 300, 64),
                                      (128, 37, 144), (256, 1000, 256), (512, 77, 512),
-                                     (1024, 515, 1024), (2048, 130, 2048), (8192, 70, 8192)])
+                                     (1024, 515, 1024), (2048, 130, 2048), (8192, 70, 8192),
+                                     (48, 100, 48), (784, 333, 800), (1040, 65, 1040)])
 def test_head_kmajor(K, N, ldt):
     note(f"head kmajor K={K} N={N} ldt={ldt}")
     cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 223
@@ -369,6 +370,27 @@ def test_head_kmajor_special_inputs():
         head_kmajor_case(K, N, K, x.astype(np.float32), f"head kmajor x={name}")
 
 
+@pytest.mark.parametrize("factor", [1e5, 1e7, 1e12])
+def test_head_kmajor_isolated_outlier(factor):
+    """One activation far above the rest of its 64-value segment, on a code
+    row that is zero for many tokens: the rest keeps its own precision."""
+    K, N = 768, 3000
+    E = synth.head_table(K, N, cfg=231)
+    E[100, : N // 2] = 0.0
+    Q, hs = ORC.i8_quantize_head(E, ldq=N)
+    x = synth.activations(1, K, cfg=231)[0]
+    x[100] *= np.float32(factor)
+    logits = host(w4.i8_head_logits_kmajor(dev(x), dev(token_major(Q, N, K)), dev(hs), K))
+    ref, bound = ORC.i8_head_logits(x, Q, hs)
+    assert_bound(logits, ref, bound, f"head kmajor outlier x{factor:g}")
+    xs = synth.activations(5, K, cfg=232)
+    xs[:, 100] *= np.float32(factor)
+    got = host(w4.i8_head_logits_rows(dev(xs), dev(token_major(Q, N, K)), dev(hs)))
+    for m in range(5):
+        ref, bound = ORC.i8_head_logits(xs[m], Q, hs)
+        assert_bound(got[m], ref, bound, f"head rows outlier x{factor:g} row {m}")
+
+
 def test_head_kmajor_nonfinite_gives_nan():
     K, N = 128, 50
     Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=228), ldq=N)
@@ -380,7 +402,9 @@ def test_head_kmajor_nonfinite_gives_nan():
 
 @pytest.mark.parametrize("M,K,N,ldt", [(58, 768, 50257, 768), (1, 768, 50257, 784), (3, 768, 4099, 768),
                                        (5, 64, 300, 64), (9, 128, 37, 144), (6, 2048, 130, 2048),
-                                       (17, 512, 1000, 512), (4, 1024, 515, 1024)])
+                                       (17, 512, 1000, 512), (4, 1024, 515, 1024),
+                                       (130, 64, 500, 64), (65, 64, 300, 64), (33, 48, 70, 48),
+                                       (3, 4096, 90, 4096)])
 def test_head_rows(M, K, N, ldt):
     """Full-sequence logits: every row of x against the oracle's head."""
     note(f"head rows M={M} K={K} N={N} ldt={ldt}")
@@ -445,8 +469,8 @@ def test_prepack_kmajor_bit_exact(K, N):
 # (3072, 3080): every lane owns one block and the matrix fills the chip, so
 # M = 1 and 2 take the whole-run activation loads, with a ragged last
 # workgroup (3080 is not a multiple of the 12 columns per workgroup)
-KMAJOR_SHAPES = [(64, 16), (768, 768), (768, 2304), (3072, 768), (1024, 1008), (192, 530),
-                 (8192, 512), (128, 2), (4096, 4112), (320, 96), (3072, 3080)]
+KMAJOR_SHAPES = [(64, 16), (768, 768), (768, 2304), (768, 3072), (3072, 768), (1024, 1008),
+                 (192, 530), (8192, 512), (128, 2), (4096, 4112), (320, 96), (3072, 3080)]
 
 
 @pytest.mark.parametrize("K,N", KMAJOR_SHAPES)
@@ -463,8 +487,8 @@ def test_kmajor_matmul(M, K, N):
     assert_bound(y, y_ref, bound, f"kmajor M={M} {K}x{N}")
 
 
-X3_SHAPES = [(128, 16), (768, 768), (768, 2304), (3072, 768), (1024, 1008), (256, 530),
-             (8192, 512), (128, 2), (640, 4112), (384, 96), (3072, 3072)]
+X3_SHAPES = [(128, 16), (768, 768), (768, 2304), (768, 3072), (3072, 768), (1024, 1008),
+             (256, 530), (8192, 512), (128, 2), (640, 4112), (384, 96), (3072, 3072)]
 
 
 @pytest.mark.parametrize("K,N", X3_SHAPES)
@@ -552,6 +576,45 @@ def test_kmajor_matrix_cores_special_inputs():
         y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
         y = host(w4.w4_matmul_kmajor(dev(x), *P))
         assert_bound(y, y_ref, bound, f"kmajor x3 x={name}")
+
+
+@pytest.mark.parametrize("M", [3, 4, 16, 17, 58])
+@pytest.mark.parametrize("factor", [1e5, 1e7, 1e12])
+def test_kmajor_matrix_cores_isolated_outlier(M, factor):
+    """One activation far above the rest of its 512-wide K range, sitting on
+    a row of zero weights (q = z, so it adds nothing to the bound): every
+    other product must keep its own precision."""
+    K, N = 1024, 768
+    note(f"kmajor outlier M={M} factor={factor:g}")
+    W = mixed_weights(K, N, cfg=239)
+    W[300, :] = 0.0
+    W[700, 5:] = 0.0
+    x = synth.activations(M, K, cfg=239, slot=M)
+    x[:, 300] *= np.float32(factor)
+    x[M // 2, 700] = np.float32(factor)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P))
+    assert_bound(y, y_ref, bound, f"kmajor outlier x{factor:g} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 58])
+def test_large_scales_do_not_overflow(M):
+    """Weights near 1e33 (block scales above 2^104) on every matmul path."""
+    K, N = 768, 512
+    note(f"large scales M={M}")
+    W = synth.weights(K, N, cfg=240) * np.float32(5e34)
+    assert np.all(np.isfinite(W))
+    x = synth.activations(M, K, cfg=240, slot=M)
+    Wq, s, z = ORC.quantize_pack(W)
+    assert float(np.max(s)) > 2.0 ** 104
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    assert np.all(np.isfinite(y_ref))
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    assert_bound(host(w4.w4_matmul_kmajor(dev(x), *P)), y_ref, bound, f"large scales kmajor M={M}")
+    assert_bound(host(w4.w4_matmul(dev(x), dev(Wq), dev(s), dev(z))), y_ref, bound,
+                 f"large scales canonical M={M}")
 
 
 def test_kmajor_matrix_cores_deterministic_with_dirty_workspace():

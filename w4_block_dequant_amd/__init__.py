@@ -127,10 +127,11 @@ def _stream(device) -> int:
 
 
 class Workspace:
-    """Device scratch for the split-K partial sums and the head's digit image,
-    grown on demand.
+    """Device scratch for split-K partial sums, grown on demand.
 
-    One buffer per device serves every call ordered on the same stream.  A
+    One buffer per (device, stream): calls on one stream run in order, so
+    they can share it, and a call on another stream gets a buffer of its own
+    (two streams sharing one buffer would race on the partial sums).  A
     buffer that is outgrown is kept alive, not freed: a HIP graph captured
     with it still names its address, and freeing it would let the caching
     allocator hand that memory to another tensor under the graph.
@@ -144,7 +145,7 @@ class Workspace:
     def get(self, device, nbytes: int):
         if nbytes == 0:
             return None, 0
-        key = torch.device(device).index
+        key = (torch.device(device).index, _stream(device))
         with self._lock:
             buf = self._buf.get(key)
             if buf is None or buf.numel() < nbytes:
@@ -413,8 +414,8 @@ def i8_head_logits_rows(x: torch.Tensor, Qt: torch.Tensor, hs: torch.Tensor,
                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """x fp32 [M, K] -> logits fp32 [M, N] for every row (token-major table Qt [N, ldt]).
 
-    `workspace`: uint8, at least i8_head_rows_workspace_bytes(M, K) bytes (the
-    digit image of x); the shared per-device scratch when not given."""
+    `workspace`: optional uint8 tensor (the head needs none:
+    i8_head_rows_workspace_bytes returns 0)."""
     _dev(x, torch.float32, "x")
     _dev(Qt, torch.int8, "Qt")
     _dev(hs, torch.float32, "hs")

@@ -438,7 +438,7 @@ int i8_prepack_head(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *
 int i8_check_head_logits_kmajor_args(const float *x_last, int64_t K, const int8_t *Qt,
                                      int64_t ldt, const float *hs, int64_t N,
                                      const float *logits) {
-    if (K < 64 || K % 64 != 0 || K > 8192 || N < 0 || ldt < K || ldt % 16 != 0)
+    if (K < 16 || K % 16 != 0 || K > 8192 || N < 0 || ldt < K || ldt % 16 != 0)
         return W4_ERR_BAD_SHAPE;
     if (N > 0 && N > ((int64_t)1 << 31) / ldt - 1) return W4_ERR_BAD_SHAPE;
     if (N == 0) return W4_OK;
@@ -466,19 +466,16 @@ size_t i8_head_rows_workspace_bytes(int64_t M, int64_t K) {
 int i8_check_head_logits_rows_args(const float *x, int64_t M, int64_t K, const int8_t *Qt,
                                    int64_t ldt, const float *hs, int64_t N, const float *logits,
                                    const void *workspace, size_t workspace_bytes) {
-    if (M < 0 || K < 64 || K % 64 != 0 || K > 2048 || N < 0 || ldt < K || ldt % 16 != 0)
+    (void)workspace;
+    (void)workspace_bytes;
+    if (M < 0 || K < 16 || K % 16 != 0 || K > 8192 || N < 0 || ldt < K || ldt % 16 != 0)
         return W4_ERR_BAD_SHAPE;
     if (N > 0 && N > ((int64_t)1 << 31) / ldt - 1) return W4_ERR_BAD_SHAPE;
-    if (M > 0 && (M > ((int64_t)1 << 31) / K - 1 || M > kMaxElems / (N > 0 ? N : 1) ||
-                  (M + 3) / 4 > ((int64_t)1 << 31) / (16 * K) - 1))
-        return W4_ERR_BAD_SHAPE;
+    if (M > 0 && (M > kMaxElems / K || M > kMaxElems / (N > 0 ? N : 1))) return W4_ERR_BAD_SHAPE;
     if (M == 0 || N == 0) return W4_OK;
     if (!x || !Qt || !hs || !logits) return W4_ERR_NULL_PTR;
-    if (!aligned(x, 4) || !aligned(Qt, 16) || !aligned(hs, 4) || !aligned(logits, 4))
+    if (!aligned(x, 16) || !aligned(Qt, 16) || !aligned(hs, 4) || !aligned(logits, 4))
         return W4_ERR_MISALIGNED;
-    if (workspace == nullptr || workspace_bytes < w4::head_rows_workspace(M, K))
-        return W4_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return W4_ERR_MISALIGNED;
     return W4_OK;
 }
 

@@ -231,7 +231,8 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     // on three shapes of four).
     static const int64_t env_min = env_int("W4_X3_MIN_ROWS");
     const int64_t min_rows = env_min >= 2 ? env_min : 3;
-    if (M < min_rows || K <= 0 || N <= 0 || K % 128 != 0) return p;
+    // K < 2^22: activation offsets within a row group stay below 2^32 bytes
+    if (M < min_rows || K <= 0 || N <= 0 || K % 128 != 0 || K >= ((int64_t)1 << 22)) return p;
     p.kind = X3Plan::kRun;
     const int64_t rows = M < 64 ? M : 64;
     p.mt = (int)cdiv(rows, 16);
@@ -254,18 +255,12 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     p.mgroups = cdiv(M, 16 * p.mt);
     p.npad = p.col_wgs * 64 * p.nt;
     const int64_t NQ = K / 128;
-    // M <= 16 (one 16-row tile): the fp16 kernel, which builds all of its A
-    // operands before the first quad (3.8B layer at M = 4: 62 -> 55 us; at
-    // M = 16: 70 -> 62 us; at M = 58 the bf16 kernel stays ahead)
-    static const int64_t env_bf16 = env_int("W4_X3_BF16");
-    p.h3 = p.mt == 1 && p.nt == 1 && p.mgroups == 1 && env_bf16 != 1;
     // enough workgroups to fill the chip; larger row tiles carry more matrix
     // work per weight byte, so fewer (and less split-K partial traffic)
     static const int64_t env_wgs = env_int("W4_X3_TARGET_WGS");
-    // bf16: about four workgroups per compute unit, measured best at M = 16
-    // and 58 on the 3.8B shapes (the extra split-K partials cost less than
-    // idle CUs); fp16 (its workgroups hold up to 52 KB of LDS): about two
-    const int64_t target = env_wgs > 0 ? env_wgs : (p.h3 ? 512 : 1024);
+    // about four workgroups per compute unit, measured best at M = 16 and 58
+    // on the 3.8B shapes (the extra split-K partials cost less than idle CUs)
+    const int64_t target = env_wgs > 0 ? env_wgs : 1024;
     int64_t splits = cdiv(target, p.col_wgs * p.mgroups);
     // No split when the matrix already forms half a chip of workgroups and
     // each one's K loop is short (K <= 1024): the split-K reduce is a second
@@ -274,7 +269,7 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     if (env_wgs <= 0 && p.col_wgs * p.mgroups >= 128 && NQ <= 8) splits = 1;
     if (splits > NQ) splits = NQ;
     if (splits < 1) splits = 1;
-    const int64_t qmax = p.h3 ? 4 : 12;
+    const int64_t qmax = 12;
     const int64_t want = cdiv(NQ, splits);  // quads per workgroup, then the largest
     static const int allowed[] = {12, 8, 6, 4, 3, 2, 1};  // instantiated count <= want
     p.quads_per_wg = 1;
@@ -286,14 +281,6 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     p.splits = cdiv(NQ, p.quads_per_wg);
     p.workspace = splitk_bytes(p.splits, p.npad, M);
     return p;
-}
-
-int plan_head_kmajor_waves(int64_t K, int64_t N) {
-    (void)N;
-    static const int64_t env_w = env_int("W4_HEAD_MFMA_WAVES");
-    if (K > 1024) return 4;
-    if (env_w == 1 || env_w == 2 || env_w == 4) return (int)env_w;
-    return 4;
 }
 
 }  // namespace w4

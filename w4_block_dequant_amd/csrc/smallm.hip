@@ -9,8 +9,8 @@
 // A workgroup (4 waves) owns a 256-column tile and a range of K-blocks.  Per
 // 32-row block every thread loads 4 rows x 8 columns of packed codes (rows of
 // 128 contiguous bytes across 32 threads), dequantizes them exactly --
-// (q - z) as an fp16-subnormal pair, times scale * 2^24 in one v_fma_mix,
-// i.e. fl32((q - z) * scale), the same value the oracle forms -- and stores
+// (q - z) as an fp16-subnormal pair, widened to the exact integer, times the
+// scale: fl32((q - z) * scale), the same value the oracle forms -- and stores
 // the fp32 tile in one of two LDS buffers.  After one barrier each wave runs
 // its 64 columns (4 MFMA n-tiles) against up to 4 MFMA m-tiles of X, reading
 // its B operands with ds_read_b128, while the next block's loads are in
@@ -105,18 +105,21 @@ __global__ __launch_bounds__(256) void k_mm_mfma(
         f32x4_t o[4][2];
         const NibblePairs zp = nibble_pairs(R.z);
         const bool on = live && lok;
-        float su[8];  // scale * 2^24 or 2^20 (0 for columns past N or a dead step)
+        float su[8];  // the scale (0 for columns past N or a dead step)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) su[j] = on ? R.s[j >> 2][j & 3] * nibble_unscale(j) : 0.0f;
+        for (int j = 0; j < 8; ++j) su[j] = on ? R.s[j >> 2][j & 3] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const NibblePairs qp = nibble_pairs(R.w[r]);
             float w[8];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                // (q - z) first (exact: a small integer), then the one rounding
+                // of fl32((q - z) * scale); scaling the scale by 2^24 instead
+                // would overflow for scales of 2^104 and up
                 const half2_t d = qp.p[m] - zp.p[m];
-                w[m] = (float)d.x * su[m];
-                w[m + 4] = (float)d.y * su[m + 4];
+                w[m] = ((float)d.x * nibble_unscale(m)) * su[m];
+                w[m + 4] = ((float)d.y * nibble_unscale(m + 4)) * su[m + 4];
             }
             o[r][0] = f32x4_t{w[0], w[1], w[2], w[3]};
             o[r][1] = f32x4_t{w[4], w[5], w[6], w[7]};
