@@ -127,6 +127,23 @@ int w4_matmul(const float *x, int64_t M, int64_t K,
               const float *bias, float *y,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* w4_matmul for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and result, but split-K partial sums go to a device array that the
+ * library holds for the life of the process, W4_NOALLOC_SCRATCH_BYTES bytes
+ * on each GPU it runs on.  A shape whose w4_matmul_workspace_bytes exceeds
+ * that gives W4_ERR_WORKSPACE (checked on the host, nothing enqueued).  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (the kernels never need it cleared):
+ * calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race on it and must be ordered by the caller.  The first
+ * call on a device looks up that device's array (a HIP symbol query).    */
+#define W4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int w4_matmul_noalloc(const float *x, int64_t M, int64_t K,
+                      const uint8_t *Wq, const float *scales, const uint8_t *zeros, int64_t N,
+                      const float *bias, float *y, void *stream);
+
 /* Argument check of w4_matmul without any HIP call (same return codes,
  * minus W4_ERR_DEVICE / W4_ERR_LAUNCH); usable on a machine with no GPU.   */
 int w4_check_matmul_args(const float *x, int64_t M, int64_t K,

@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
                  "w4g_check_matmul_kmajor_args", "w4g_matmul_kmajor",
                  "w4_check_matmul_kmajor_ep_args",
                  "w4h_quantize_pack", "w4h_dequantize", "w4h_prepack_kmajor",
-                 "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args"):
+                 "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args", "w4_matmul_noalloc"):
         assert must in names
 
 
@@ -155,6 +155,20 @@ def test_entry_points_reject_before_any_hip_call():
     # empty work succeeds without a device
     assert lib.w4_matmul(None, 0, 768, None, None, None, 768, None, None, None, 0, None) == w4.W4_OK
     assert lib.i8_embed(None, 0, None, 10, None, 768, 10, None, None, None) == w4.W4_OK
+
+
+def test_noalloc_host_checks():
+    lib = w4.library()
+    f = lib.w4_matmul_noalloc
+    # a shape whose split-K partials exceed the library's scratch: refused on the host
+    assert w4.w4_matmul_workspace_bytes(64, 8192, 3072) > w4.NOALLOC_SCRATCH_BYTES
+    assert f(A, 64, 8192, A, A, A, 3072, None, A, None) == w4.W4_ERR_WORKSPACE
+    assert f(A, 1, 100, A, A, A, 64, None, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert f(A + 4, 1, 768, A, A, A, 768, None, A, None) == w4.W4_ERR_MISALIGNED
+    assert f(None, 1, 768, A, A, A, 768, None, A, None) == w4.W4_ERR_NULL_PTR
+    assert f(None, 0, 768, None, None, None, 768, None, None, None) == w4.W4_OK
+    if NO_GPU:
+        assert f(A, 58, 3072, A, A, A, 3072, None, A, None) == w4.W4_ERR_DEVICE
 
 
 def check_headk(K, N, ldt=None, x=A, Qt=A, hs=A, out=A):

@@ -44,6 +44,7 @@ _SIGS = {
     "w4_matmul_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w4_matmul": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "w4_check_matmul_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
+    "w4_matmul_noalloc": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
     "w4_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
     "w4_matmul_kmajor_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w4_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
@@ -228,6 +229,34 @@ def w4_matmul(x: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, zeros: to
     _check("w4_matmul", _lib.w4_matmul(_ptr(x), M, K, _ptr(Wq), _ptr(scales), _ptr(zeros), N,
                                        _ptr(bias), _ptr(out), _ptr(ws), wsb,
                                        _stream(x.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def w4_matmul_noalloc(x: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor,
+                      zeros: torch.Tensor, bias: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None):
+    """w4_matmul through the allocation-free entry point (the library's own
+    per-GPU scratch; calls on one GPU must not overlap)."""
+    _dev(x, torch.float32, "x")
+    _dev(Wq, torch.uint8, "Wq")
+    _dev(scales, torch.float32, "scales")
+    _dev(zeros, torch.uint8, "zeros")
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+    M, K = x.shape
+    N = scales.shape[1]
+    if Wq.shape != (K, N // 2):
+        raise ValueError(f"Wq shape {tuple(Wq.shape)} does not match K={K}, N={N}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, torch.float32, "out")
+    _check("w4_matmul_noalloc", _lib.w4_matmul_noalloc(
+        _ptr(x), M, K, _ptr(Wq), _ptr(scales), _ptr(zeros), N, _ptr(bias), _ptr(out),
+        _stream(x.device)))
     return out
 
 
