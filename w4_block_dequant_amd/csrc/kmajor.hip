@@ -18,8 +18,11 @@
 // column contiguously.  Per packed word: 1 shift, 4 masks, 4 packed-fp16
 // subtractions (q - z as exact fp16 subnormals) and 8 v_fma_mix_f32.  The
 // per-lane block sums are scaled, then summed over the column's lanes in a
-// fixed order: through LDS, a few lanes per output each adding a contiguous
-// run, then two lane exchanges.  Results are deterministic.
+// fixed order: where every 32-lane half of a wave lies in one column slot
+// (K a multiple of 1024), each half adds its lanes in registers (DPP) and one
+// value per half crosses LDS; otherwise all lane partials go through LDS, a
+// few lanes per output each adding a contiguous run, then two lane
+// exchanges.  Results are deterministic.
 #include <type_traits>
 
 #include "common.h"
@@ -66,6 +69,24 @@ __global__ __launch_bounds__(256) void k_prepack_blocks(const void *__restrict__
     Ps[(2 * j) * NB + b1] = scales[b1 * N + 2 * j];
     Ps[(2 * j + 1) * NB + b0] = scales[b0 * N + 2 * j + 1];
     Ps[(2 * j + 1) * NB + b1] = scales[b1 * N + 2 * j + 1];
+}
+
+// Sum of v over each 32-lane half of the wave, in DPP steps (no LDS): pairs,
+// quads, rotations by 4 and 8 within each 16-lane row, then row 0 (2) into
+// row 1 (3).  The sums are valid in lanes 31 and 63; the order of the
+// additions is fixed, so the result does not depend on timing.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                   0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float sum32(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+    v = dpp_add<0x128, 0xF>(v);  // row_ror:8
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    return v;
 }
 
 // acc[r] += x_r[k] * (q[k] - z) over the 16 codes k = 16h .. 16h+15 of two
@@ -125,7 +146,7 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // of one block per lane do not collide) then hands every lane its own
 // block.  A lane's own block's 128 bytes would otherwise come from 8 loads
 // that each touch 64 different cache lines.
-template <int MR, int P, bool CHECK, bool LOOP, bool H, bool EP, bool AFF = false,
+template <int MR, int P, bool CHECK, int LM, bool H, bool EP, bool AFF = false,
           bool XC = false>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, const uint8_t *__restrict__ Pq, const void *__restrict__ Ps,
@@ -146,8 +167,8 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         for (int p = 0; p < P; ++p) part[r][p] = 0.0f;
 
     if (g < G) {
-        // LOOP = false: NBL >= NB, each lane owns at most one block (no loop)
-        for (int b = bl; LOOP ? b < NB : (b == bl && b < NB); b += NBL) {
+        // LM != 1: NBL >= NB, each lane owns at most one block (no loop)
+        for (int b = bl; LM == 1 ? b < NB : (b == bl && b < NB); b += NBL) {
             // activations of this block, for each of the MR rows
             float xr[MR][kBlock];
             f32x4_t xg[XC ? MR : 1][XC ? kBlock / 4 : 1];  // XC: 16 bytes of each of 8 runs
@@ -283,6 +304,49 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         }
     }
 
+    if (LM == 2) {
+        // Every 32-lane half belongs to one column slot (slots start at
+        // multiples of NBL): each half sums its partials in registers, and
+        // only one value per half and output goes through LDS, [MR][CC][NHV].
+        // 3.8B M=1 pass 0.817 -> 0.763 ms against the LDS sum of all lanes.
+        const int NHV = NBL >> 5;
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int p = 0; p < P; ++p) part[r][p] = sum32(part[r][p]);
+        if (g < G && (bl & 31) == 31) {
+#pragma unroll
+            for (int r = 0; r < MR; ++r)
+#pragma unroll
+                for (int p = 0; p < P; ++p) red[(r * CC + p * G + g) * NHV + (bl >> 5)] = part[r][p];
+        }
+        __syncthreads();
+        for (int o = L; o < MR * CC; o += blockDim.x) {
+            float v = red[o * NHV];
+            for (int h = 1; h < NHV; ++h) v += red[o * NHV + h];
+            const int r = MR == 1 ? 0 : o / CC, c = o - r * CC;
+            const int n = n0 + c, m = m0 + r;
+            if (n >= N || m >= M) continue;
+            if (EP) {
+                if (bias) v += bias[n];
+                if (act == W4_ACT_SWIGLU) {
+                    // CC is even: column pair (c, c + 1), c even, is outputs o and o + 1
+                    if ((c & 1) == 0) {
+                        float up = red[(o + 1) * NHV];
+                        for (int h = 1; h < NHV; ++h) up += red[(o + 1) * NHV + h];
+                        if (bias) up += bias[n + 1];
+                        ep_store_glu(v, up, residual, y, (size_t)m * (N / 2) + n / 2);
+                    }
+                } else {
+                    ep_store(v, act, residual, y, (size_t)m * N + n);
+                }
+            } else {
+                y[(size_t)m * N + n] = bias ? v + bias[n] : v;
+            }
+        }
+        return;
+    }
+
     // lane partials -> LDS as [MR][CC][NBL]; column c = p * G + g
     if (g < G) {
 #pragma unroll
@@ -414,7 +478,11 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const int64_t C = (int64_t)p.groups * p.passes;
     const dim3 grid((unsigned)((N + C - 1) / C), (unsigned)((M + p.rows - 1) / p.rows));
     const bool check = (N % C) != 0;
+    // lane mode: 1 = lanes loop over blocks; else one block per lane, and 2
+    // when every 32-lane half of a wave lies in one column slot (its partial
+    // sums are added in registers before the cross-wave step)
     const bool loop = p.lanes_per_col < K / kBlock;
+    const int lm = loop ? 1 : (p.lanes_per_col % 32 == 0 ? 2 : 0);
     // whole-run activation loads: one or two rows, exactly one block per lane (no
     // idle lanes: every lane of a wave takes part in the runs' loads), 8-lane
     // groups inside one column slot
@@ -439,19 +507,21 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV>), grid,      \
                            dim3(p.threads), shm, stream, W4_KM_ARGS)
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
-    if (MRV <= 2 && !LV && xc) {                                                                \
-        W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && !LV);                                        \
+    if (MRV <= 2 && LV != 1 && xc) {                                                            \
+        W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1);                                    \
     } else {                                                                                    \
         W4_KM_LAUNCH2(MRV, PV, CV, LV, false);                                                  \
     }
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
         if (check) {                                                                            \
-            if (loop) { W4_KM_LAUNCH(MRV, PV, true, true); }                                    \
-            else { W4_KM_LAUNCH(MRV, PV, true, false); }                                        \
+            if (lm == 1) { W4_KM_LAUNCH(MRV, PV, true, 1); }                                    \
+            else if (lm == 2) { W4_KM_LAUNCH(MRV, PV, true, 2); }                               \
+            else { W4_KM_LAUNCH(MRV, PV, true, 0); }                                            \
         } else {                                                                                \
-            if (loop) { W4_KM_LAUNCH(MRV, PV, false, true); }                                   \
-            else { W4_KM_LAUNCH(MRV, PV, false, false); }                                       \
+            if (lm == 1) { W4_KM_LAUNCH(MRV, PV, false, 1); }                                   \
+            else if (lm == 2) { W4_KM_LAUNCH(MRV, PV, false, 2); }                              \
+            else { W4_KM_LAUNCH(MRV, PV, false, 0); }                                           \
         }                                                                                       \
         return hipGetLastError();                                                               \
     }
