@@ -30,8 +30,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _HDR = os.path.join(_HERE, "oracle.h")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
-          "-Wall", "-Wextra"]
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+          "-shared", "-Wall", "-Wextra"]
 
 OK, BAD_SHAPE, NONFINITE, NO_MEMORY = 0, 1, 2, 3
 BLOCK = 32
@@ -62,6 +62,8 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 
 _SIGS = {
+    "orc_set_threads": (None, [ctypes.c_int]),
+    "orc_get_threads": (ctypes.c_int, []),
     "orc_pack_u4": (None, [_P, _I64, _P]),
     "orc_unpack_u4": (None, [_P, _I64, _P]),
     "orc_w4_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
@@ -135,6 +137,13 @@ class Oracle:
 
     def __init__(self, clib=None):
         self._l = clib if clib is not None else lib()
+
+    # -- threads (results do not depend on them) ----------------------------
+    def set_threads(self, n: int):
+        self._l.orc_set_threads(int(n))
+
+    def threads(self) -> int:
+        return int(self._l.orc_get_threads())
 
     # -- nibble packing -------------------------------------------------------
     def pack_u4(self, v):

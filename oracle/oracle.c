@@ -1,17 +1,41 @@
 /*
  * CPU oracle: plain, slow, obviously correct.  TEST INFRASTRUCTURE ONLY (see
- * oracle.h).  Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off.
- * No intrinsics, no threads, no blocking: every output is one loop over its
- * definition.  fp32 steps are written as fp32 expressions (x86-64 evaluates
- * float in float); fp64 steps are explicit casts to double.
+ * oracle.h).  Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off
+ * -fopenmp.  No intrinsics, no blocking: every output is one loop over its
+ * definition.  The matmul and the dequantization share their independent
+ * outputs (columns, rows) among OpenMP threads; each output's own loop runs
+ * in order, so the results do not depend on the thread count.  fp32 steps are
+ * written as fp32 expressions (x86-64 evaluates float in float); fp64 steps
+ * are explicit casts to double.
  */
 #include "oracle.h"
 
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define BLOCK 32
+
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 static int bad_w4_shape(int64_t K, int64_t N)
 {
@@ -124,6 +148,7 @@ int orc_w4_dequantize(const uint8_t *Wq, const float *scales, const uint8_t *zer
     uint8_t *z = (uint8_t *)malloc((size_t)((K / BLOCK) * N) + 1);
     if (!q || !z) { free(q); free(z); return ORC_NO_MEMORY; }
     orc_w4_unpack(Wq, zeros, K, N, q, z);
+#pragma omp parallel for schedule(static)
     for (int64_t k = 0; k < K; ++k) {
         for (int64_t n = 0; n < N; ++n) {
             int64_t blk = (k / BLOCK) * N + n;
@@ -179,6 +204,9 @@ int orc_w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t 
 static void row_f64(const float *xr, int64_t K, const float *W, int64_t N, const float *bias,
                     double *t, double *tb)
 {
+    /* output columns are independent and each one's sum runs over k in order,
+     * so the result does not depend on how many threads share the columns */
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         double acc = 0.0, mag = 0.0;
         for (int64_t k = 0; k < K; ++k) {

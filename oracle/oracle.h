@@ -44,6 +44,12 @@ enum {
     ORC_NO_MEMORY = 3  /* malloc failed                                    */
 };
 
+/* Threads shared among a call's independent outputs (OpenMP; 0 or less
+ * leaves the setting unchanged), and the current count.  Results do not
+ * depend on it.                                                              */
+void orc_set_threads(int n);
+int orc_get_threads(void);
+
 /* Pack count (even) 4-bit values, one per byte in v[0..count), two per byte:
  * out[i] = v[2i] | v[2i+1] << 4 (the low nibble holds the even element).     */
 void orc_pack_u4(const uint8_t *v, int64_t count, uint8_t *out);
