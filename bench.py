@@ -1,6 +1,7 @@
 """Benchmark of the 4-bit block-dequant decode matmul on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary]
+                    [--kernel kmajor|canonical]   (or W4_KERNEL=...)
 
 The step is one decode body pass of the 3.8B-dense-shaped model at M = 1:
 32 layers x 4 W4 matmuls (3072x9216 QKV, 3072x3072 out, 3072x16384
@@ -8,22 +9,27 @@ gate+up, 8192x3072 down), 2.32 GB of packed weights, i.e. 128 launches of
 the fused dequant-GEMV on one stream, captured once in a HIP graph and
 replayed.  The weights are quantized on the GPU into the canonical layout
 and prepacked once (K-major copy of the same bytes) before timing; the
-timed GEMV reads the prepacked copy.  The weights are far larger than the 256 MB Infinity Cache, so
-every pass streams them from HBM.  `value` is the pass's algorithmic bytes
-(packed weights, scales, zero points, x and y, each counted once) divided
-by the measured time per pass.
+timed GEMV reads the prepacked copy (`--kernel canonical` times the
+canonical-layout GEMV instead, for A/B).  The weights are far larger than
+the 256 MB Infinity Cache, so every pass streams them from HBM.  `value` is
+the pass's algorithmic bytes (packed weights, scales, zero points, x and y,
+each counted once) divided by the measured time per pass.
 
 Also reported on the same JSON line:
   * roofline: the GEMV kernel's algorithmic bytes per launch over its
     average launch duration (the timed pass over its 128 launches, all of
-    them this kernel), against the 8 TB/s HBM peak, plus per-shape times
-    from graphs of one shape's 32 launches;
-  * cpu_baseline: the CPU oracle (dequantize, then fp64 matmul, one thread)
-    on the first layers of the same body, in the same unit;
-  * parity: GPU outputs of those layers against the oracle's, per output;
+    them this kernel), against the 8 TB/s HBM peak and against the launch
+    floor: the same 128-launch graph with a plain streaming-read kernel
+    (w4_read_bytes) reading each matrix's packed bytes; per-shape times from
+    graphs of one shape's 32 launches; the committed rocprofv3 figures for
+    the same kernel beside the live ones;
+  * cpu_baseline: the CPU oracle (dequantize, then fp64 matmul) at 1, 4 and
+    all host threads, median of 3, on a bounded sample of every workload;
+  * parity: GPU outputs of the first layers against the oracle, per output;
   * secondary: the GPT-2-small-shaped decode pass (48 matmuls with bias),
     the int8 head [768, 50257], the GPT-2 prefill pass at M = 58 plus the
-    last-row head, and the 3.8B pass at M = 4 and M = 16.
+    last-row head, the 3.8B pass at M = 4 and M = 16, each against its own
+    roofline.
 Inputs are seeded synthetic data of the workloads' shapes and distributions
 (see synth.py); nothing is read from disk.
 """
@@ -41,6 +47,8 @@ import numpy as np
 METRIC = "W4 decode GEMV achieved HBM GB/s (% of peak) + body-pass tokens/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FLOOR_LOADS = (4, 8, 16)       # streaming-read reference: 16-byte loads per lane
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # The dominant kernel of the timed pass, the sources that define it, and the
@@ -64,6 +72,9 @@ PROFILE_COMMANDS = (
     "-o run -- python bench.py --profile-run --steps 2",
     "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/w4prof/write "
     "-o run -- python bench.py --profile-run --steps 2",
+    "timeout -s KILL 300 rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_BUBBLE_sum "
+    "TCC_EA0_RDREQ_DRAM_sum --output-format csv -d /tmp/w4prof/rdreq -o run "
+    "-- python bench.py --profile-run --steps 2",
     "python bench.py --json-out /tmp/w4prof/bench.json",
     "rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/w4prof/trace_all -o run "
     "-- python bench.py --steps 10 --warmup 2 --skip-cpu "
@@ -115,12 +126,123 @@ def committed_traffic():
                            "source": f"{PROFILE_DIR}/{TRAFFIC_SUMMARY}"}
 
 
+def committed_trace(avg_bytes: float, launches: int):
+    """The GEMV's rocprofv3 kernel-trace average from the committed summary, as
+    a roofline figure beside the live one (null once the sources changed)."""
+    f = read_summary_fields(os.path.join(ROOT, PROFILE_DIR, TRACE_SUMMARY))
+    if not f or f.get("gemv_source_sha256") != gemv_digest():
+        return None
+    try:
+        us = float(f["gemv_avg_us_rocprof"])
+    except (KeyError, ValueError):
+        return None
+    gbs = avg_bytes / (us * 1e-6) / 1e9
+    out = {"avg_launch_us_rocprof": us, "achieved_GB_s_rocprof": round(gbs, 1),
+           "frac_rocprof": round(gbs / HBM_PEAK_GBS, 4),
+           "source": f"{PROFILE_DIR}/{TRACE_SUMMARY}"}
+    for k in ("gemv_avg_us_bench_untraced", "tracer_overhead"):
+        if k in f:
+            out[k] = f[k]
+    return out
+
+
+def cpu_baseline(orc, pass_bytes: int, log):
+    """The CPU oracle (dequantize, then fp64 matmul; the head: dequantize the
+    int8 table, then the fp64 product) on a bounded sample of every workload,
+    at 1 and 4 threads (the page's thread counts) and on every host core,
+    median of 3 runs each.  GB/s of algorithmic bytes; equivalent tokens/s =
+    rows / time for the whole workload at that rate.  Results do not depend
+    on the thread count (each output's sum runs in order)."""
+    import platform
+    import statistics
+
+    import synth
+
+    nproc = os.cpu_count() or 1
+    threads = sorted({1, 4, nproc})
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+
+    def w4_case(shapes, M, cfg, with_bias):
+        items = []
+        for slot, (K, N) in shapes:
+            W = synth.weights(K, N, cfg, 0, slot)
+            packed = orc.quantize_pack(W)
+            x = synth.activations(M, K, cfg, 0, slot)
+            b = synth.bias(N, cfg, 0, slot) if with_bias else None
+            nb = K * N // 2 + (K // 32) * N * 4 + (K // 32) * N // 2
+            items.append((x, packed, b, nb + 4 * M * K + 4 * M * N + (4 * N if with_bias else 0)))
+        return (lambda: [orc.w4_matmul(x, *pk, b) for x, pk, b, _ in items],
+                sum(it[3] for it in items))
+
+    cases = []
+    f1, b1 = w4_case([(0, (768, 768))], 1, synth.CFG_SINGLE, False)
+    cases.append(("config1_768x768_m1", f1, b1, b1, 1, "the whole matmul"))
+    f2, b2 = w4_case(list(enumerate(synth.GPT2_SHAPES)), 1, synth.CFG_GPT2_DECODE, True)
+    cases.append(("config2_gpt2_decode_pass_m1", f2, b2, b2 * synth.GPT2_LAYERS, 1,
+                  "layer 0 of 12 (4 matmuls with bias)"))
+    E = synth.head_table()
+    Q, hs = orc.i8_quantize_head(E)
+    del E
+    xl = synth.activations(1, synth.GPT2_HIDDEN, synth.CFG_HEAD)[0]
+    bh = synth.GPT2_HIDDEN * synth.GPT2_VOCAB + 8 * synth.GPT2_VOCAB + 4 * synth.GPT2_HIDDEN
+    cases.append(("config3_int8_head_768x50257", lambda: orc.i8_head_logits(xl, Q, hs), bh, bh, 1,
+                  "the whole head (last row)"))
+    f4, b4 = w4_case([(1, (768, 768))], synth.GPT2_PROMPT, synth.CFG_GPT2_PREFILL, True)
+    full4 = sum(K * N // 2 + (K // 32) * N * 4 + (K // 32) * N // 2
+                + 4 * synth.GPT2_PROMPT * (K + N) + 4 * N
+                for K, N in synth.GPT2_SHAPES) * synth.GPT2_LAYERS
+    cases.append(("config4_gpt2_prefill_m58_body", f4, b4, full4, synth.GPT2_PROMPT,
+                  "the 768x768 out-projection of layer 0 at M=58 (the body's 48 matmuls "
+                  "scaled by bytes; the head is config 3)"))
+    f5, b5 = w4_case(list(enumerate(synth.DENSE38_SHAPES)), 1, synth.CFG_DENSE38, False)
+    cases.append(("config5_dense38_pass_m1", f5, b5, pass_bytes, 1,
+                  "layer 0 of 32 (4 matmuls)"))
+    before = orc.threads()
+    out = {}
+    try:
+        for name, fn, sample_bytes, full_bytes, rows, sample in cases:
+            res = {}
+            for t in threads:
+                orc.set_threads(t)
+                times = []
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    fn()
+                    times.append(time.perf_counter() - t0)
+                med = statistics.median(times)
+                gbs = sample_bytes / med / 1e9
+                res[str(t)] = {"s": round(med, 4), "GB_s": round(gbs, 4),
+                               "tokens_per_s_equiv": round(rows * gbs * 1e9 / full_bytes, 4)}
+            out[name] = {"sample": sample, "sample_bytes": sample_bytes, "threads": res}
+            log(f"CPU oracle {name}: {res}")
+    finally:
+        orc.set_threads(before)
+    main = out["config5_dense38_pass_m1"]["threads"][str(nproc)]
+    return {"value": main["GB_s"], "unit": "GB/s", "cores": nproc, "kind": "oracle",
+            "sample": "layer 0 of the 3.8B-dense M=1 pass (4 matmuls, "
+                      f"{b5 / 1e6:.1f} MB), dequantize then fp64 matmul, median of 3, "
+                      f"{nproc} threads; every workload at 1, 4 and {nproc} threads below",
+            "tokens_per_s_equiv": main["tokens_per_s_equiv"], "cpu_model": model,
+            "threads": threads, "configs": out}
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--skip-secondary", action="store_true")
+    p.add_argument("--kernel", choices=("kmajor", "canonical"),
+                   default=os.environ.get("W4_KERNEL", "kmajor"),
+                   help="GEMV timed in the step (A/B switch; also W4_KERNEL)")
     p.add_argument("--skip-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-oracle time budget for the baseline sample")
@@ -163,7 +285,7 @@ def main():
 
     class Mat:
         __slots__ = ("layer", "slot", "K", "N", "Wq", "s", "z", "P", "b", "x", "y", "bytes",
-                     "flops")
+                     "wbytes", "flops")
 
     def build_body(name, cfg, M, with_bias, outliers, f16=False, g64=False):
         shapes = synth.body(name)
@@ -201,6 +323,7 @@ def main():
                 wbytes = K * N // 2 + 2 * 4 * (K // 64) * N
             else:
                 wbytes = K * N // 2 + (K // 32) * N * (2 if f16 else 4) + (K // 32) * N // 2
+            m.wbytes = wbytes
             m.bytes = wbytes + 4 * M * K + 4 * M * N + (4 * N if with_bias else 0)
             m.flops = 2 * M * K * N
             mats.append(m)
@@ -289,7 +412,7 @@ def main():
 
     if args.profile_run_mfma:
         # eager passes on the matrix-core paths: 3.8B body at M = 16 (prepacked:
-        # the fp16 kernel; canonical: fp32 MFMA), GPT-2 body at M = 58
+        # the bf16 kernel; canonical: fp32 MFMA), GPT-2 body at M = 58
         # (prepacked: the bf16 kernel)
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
         gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)
@@ -307,18 +430,18 @@ def main():
         return
 
     # ------------------------------------------------------------ timed steps
-    graph = capture(lambda: run_pass(dense))
+    graph = capture(lambda: run_pass(dense, layout=args.kernel))
     ms, wall = time_graph(graph, args.steps, args.warmup)
     pass_bytes = sum(m.bytes for m in dense)
     pass_flops = sum(m.flops for m in dense)
     value = pass_bytes / (ms * 1e-3) / 1e9
-    log(f"dense38 M=1 pass: {ms:.4f} ms, {value:.1f} GB/s, {1e3 / ms:.1f} tok/s")
+    log(f"dense38 M=1 pass ({args.kernel}): {ms:.4f} ms, {value:.1f} GB/s, {1e3 / ms:.1f} tok/s")
 
     # ------------------------------------------------------ per-kernel roofline
-    # Every launch of the timed pass is the K-major GEMV kernel, so its average
-    # launch duration is the timed pass time (HIP events on the launch stream
-    # around the graph replays) over the launches; the small gaps between graph
-    # nodes are included, which makes it a slight overestimate.
+    # Every launch of the timed pass is the GEMV kernel, so its average launch
+    # duration is the timed pass time (HIP events on the launch stream around
+    # the graph replays) over the launches; the small gaps between graph nodes
+    # are included, which makes it a slight overestimate.
     launches = len(dense)
     avg_bytes = pass_bytes / launches
     avg_ms = ms / launches
@@ -326,7 +449,7 @@ def main():
     per_shape = {}
     for slot, (K, N) in enumerate(synth.DENSE38_SHAPES):
         sub = [m for m in dense if m.slot == slot]
-        gs = capture(lambda: run_pass(sub))
+        gs = capture(lambda: run_pass(sub, layout=args.kernel))
         mss, _ = time_graph(gs, max(5, args.steps // 2), 2)
         del gs
         us = 1e3 * mss / len(sub)
@@ -334,49 +457,63 @@ def main():
                                  "GB_s": round(sub[0].bytes / (us * 1e-6) / 1e9, 1)}
     log(f"GEMV per launch: {1e3 * avg_ms:.2f} us avg, {achieved:.1f} GB/s; {per_shape}")
     traffic, traffic_detail = committed_traffic()
+    profile = committed_trace(avg_bytes, launches)
 
-    # the same pass on the canonical layout (split-K GEMV), for comparison
-    gcan = capture(lambda: run_pass(dense, layout="canonical"))
+    # the launch floor: the same 128 launches reading each matrix's packed bytes
+    # with the streaming-read reference and nothing else
+    wb = [m.wbytes for m in dense]
+    floor_bufs = [torch.empty(n, dtype=torch.uint8, device=dev) for n in wb]
+    floor_out = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+    floor = {}
+    for L in FLOOR_LOADS:
+        gf = capture(lambda L=L: [w4.w4_read_bytes(buf, L, out=floor_out) for buf in floor_bufs])
+        msf, _ = time_graph(gf, max(5, args.steps // 2), 2)
+        del gf
+        floor[L] = msf
+    del floor_bufs
+    torch.cuda.empty_cache()
+    floor_L = min(floor, key=floor.get)
+    floor_ms = floor[floor_L]
+    floor_line = {"ms": round(floor_ms, 5), "us_per_launch": round(1e3 * floor_ms / launches, 3),
+                  "GB_s": round(pass_bytes / (floor_ms * 1e-3) / 1e9, 1),
+                  "frac_hbm_peak": round(pass_bytes / (floor_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "loads_per_lane": floor_L,
+                  "ms_by_loads_per_lane": {str(k): round(v, 5) for k, v in floor.items()},
+                  "kernel": "w4_read_bytes (streaming read of each matrix's packed bytes, "
+                            "one launch per matrix, same graph)"}
+    log(f"launch floor: {floor_line}")
+
+    # the same pass on the other layout, for comparison
+    other = "canonical" if args.kernel == "kmajor" else "kmajor"
+    gcan = capture(lambda: run_pass(dense, layout=other))
     ms_can, _ = time_graph(gcan, max(3, args.steps // 4), 2)
     del gcan
-    canonical = {"ms": round(ms_can, 4),
-                 "GB_s": round(pass_bytes / (ms_can * 1e-3) / 1e9, 1),
-                 "tokens_per_s": round(1e3 / ms_can, 1)}
-    log(f"canonical-layout pass: {canonical}")
-    # restore the K-major outputs for the parity check below
-    run_pass(dense)
+    other_pass = {"layout": other, "ms": round(ms_can, 4),
+                  "GB_s": round(pass_bytes / (ms_can * 1e-3) / 1e9, 1),
+                  "tokens_per_s": round(1e3 / ms_can, 1),
+                  "vs_timed_pass": round(ms_can / ms, 4)}
+    log(f"{other}-layout pass: {other_pass}")
+    # restore the timed layout's outputs for the parity check below
+    run_pass(dense, layout=args.kernel)
 
     # ------------------------------------------------ parity + CPU baseline
     import oracle
     orc = oracle.default()
     parity = {"checked_outputs": 0, "max_err_over_bound": 0.0, "ok": True}
+    torch.cuda.synchronize()
+    for m in dense[:8]:   # the first two layers: every shape twice
+        W = synth.weights(m.K, m.N, synth.CFG_DENSE38, m.layer, m.slot)
+        Wq, s, z = orc.quantize_pack(W)
+        y_ref, bound = orc.w4_matmul(m.x.cpu().numpy(), Wq, s, z)
+        y = m.y.cpu().numpy()
+        r = float(np.max(np.abs(y.astype(np.float64) - y_ref) / bound))
+        parity["checked_outputs"] += y.size
+        parity["max_err_over_bound"] = max(parity["max_err_over_bound"], r)
+        parity["ok"] &= bool(r <= 1.0)
+    log(f"parity: {parity}")
     cpu = None
     if not args.skip_cpu:
-        torch.cuda.synchronize()
-        cpu_time, cpu_bytes, done = 0.0, 0, 0
-        for m in dense:
-            W = synth.weights(m.K, m.N, synth.CFG_DENSE38, m.layer, m.slot)
-            Wq, s, z = orc.quantize_pack(W)
-            x = m.x.cpu().numpy()
-            t0 = time.perf_counter()
-            y_ref, bound = orc.w4_matmul(x, Wq, s, z)
-            cpu_time += time.perf_counter() - t0
-            cpu_bytes += m.bytes
-            done += 1
-            y = m.y.cpu().numpy()
-            r = float(np.max(np.abs(y.astype(np.float64) - y_ref) / bound))
-            parity["checked_outputs"] += y.size
-            parity["max_err_over_bound"] = max(parity["max_err_over_bound"], r)
-            parity["ok"] &= bool(r <= 1.0)
-            if cpu_time >= args.cpu_seconds:
-                break
-        cpu_gbs = cpu_bytes / cpu_time / 1e9
-        cpu = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {done} of the 128 M=1 matmuls of the 3.8B-dense body "
-                         f"({cpu_bytes / 1e6:.1f} MB of W4), dequantize then fp64 matmul, "
-                         f"{cpu_time:.1f} s",
-               "tokens_per_s_equiv": round(cpu_gbs * 1e9 / pass_bytes, 4)}
-        log(f"CPU oracle: {cpu_gbs:.3f} GB/s over {done} matmuls; parity {parity}")
+        cpu = cpu_baseline(orc, pass_bytes, log)
 
     # ------------------------------------------------------------- secondary
     secondary = {}
@@ -407,32 +544,42 @@ def main():
                     "down-projections; same weight bytes"}
         log(f"fused-epilogue pass: {secondary['dense38_m1_pass_fused_epilogues']}")
 
-        # 3.8B body at M = 4 (small-batch decode: the matrix cores from 3 rows
-        # on), same weights; HBM-bound (8 flops per 0.64-byte weight)
-        d4 = with_x(dense, synth.CFG_DENSE38, 4, outliers=True)
-        g4 = capture(lambda: run_pass(d4))
-        ms4, _ = time_graph(g4, 3, 1)
-        b4 = sum(m.bytes for m in d4)
-        secondary["dense38_m4_pass_kmajor"] = {
-            "ms": round(ms4, 4), "tokens_per_s": round(4e3 / ms4, 1),
-            "GB_s": round(b4 / (ms4 * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"M=4 pass: {secondary['dense38_m4_pass_kmajor']}")
-        del g4, d4
+        # 3.8B body at M = 4 and M = 16 (batched decode), same weights.  From 3
+        # rows on the K-major path runs the bf16 matrix cores on exact
+        # three-part activations (one 16-row tile up to 16 rows): 3 bf16 MFMAs
+        # per fp32 product on 16 rows however many are used.  That work at the
+        # bf16 peak (348 GFLOP, 139 us) is below the HBM time of the 2.42 GB
+        # (303 us at M = 16), so each line's own roofline is HBM.
+        def own_roofline(mats, msv, mfma_rows):
+            b = sum(m.bytes for m in mats)
+            mf = sum(3 * 2 * mfma_rows * m.K * m.N for m in mats)
+            t_hbm = b / (HBM_PEAK_GBS * 1e9)
+            t_mfma = mf / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+            bound = "hbm" if t_hbm >= t_mfma else "bf16 mfma"
+            return {"bound": bound, "bound_ms": round(1e3 * max(t_hbm, t_mfma), 4),
+                    "frac": round(max(t_hbm, t_mfma) / (msv * 1e-3), 4),
+                    "GB_s": round(b / (msv * 1e-3) / 1e9, 1),
+                    "bf16_mfma_TFLOP_s_issued": round(mf / (msv * 1e-3) / 1e12, 1)}
 
-        # 3.8B body at M = 16 (batched decode), same weights
-        d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
-        fl16 = sum(m.flops for m in d16)
-        for layout, name in (("kmajor", "dense38_m16_pass_kmajor_mfma"),
-                             ("canonical", "dense38_m16_pass_canonical_fp32_mfma")):
-            g16 = capture(lambda: run_pass(d16, layout=layout))
-            ms16, _ = time_graph(g16, 3, 1)
-            secondary[name] = {
-                "ms": round(ms16, 4), "tokens_per_s": round(16e3 / ms16, 1),
-                "TFLOP_s": round(fl16 / (ms16 * 1e-3) / 1e12, 3),
-                "frac_fp32_mfma_peak": round(fl16 / (ms16 * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
-            del g16
-        del d16
+        for Mb in (4, 16):
+            dm = with_x(dense, synth.CFG_DENSE38, Mb, outliers=True)
+            flm = sum(m.flops for m in dm)
+            for layout in ("kmajor", "canonical"):
+                gm = capture(lambda: run_pass(dm, layout=layout))
+                msm, _ = time_graph(gm, 3, 1)
+                del gm
+                line_m = {"ms": round(msm, 4), "tokens_per_s": round(Mb * 1e3 / msm, 1),
+                          "TFLOP_s": round(flm / (msm * 1e-3) / 1e12, 3)}
+                if layout == "kmajor":
+                    line_m["roofline"] = own_roofline(dm, msm, 16)
+                    line_m["kernel"] = "k_mm_x3 (bf16 x3 matrix cores, exact operands)"
+                else:
+                    line_m["frac_fp32_mfma_peak"] = round(
+                        flm / (msm * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
+                    line_m["kernel"] = "k_mm_mfma (fp32 matrix cores)"
+                secondary[f"dense38_m{Mb}_pass_{layout}"] = line_m
+                log(f"M={Mb} {layout} pass: {line_m}")
+            del dm
         del graph
         dense.clear()
         torch.cuda.empty_cache()
@@ -545,16 +692,13 @@ def main():
         secondary["i8_head_768x50257"] = head_times
 
         # full-sequence logits [58 x 50257] (the export before the last-position
-        # slice): the digit image of x, then one pass over the token-major
-        # table; 8 table copies in turn
+        # slice): one pass over the token-major table for all rows; 8 table
+        # copies in turn
         xs = torch.from_numpy(synth.activations(synth.GPT2_PROMPT, synth.GPT2_HIDDEN,
                                                 synth.CFG_HEAD)).to(dev)
         outs = torch.empty((synth.GPT2_PROMPT, synth.GPT2_VOCAB), device=dev)
         tabs = [Qk.clone() for _ in range(8)]
-        wsr = torch.empty(w4.library().i8_head_rows_workspace_bytes(
-            synth.GPT2_PROMPT, synth.GPT2_HIDDEN), dtype=torch.uint8, device=dev)
-        gs = capture(lambda: [w4.i8_head_logits_rows(xs, tabs[i % 8], hsk, out=outs,
-                                                     workspace=wsr)
+        gs = capture(lambda: [w4.i8_head_logits_rows(xs, tabs[i % 8], hsk, out=outs)
                               for i in range(16)])
         mss, _ = time_graph(gs, 10, 2)
         del gs, tabs
@@ -575,6 +719,11 @@ def main():
             w4.i8_head_logits_kmajor(last.y[-1], Qk, hsk, synth.GPT2_HIDDEN, out=lg)
 
         fp = sum(m.flops for m in pre) + 2 * synth.GPT2_HIDDEN * synth.GPT2_VOCAB
+        # own roofline: the body's bytes plus the head table at 8 TB/s, or the
+        # bf16 MFMA work of the body (4 row tiles of 16, 3 parts) at 2.5 PFLOP/s
+        pre_bytes = sum(m.bytes for m in pre) + hb_lane + synth.GPT2_HIDDEN * synth.GPT2_VOCAB
+        pre_mfma = sum(3 * 2 * 64 * m.K * m.N for m in pre)
+        t_pre = max(pre_bytes / (HBM_PEAK_GBS * 1e9), pre_mfma / (BF16_MFMA_PEAK_TFLOPS * 1e12))
         for layout, name in (("kmajor", "gpt2_prefill_m58_pass_plus_head"),
                              ("canonical", "gpt2_prefill_m58_pass_plus_head_canonical_mfma")):
             gp = capture(lambda: run_pass(pre, head_last, layout=layout))
@@ -582,7 +731,9 @@ def main():
             del gp
             secondary[name] = {
                 "ms": round(msp, 4), "tokens_per_s": round(synth.GPT2_PROMPT * 1e3 / msp, 1),
-                "TFLOP_s": round(fp / (msp * 1e-3) / 1e12, 3)}
+                "TFLOP_s": round(fp / (msp * 1e-3) / 1e12, 3),
+                "frac_own_roofline": round(t_pre / (msp * 1e-3), 4),
+                "own_roofline_ms": round(1e3 * t_pre, 4)}
 
     line = {
         "metric": METRIC,
@@ -601,6 +752,7 @@ def main():
             "workload": "3.8B-dense-shaped decode body pass, M=1: 32 layers x (3072x9216, "
                         "3072x3072, 3072x16384, 8192x3072) W4 matmuls, uint4 block-32 "
                         "asymmetric, fp32 scales, packed uint4 zeros",
+            "kernel_switch": args.kernel,
             "launches_per_step": launches,
             "algorithmic_bytes_per_step": pass_bytes,
             "flops_per_step": pass_flops,
@@ -612,9 +764,13 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "traffic_detail": traffic_detail,
-                     "kernel": GEMV_KERNEL, "avg_launch_us": round(1e3 * avg_ms, 3),
-                     "avg_bytes_per_launch": round(avg_bytes), "per_shape": per_shape},
-        "canonical_layout_pass": canonical,
+                     "kernel": GEMV_KERNEL if args.kernel == "kmajor" else "k_gemv_fast",
+                     "avg_launch_us": round(1e3 * avg_ms, 3),
+                     "avg_bytes_per_launch": round(avg_bytes), "per_shape": per_shape,
+                     "launch_floor": floor_line,
+                     "frac_of_launch_floor": round(floor_ms / ms, 4),
+                     "profile": profile},
+        "other_layout_pass": other_pass,
         "cpu_baseline": cpu,
         "parity": parity,
         "secondary": secondary,
@@ -702,6 +858,30 @@ def summarize_profiles(src: str, out_dir: str):
                   f"- bench_ms_per_step: {plain.get('ms_per_step')}",
                   f"- roofline_achieved_GB_s: {rl.get('achieved')}",
                   f"- roofline_frac: {rl.get('frac')}"]
+        if bench and rl.get("avg_launch_us"):
+            traced = bench.get("roofline", {}).get("avg_launch_us")
+            if traced:
+                # the same bench clock (HIP events around the graph) with and
+                # without the tracer: what tracing adds per launch
+                lines.append(f"- tracer_overhead: {traced / rl['avg_launch_us']:.4f}")
+    # per launch shape: the trace's dispatches grouped by grid and workgroup size
+    groups = {}
+    for r in rows:
+        if GEMV_KERNEL in r["Kernel_Name"]:
+            key = (int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if groups:
+        lines += ["", "GEMV dispatches by launch shape (grid threads, workgroup threads; the "
+                  "3.8B shapes are 147456/192 for 3072x9216, 98304/192 for 3072x3072, "
+                  "196608/192 for 3072x16384 and 131072/256 for 8192x3072):", "",
+                  "| grid | workgroup | calls | avg us | median us |", "|---|---|---|---|---|"]
+        for (gx, wx), v in sorted(groups.items()):
+            lines.append(f"| {gx} | {wx} | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                         f"{_pct(v, 50) / 1e3:.3f} |")
+        if plain:
+            lines += ["", "Untraced per-shape launch times of the same bench (graphs of one "
+                      "shape's 32 launches, HIP events, gaps included): "
+                      + json.dumps(plain.get("roofline", {}).get("per_shape", {}))]
     lines.append(f"- gemv_source_sha256: {gemv_digest()}")
     with open(os.path.join(out_dir, TRACE_SUMMARY), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -751,6 +931,32 @@ def summarize_profiles(src: str, out_dir: str):
         tot = res["fetch"]["per_launch"] + res["write"]["per_launch"]
         lines += [f"- algorithmic_bytes_per_launch: {alg}",
                   f"- traffic_over_algorithmic: {tot / alg:.4f}"]
+    # cross-check: the raw read requests at the memory interface (32-byte,
+    # 64-byte and 128-byte ones) counted separately, for the copy and the GEMV
+    rq = {c: per_dispatch("rdreq", c) for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                                               "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum")}
+    if all(rq.values()):
+        def req_bytes(sel):
+            tot = {}
+            for c, d in rq.items():
+                v = [x for k, x in d if sel(k)]
+                tot[c] = statistics.median(v) if v else float("nan")
+            r, r32, bub = tot["TCC_EA0_RDREQ_sum"], tot["TCC_EA0_RDREQ_32B_sum"], tot["TCC_BUBBLE_sum"]
+            return 128 * bub + 64 * (r - bub - r32) + 32 * r32, tot
+        cb, ct = req_bytes(lambda k: "neg_kernel" in k)
+        gb, gt = req_bytes(lambda k: GEMV_KERNEL in k)
+        lines += ["", "Raw read requests at the memory interface (median per dispatch): "
+                  "128-byte (TCC_BUBBLE), 32-byte (TCC_EA0_RDREQ_32B) and the rest 64-byte "
+                  "(of TCC_EA0_RDREQ); DRAM requests (TCC_EA0_RDREQ_DRAM) beside them.", "",
+                  f"- rdreq_copy_requests: {ct['TCC_EA0_RDREQ_sum']:.0f}",
+                  f"- rdreq_copy_bytes_from_requests: {cb:.0f}",
+                  f"- rdreq_copy_fraction_of_true_bytes: {cb / copy_bytes:.5f}",
+                  f"- rdreq_gemv_requests: {gt['TCC_EA0_RDREQ_sum']:.0f}",
+                  f"- rdreq_gemv_32B_requests: {gt['TCC_EA0_RDREQ_32B_sum']:.0f}",
+                  f"- rdreq_gemv_128B_requests: {gt['TCC_BUBBLE_sum']:.0f}",
+                  f"- rdreq_gemv_dram_requests: {gt['TCC_EA0_RDREQ_DRAM_sum']:.0f}",
+                  f"- rdreq_gemv_bytes_from_requests: {gb:.0f}",
+                  f"- rdreq_gemv_bytes_scaled_by_copy: {gb * copy_bytes / cb:.0f}"]
     lines.append(f"- gemv_source_sha256: {gemv_digest()}")
     with open(os.path.join(out_dir, TRAFFIC_SUMMARY), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -771,12 +977,13 @@ def summarize_profiles(src: str, out_dir: str):
              "", "Made by:", "", cmds, "",
              "Every dispatch of the traced run of the full bench (the secondary lines "
              "included), by total time.  Template arguments name the instantiation: "
-             "`k_mm_h3<MT, NT, QPW, DQ, fp16 scales>` is the fp16 matrix-core matmul for one "
-             "16-row tile (M = 4 and 16 here), `k_mm_x3<...>` the bf16 one for M > 16 with MT "
-             "tiles of 16 rows (1 for the small GPT-2 matrices at M = 58), `k_gemv_kmajor<rows, passes, "
-             "ragged, loop, fp16 scales, epilogue, affine>` the K-major GEMV, "
-             "`k_head_logits_mfma` the last-row head, `k_head_digits` + "
-             "`k_head_rows_mfma` the full-sequence head.", "",
+             "`k_gemv_kmajor<rows, passes, ragged, lane mode, fp16 scales, epilogue, affine, "
+             "whole-run x>` the K-major GEMV (lane mode 2: 32-lane halves summed in "
+             "registers), `k_mm_x3<MT, NT, QPW, DQ, fp16 scales>` the bf16 matrix-core "
+             "matmul for M >= 3 with MT tiles of 16 rows, `k_gemv_fast` + `k_splitk_reduce` the "
+             "canonical-layout GEMV, `k_mm_mfma` the canonical fp32 matrix-core matmul, "
+             "`k_head_fp32` the last-row head, `k_head_rows_x3` the full-sequence head, "
+             "`k_read_bytes` the launch floor's streaming read.", "",
              "| kernel | calls | avg us | p10 us | median us | p90 us | min us | max us | total ms |",
              "|---|---|---|---|---|---|---|---|---|"]
     for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:40]:
@@ -813,11 +1020,10 @@ def summarize_profiles(src: str, out_dir: str):
              "prepacked).  `MfmaUtil` is rocprofv3's derived metric: MFMA-busy cycles over "
              "active cycles times SIMDs, in percent.  MFMA FLOP/s count the matrix-core "
              "operations the kernel issued (MOPS x 512 over the dispatch's duration under "
-             "counter collection): `k_mm_h3` (M <= 16) and `k_mm_x3` (M > 16) issue three "
-             "fp16 or bf16 MFMAs per fp32 product (three-part splits of each activation), "
-             "so their useful fp32 rate is a third of their fp16/bf16 rate; `k_mm_mfma` "
-             "runs fp32 MFMA.  Peaks: fp16 and bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s "
-             "(dense).", "",
+             "counter collection): `k_mm_x3` issues three bf16 MFMAs per fp32 product "
+             "(exact three-part splits of each activation) on whole 16-row tiles, so its "
+             "useful fp32 rate is at most a third of its bf16 rate; `k_mm_mfma` runs fp32 "
+             "MFMA.  Peaks: bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s (dense).", "",
              "| kernel | dispatches | MfmaUtil % (mean) | fp16 MFMA TFLOP/s | "
              "bf16 MFMA TFLOP/s | fp32 MFMA TFLOP/s | avg us |",
              "|---|---|---|---|---|---|---|"]

@@ -363,6 +363,22 @@ int i8_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t 
                     const float *hs, int64_t K, int64_t N, float *out,
                     int *d_status, void *stream);
 
+/* ---- measurement: streaming-read reference ---------------------------------
+ * Reads [src, src + bytes) once with 16-byte streaming loads, loads_per_lane
+ * (4, 6, 8, 12 or 16) of them per lane, 256 lanes (4 waves) per workgroup,
+ * and writes out[w] = XOR of the 32-bit words wave w read, for w below
+ * w4_read_bytes_words(bytes, loads_per_lane) (0 for arguments out of range):
+ * lane t of workgroup g reads the 16-byte pieces g 256 + t + j 256 G (G
+ * workgroups, j < loads_per_lane) that lie below bytes.
+ * The benchmark times one launch per weight matrix, each over that matrix's
+ * packed byte count, as the launch floor of the decode pass: the same bytes
+ * and launches as the GEMV, without its arithmetic.  bytes % 16 == 0; src
+ * 16-byte aligned, out 4-byte aligned.                                      */
+size_t w4_read_bytes_words(int64_t bytes, int loads_per_lane);
+
+int w4_read_bytes(const void *src, int64_t bytes, int loads_per_lane, uint32_t *out,
+                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
                  "w4g_check_matmul_kmajor_args", "w4g_matmul_kmajor",
                  "w4_check_matmul_kmajor_ep_args",
                  "w4h_quantize_pack", "w4h_dequantize", "w4h_prepack_kmajor",
-                 "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args", "w4_matmul_noalloc"):
+                 "w4h_matmul_kmajor", "w4h_check_matmul_kmajor_args", "w4_matmul_noalloc",
+                 "w4_read_bytes", "w4_read_bytes_words"):
         assert must in names
 
 
@@ -155,6 +156,20 @@ def test_entry_points_reject_before_any_hip_call():
     # empty work succeeds without a device
     assert lib.w4_matmul(None, 0, 768, None, None, None, 768, None, None, None, 0, None) == w4.W4_OK
     assert lib.i8_embed(None, 0, None, 10, None, 768, 10, None, None, None) == w4.W4_OK
+
+
+def test_read_bytes_host_checks():
+    lib = w4.library()
+    assert lib.w4_read_bytes_words(1 << 20, 8) == 4 * (1 << 20) // (256 * 16 * 8)
+    assert lib.w4_read_bytes_words(1 << 20, 5) == 0
+    assert lib.w4_read_bytes_words(100, 8) == 0
+    assert lib.w4_read_bytes(A, 100, 8, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_read_bytes(A, 4096, 7, A, None) == w4.W4_ERR_BAD_SHAPE
+    assert lib.w4_read_bytes(A + 8, 4096, 8, A, None) == w4.W4_ERR_MISALIGNED
+    assert lib.w4_read_bytes(None, 4096, 8, A, None) == w4.W4_ERR_NULL_PTR
+    assert lib.w4_read_bytes(None, 0, 8, None, None) == w4.W4_OK
+    if NO_GPU:
+        assert lib.w4_read_bytes(A, 4096, 8, A, None) == w4.W4_ERR_DEVICE
 
 
 def test_noalloc_host_checks():

@@ -902,3 +902,21 @@ def test_shared_workspace_growth_keeps_captured_graphs_valid():
         y.zero_()
         g.replay()
         assert_bits(host(y), ref, "graph replay after the scratch grew")
+
+
+@pytest.mark.parametrize("nbytes,loads", [(1 << 20, 8), (4096 * 16 + 48, 4), (18186240, 16),
+                                          (16, 6), (300000 * 16, 12)])
+def test_read_bytes_xor_words(nbytes, loads):
+    """The streaming-read reference: wave w's word is the XOR of the 32-bit
+    words it read (lane t of workgroup g reads pieces g*256 + t + j*256*G)."""
+    g = np.random.default_rng(nbytes)
+    data = g.integers(0, 256, size=nbytes, dtype=np.uint8)
+    out = host(w4.w4_read_bytes(dev(data), loads))
+    words = w4.library().w4_read_bytes_words(nbytes, loads)
+    lanes = words * 64
+    pieces = data.view(np.uint32).reshape(-1, 4)
+    n16 = pieces.shape[0]
+    grp = (np.arange(n16) % lanes) // 64
+    want = np.zeros(words, np.uint32)
+    np.bitwise_xor.at(want, grp, np.bitwise_xor.reduce(pieces, axis=1))
+    assert np.array_equal(out[:words].view(np.uint32), want)

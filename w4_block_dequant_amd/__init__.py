@@ -45,6 +45,8 @@ _SIGS = {
     "w4_matmul": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "w4_check_matmul_args": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ]),
     "w4_matmul_noalloc": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P]),
+    "w4_read_bytes_words": (_SZ, [_I64, _INT]),
+    "w4_read_bytes": (_INT, [_P, _I64, _INT, _P, _P]),
     "w4_prepack_kmajor": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P]),
     "w4_matmul_kmajor_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w4_matmul_kmajor": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
@@ -229,6 +231,19 @@ def w4_matmul(x: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, zeros: to
     _check("w4_matmul", _lib.w4_matmul(_ptr(x), M, K, _ptr(Wq), _ptr(scales), _ptr(zeros), N,
                                        _ptr(bias), _ptr(out), _ptr(ws), wsb,
                                        _stream(x.device)))
+    return out
+
+
+def w4_read_bytes(src: torch.Tensor, loads_per_lane: int = 8, out: torch.Tensor | None = None):
+    """Streaming-read reference over a contiguous uint8 tensor (the benchmark's
+    launch floor); returns the per-workgroup XOR words."""
+    _dev(src, torch.uint8, "src")
+    n = src.numel()
+    words = _lib.w4_read_bytes_words(n, loads_per_lane)
+    if out is None:
+        out = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    _check("w4_read_bytes", _lib.w4_read_bytes(_ptr(src), n, loads_per_lane, _ptr(out),
+                                               _stream(src.device)))
     return out
 
 

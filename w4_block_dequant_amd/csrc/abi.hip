@@ -508,4 +508,25 @@ int i8_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Qt, int64_t 
         w4::launch_embed_kmajor(tokens, T, Qt, ldt, hs, K, N, out, d_status, as_stream(stream)));
 }
 
+size_t w4_read_bytes_words(int64_t bytes, int loads_per_lane) {
+    if (bytes <= 0 || bytes % 16 != 0) return 0;
+    if (loads_per_lane != 4 && loads_per_lane != 6 && loads_per_lane != 8 &&
+        loads_per_lane != 12 && loads_per_lane != 16)
+        return 0;
+    return (size_t)w4::read_bytes_words(bytes, loads_per_lane);
+}
+
+int w4_read_bytes(const void *src, int64_t bytes, int loads_per_lane, uint32_t *out,
+                  void *stream) {
+    if (bytes < 0 || bytes % 16 != 0) return W4_ERR_BAD_SHAPE;
+    if (bytes == 0) return W4_OK;
+    if (w4_read_bytes_words(bytes, loads_per_lane) == 0) return W4_ERR_BAD_SHAPE;
+    if ((uint64_t)w4_read_bytes_words(bytes, loads_per_lane) > 0x7FFFFFFFu) return W4_ERR_BAD_SHAPE;
+    if (!src || !out) return W4_ERR_NULL_PTR;
+    if (!aligned(src, 16) || !aligned(out, 4)) return W4_ERR_MISALIGNED;
+    int st = device_check();
+    if (st) return st;
+    return launched(w4::launch_read_bytes(src, bytes, loads_per_lane, out, as_stream(stream)));
+}
+
 }  // extern "C"

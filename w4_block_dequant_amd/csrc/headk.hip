@@ -162,6 +162,141 @@ __global__ __launch_bounds__(256) void k_head_fp32(const float *__restrict__ x, 
     }
 }
 
+// Full-sequence logits on the bf16 matrix cores with exact operands (M >= 4,
+// K <= 1024).  A token's codes are exact in bf16 (|Q| <= 127), and every fp32
+// activation is exactly h + m + l with h = bf16(x), m = bf16(x - h),
+// l = x - h - m (each difference exact in fp32, l exact in bf16), so each
+// v_mfma_f32_16x16x32_bf16 forms exact products and only its fp32
+// accumulation rounds, as in the fp32 kernel; hs[n] is applied at the end.
+//
+// One wave owns 16 tokens (lane c = lane % 16 is token t0 + c) for all rows;
+// a workgroup of WAVES waves shares each tile's activation parts.
+// Lane group g = lane / 16 owns the contiguous k range [g KQ, (g + 1) KQ) of
+// the padded K (KP = 4 KQ, a multiple of 64), 8 k per MFMA step: its codes
+// come in whole 16-byte loads, are turned into bf16 once and stay in
+// registers (4 dwords per step).  The rows pass through LDS one 16-row tile
+// at a time as three bf16 part planes [part][row][KP + 8] (the 8-element pad
+// spreads the rows over the LDS banks), built once per workgroup; the A
+// operand of step s for lane (g, r) is row r's parts at k = g KQ + 8 s.
+// Rows with a non-finite entry are flagged while they are built and give NaN.
+template <int SMAX, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__restrict__ x, int M, int K,
+                                                      const int8_t *__restrict__ Qt, int ldt,
+                                                      const float *__restrict__ hs, int N,
+                                                      float *__restrict__ logits) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    extern __shared__ u32x4_t aplane_v[];  // [3][16][KP + 8] bf16
+    __shared__ int rowbad[16];
+    uint16_t *ap = reinterpret_cast<uint16_t *>(aplane_v);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int t0 = (blockIdx.x * WAVES + wave) * 16;
+    const int KP = (K + 63) / 64 * 64, KQ = KP / 4, S = KQ / 8, RS = KP + 8;
+    const int n = min(t0 + c, N - 1);
+
+    // codes of this lane's token and k range, as bf16 pairs: step s uses b[s]
+    u32x4_t b[SMAX];
+    {
+        const int8_t *row = Qt + (size_t)n * ldt;
+#pragma unroll
+        for (int j = 0; j < SMAX / 2; ++j) {
+            if (2 * j < S) {
+                const int k0 = min(g * KQ + 16 * j, ldt - 16);  // past K: a valid piece, zero A
+                // ordinary (cached) loads: one load instruction covers 16 bytes
+                // of 64 different lines, which the next ones finish
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(row + k0);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                uint32_t o[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float lo = (float)(int)(int8_t)(w[d] >> (16 * h));
+                        const float hi = (float)(int)(int8_t)(w[d] >> (16 * h + 8));
+                        // bf16 of a small integer is the upper half of its fp32 bits
+                        o[2 * d + h] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi),
+                                                             __builtin_bit_cast(uint32_t, lo),
+                                                             0x07060302u);
+                    }
+                b[2 * j] = u32x4_t{o[0], o[1], o[2], o[3]};
+                b[2 * j + 1] = u32x4_t{o[4], o[5], o[6], o[7]};
+            }
+        }
+    }
+    const float hsn = hs[n];
+    const int K8 = KP / 8;  // 8-element pieces per row
+
+    for (int m0 = 0; m0 < M; m0 += 16) {
+        __syncthreads();  // the previous tile's reads are done
+        if (tid < 16) rowbad[tid] = 0;
+        __syncthreads();
+        // build: piece e = (row, 8 k) of the tile, three bf16 parts each
+        for (int e = tid; e < 16 * K8; e += 64 * WAVES) {
+            const int r = e / K8, k = 8 * (e - r * K8);
+            float xv[8];
+            const bool live = m0 + r < M && k < K;  // K % 16 == 0: a piece is all in or all out
+            if (live) {
+                const f32x4_t *xp = reinterpret_cast<const f32x4_t *>(x + (size_t)(m0 + r) * K + k);
+                const f32x4_t a0 = xp[0], a1 = xp[1];
+                xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+                xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xv[i] = 0.0f;
+            }
+            bool fin = true;
+            uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = xv[2 * i], bq = xv[2 * i + 1];
+                fin &= __builtin_isfinite(a) && __builtin_isfinite(bq);
+                const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, bq}, bf16x2_t));
+                const float ra = a - __builtin_bit_cast(float, h << 16);
+                const float rb = bq - __builtin_bit_cast(float, h & 0xFFFF0000u);
+                const uint32_t m = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{ra, rb}, bf16x2_t));
+                const float la = ra - __builtin_bit_cast(float, m << 16);
+                const float lb = rb - __builtin_bit_cast(float, m & 0xFFFF0000u);
+                ph[i] = h;
+                pm[i] = m;
+                pl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{la, lb}, bf16x2_t));
+            }
+            if (!fin) rowbad[r] = 1;
+            *reinterpret_cast<u32x4_t *>(ap + (0 * 16 + r) * RS + k) = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+            *reinterpret_cast<u32x4_t *>(ap + (1 * 16 + r) * RS + k) = u32x4_t{pm[0], pm[1], pm[2], pm[3]};
+            *reinterpret_cast<u32x4_t *>(ap + (2 * 16 + r) * RS + k) = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+        }
+        __syncthreads();
+        // two accumulators (even and odd steps): two independent MFMA chains
+        f32x4v acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            if (s < S) {
+                const int k = g * KQ + 8 * s;
+                const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (2 * 16 + c) * RS + k));
+                const bf16x8_t am = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (1 * 16 + c) * RS + k));
+                const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (0 * 16 + c) * RS + k));
+                const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b[s]);
+                f32x4v &a = acc2[s & 1];
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bb, a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, a, 0, 0, 0);
+            }
+        }
+        const f32x4v acc = acc2[0] + acc2[1];
+        // lane (g, c) holds D[4 g + v][c]: row m0 + 4 g + v, token t0 + c
+        const int t = t0 + c;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + 4 * g + v;
+            if (m < M && t < N)
+                logits[(size_t)m * N + t] = rowbad[4 * g + v] ? __builtin_nanf("") : acc[v] * hsn;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_head_prepack(const int8_t *Q, int64_t K, int64_t N, int64_t ldq, int8_t *Qt,
@@ -223,7 +358,32 @@ hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const i
                                    int64_t ldt, const float *hs, int64_t N, float *logits,
                                    void *workspace, hipStream_t stream) {
     (void)workspace;
-    return launch_head_fp32(x, M, K, Qt, ldt, hs, N, logits, stream);
+    // from 4 rows on (and K up to 1024, whose codes fit a wave's registers)
+    // the matrix cores; below, or for longer rows, the fp32 kernel
+    const int64_t KP = (K + 63) / 64 * 64;
+    if (M < 4 || KP > 1024) return launch_head_fp32(x, M, K, Qt, ldt, hs, N, logits, stream);
+    const size_t shm = (size_t)3 * 16 * (KP + 8) * 2;
+    // 8 waves (128 tokens) per workgroup: each tile's activation parts are
+    // built once for twice the tokens of a 4-wave workgroup
+    constexpr int WV = 8;
+    const dim3 grid((unsigned)((N + 16 * WV - 1) / (16 * WV)));
+    const int S = (int)(KP / 32);  // MFMA steps per lane group
+    // more than 64 KB of dynamic LDS (K above 640) is allowed once per kernel
+#define W4_HR(SV)                                                                                 \
+    do {                                                                                          \
+        static const hipError_t attr = hipFuncSetAttribute(                                      \
+            reinterpret_cast<const void *>(&k_head_rows_x3<SV, WV>),                             \
+            hipFuncAttributeMaxDynamicSharedMemorySize, 3 * 16 * (32 * SV + 8) * 2);             \
+        if (attr != hipSuccess) return attr;                                                      \
+        hipLaunchKernelGGL((k_head_rows_x3<SV, WV>), grid, dim3(64 * WV), shm, stream, x,         \
+                           (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits);                     \
+    } while (0)
+    if (S <= 8) W4_HR(8);
+    else if (S <= 16) W4_HR(16);
+    else if (S <= 24) W4_HR(24);
+    else W4_HR(32);
+#undef W4_HR
+    return hipGetLastError();
 }
 
 }  // namespace w4

@@ -75,4 +75,11 @@ hipError_t launch_embed_kmajor(const int64_t *tokens, int64_t T, const int8_t *Q
                                const float *hs, int64_t K, int64_t N, float *out, int *d_status,
                                hipStream_t stream);
 
+// Streaming-read reference: `loads` 16-byte loads per lane, 256 lanes per
+// workgroup, one XOR word per wave into out[read_bytes_words(...)].
+int64_t read_bytes_groups(int64_t bytes, int loads);
+int64_t read_bytes_words(int64_t bytes, int loads);
+hipError_t launch_read_bytes(const void *src, int64_t bytes, int loads, uint32_t *out,
+                             hipStream_t stream);
+
 }  // namespace w4
