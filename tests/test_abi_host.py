@@ -143,7 +143,10 @@ def test_entry_points_reject_before_any_hip_call():
     assert km(None, 1, 128, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_NULL_PTR
     # M >= 3 on the matrix-core path: split-K needs a workspace for narrow N
     assert w4.w4_matmul_kmajor_workspace_bytes(2, 3072, 3072) == 0      # M = 2: the GEMV
-    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 3072) > 0       # M = 3: matrix cores
+    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 3072) == 0      # M = 3: whole-K matrix cores
+    assert w4.w4_matmul_kmajor_workspace_bytes(8, 3072, 3072) == 0      # up to 8 rows
+    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 768) > 0        # too few columns: split-K
+    assert w4.w4_matmul_kmajor_workspace_bytes(9, 3072, 3072) > 0       # 9 rows: split-K
     need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072)
     assert need > 0
     assert w4.w4_matmul_kmajor_workspace_bytes(1, 3072, 3072) == 0

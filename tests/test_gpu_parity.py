@@ -631,6 +631,92 @@ def test_kmajor_matrix_cores_deterministic_with_dirty_workspace():
     assert_bits(y1, y2, "x3 repeat")
 
 
+# The whole-K matrix-core kernel (3 <= M <= 8 rows, N >= 2033: one
+# workgroup per 16 columns over all of K, no workspace).  K = 128 and 256
+# leave waves of a workgroup with no quads; 2050, 3080 and 2344 are ragged N;
+# 8192 gives 16 quads per wave; M = 3 and 5..8 exercise the row padding of
+# the 4- and 8-row activation images.
+WHOLE_K_SHAPES = [(128, 2048), (256, 2050), (384, 2344), (3072, 3080), (8192, 2064)]
+
+
+@pytest.mark.parametrize("K,N", WHOLE_K_SHAPES)
+@pytest.mark.parametrize("M", [3, 4, 5, 6, 8])
+def test_kmajor_whole_k_kernel(M, K, N):
+    assert w4.w4_matmul_kmajor_workspace_bytes(M, K, N) == 0
+    note(f"kmajor whole-K M={M} K={K} N={N}")
+    W = mixed_weights(K, N, cfg=242)
+    x = synth.activations(M, K, cfg=242, slot=M, outliers=True)
+    b = synth.bias(N, cfg=242)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z, b)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y1 = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y1, y_ref, bound, f"kmajor whole-K M={M} {K}x{N}")
+    y2 = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bits(y1, y2, "whole-K repeat")
+
+
+@pytest.mark.parametrize("act,res", [("gelu", False), ("swiglu", True), ("none", True)])
+@pytest.mark.parametrize("M", [4, 7])
+def test_kmajor_whole_k_epilogue(M, act, res):
+    K, N = 384, 2344
+    note(f"kmajor whole-K epilogue M={M} act={act} residual={res}")
+    W = mixed_weights(K, N, cfg=243)
+    x = synth.activations(M, K, cfg=243, slot=M, outliers=True)
+    b = synth.bias(N, cfg=243)
+    nout = N // 2 if act == "swiglu" else N
+    r = synth.activations(M, nout, cfg=244, slot=M) if res else None
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, b, r, act=act)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b), act=act,
+                                 residual=None if r is None else dev(r)))
+    assert_bound(y, y_ref, bound, f"kmajor whole-K epilogue {act} M={M}")
+
+
+@pytest.mark.parametrize("M", [3, 8])
+def test_kmajor_whole_k_special_inputs(M):
+    K, N = 768, 2304
+    W = mixed_weights(K, N, cfg=245)
+    W[300, :] = 0.0
+    Wq, s, z = ORC.quantize_pack(W)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    base = synth.activations(M, K, cfg=245)
+    outlier = base.copy()
+    outlier[:, 300] *= np.float32(1e12)   # on a row of zero weights
+    cases = {"zeros": np.zeros((M, K), np.float32),
+             "tiny": base * np.float32(1e-30),
+             "huge": base * np.float32(1e30),
+             "subnormal": base * np.float32(1e-40),
+             "spread": base * np.where(np.arange(K) % 3 == 0, 1e3, 1e-3).astype(np.float32),
+             "row magnitudes": base * np.logspace(-30, 30, M, dtype=np.float64)
+                                        .astype(np.float32)[:, None],
+             "isolated outlier": outlier}
+    for name, x in cases.items():
+        y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+        y = host(w4.w4_matmul_kmajor(dev(x), *P))
+        assert_bound(y, y_ref, bound, f"kmajor whole-K x={name} M={M}")
+
+
+def test_kmajor_whole_k_large_scales_and_f16():
+    K, N, M = 768, 2048, 4
+    W = synth.weights(K, N, cfg=246) * np.float32(5e34)
+    x = synth.activations(M, K, cfg=246, slot=M)
+    Wq, s, z = ORC.quantize_pack(W)
+    assert float(np.max(s)) > 2.0 ** 104
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    assert_bound(host(w4.w4_matmul_kmajor(dev(x), *P)), y_ref, bound, "whole-K large scales")
+    W = mixed_weights_f16(K, N, cfg=247)
+    b = synth.bias(N, cfg=247)
+    Wq, s16, z = ORC.quantize_pack_f16(W)
+    y_ref, bound = ORC.w4h_matmul(x, Wq, s16, z, b)
+    s_dev = torch.from_numpy(s16.view(np.float16)).to(DEV)
+    P = w4.w4h_prepack_kmajor(dev(Wq), s_dev, dev(z))
+    assert_bound(host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b))), y_ref, bound,
+                 "whole-K binary16 scales")
+
+
 @pytest.mark.parametrize("slot", range(4))
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_dense38_kmajor_full_size_sampled(slot, M):

@@ -222,7 +222,7 @@ static int check_matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const 
     if (!aligned(x, 16) || !aligned(y, 4) || !aligned(bias, 4) || !aligned(residual, 4))
         return W4_ERR_MISALIGNED;
     // off the matrix cores the GEMV takes rows in groups of 4 on the grid's y axis
-    if (w4::plan_x3(M, K, N).kind != w4::X3Plan::kRun && (M + 3) / 4 > 65535)
+    if (w4::plan_x3(M, K, N).kind == w4::X3Plan::kNone && (M + 3) / 4 > 65535)
         return W4_ERR_BAD_SHAPE;
     const size_t need_ws = w4::plan_x3(M, K, N).workspace;
     if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return W4_ERR_WORKSPACE;
@@ -241,7 +241,7 @@ static int matmul_kmajor_impl(const float *x, int64_t M, int64_t K, const uint8_
     if (M == 0 || N == 0) return W4_OK;
     if ((st = device_check())) return st;
     const w4::X3Plan px = w4::plan_x3(M, K, N);
-    if (K > 0 && px.kind == w4::X3Plan::kRun)
+    if (K > 0 && px.kind != w4::X3Plan::kNone)
         return launched(w4::launch_mm_x3(px, x, M, K, Pq, Ps, f16, Pz, N, bias, residual, act, y,
                                          workspace, as_stream(stream)));
     return launched(w4::launch_gemv_kmajor(w4::plan_kmajor(M, K, N, act == W4_ACT_SWIGLU), x, M,

@@ -13,6 +13,10 @@ int64_t env_int(const char *name) {
     const char *v = getenv(name);
     return v ? atoll(v) : 0;
 }
+int64_t env_int_or(const char *name, int64_t unset) {
+    const char *v = getenv(name);
+    return v ? atoll(v) : unset;
+}
 
 // partial planes part[splits][rows][npad] (fp32)
 size_t splitk_bytes(int64_t splits, int64_t npad, int64_t rows) {
@@ -237,6 +241,37 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     const int64_t min_rows = env_min >= 2 ? env_min : 3;
     // K < 2^22: activation offsets within a row group stay below 2^32 bytes
     if (M < min_rows || K <= 0 || N <= 0 || K % 128 != 0 || K >= ((int64_t)1 << 22)) return p;
+    const int64_t NQ = K / 128;
+    // Up to 8 rows, the whole-K kernel: one launch and no partial sums, as
+    // long as its workgroups (one per 16 nt columns) fill the chip.  Measured
+    // on the 3.8B shapes (kernel trace, per matmul): at M = 4 13.6 / 7.2 /
+    // 17.4 / 14.2 us against 15.9 / 10.8 / 22.6 / 16.2 for the split-K kernel
+    // and its reduce, at M = 8 60 against 67 us per layer; at M = 16 the
+    // split-K kernel is ahead (72 against 75 us per layer), since the whole-K
+    // workgroups each split all 16 activation rows for only 16 columns.
+    // W4_X3K=16 lets it take up to 16 rows, W4_X3K=0 turns it off.
+    static const int64_t env_k = env_int_or("W4_X3K", 8);
+    static const int64_t env_tpw = env_int("W4_X3K_TPW");
+    static const int64_t env_waves = env_int("W4_X3K_WAVES");
+    if (M <= env_k && M <= 16) {
+        const int64_t tpw = env_tpw == 2 ? 2 : 1;
+        const int64_t wgs = cdiv(N, 16 * tpw);
+        if (wgs >= 128) {
+            p.kind = X3Plan::kFullK;
+            p.mb = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+            p.nt = (int)tpw;
+            // 4 waves of 6 quads where K = 3072 at M <= 4 (fewer, longer waves
+            // hide the first loads better); otherwise 8 waves
+            p.waves = NQ <= 8 ? 4 : ((M <= 4 && NQ <= 24) ? 4 : 8);
+            if (env_waves == 4 || env_waves == 8 || env_waves == 16) p.waves = (int)env_waves;
+            if (p.nt == 2 && p.waves == 16) p.waves = 8;  // 1024 threads leave too few registers
+            p.col_wgs = wgs;
+            p.mgroups = 1;
+            p.splits = 1;
+            p.workspace = 0;
+            return p;
+        }
+    }
     p.kind = X3Plan::kRun;
     const int64_t rows = M < 64 ? M : 64;
     p.mt = (int)cdiv(rows, 16);
@@ -258,7 +293,6 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     p.col_wgs = cdiv(N, 64 * p.nt);
     p.mgroups = cdiv(M, 16 * p.mt);
     p.npad = p.col_wgs * 64 * p.nt;
-    const int64_t NQ = K / 128;
     // enough workgroups to fill the chip; larger row tiles carry more matrix
     // work per weight byte, so fewer (and less split-K partial traffic)
     static const int64_t env_wgs = env_int("W4_X3_TARGET_WGS");

@@ -81,8 +81,11 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols = false);
 // grid = col_wgs x splits x mgroups.  dq quads of loads in flight.  Needs
 // K % 128 == 0 and K < 2^22.
 struct X3Plan {
-    enum Kind { kNone = 0, kRun = 1 } kind = kNone;
+    // kRun: the split-K kernel (k_mm_x3, partial sums + reduce);
+    // kFullK: one workgroup per 16 nt columns over all of K (k_mm_x3k)
+    enum Kind { kNone = 0, kRun = 1, kFullK = 2 } kind = kNone;
     int mt = 1, nt = 1, dq = 2;
+    int mb = 4, waves = 4;  // kFullK: rows built, waves per workgroup
     int64_t col_wgs = 0, mgroups = 0, splits = 1, quads_per_wg = 0, npad = 0;
     size_t workspace = 0;
 };

@@ -268,12 +268,267 @@ __global__ __launch_bounds__(256) void k_mm_x3(const float *__restrict__ x, int 
         }
 }
 
+// Whole-K variant for 3 <= M <= 16 rows: one launch per matmul, no partial
+// sums in memory.  A workgroup owns 16 TPW columns and all of K; its W waves
+// take the quads (4 blocks) q = wave, wave + W, ... and their 16 x 16 tiles
+// are added in LDS in wave order at the end (deterministic).  Per quad a
+// wave converts the codes (the 4 x 4 word transpose of k_mm_x3) and builds
+// the bf16 parts of the activations of its own quad in a wave-private LDS
+// image, so the workgroup splits each activation once and needs no barrier
+// inside the K loop.
+//
+// Only the first MB >= M rows of the A operand are built (MB = 4, 8 or 16);
+// A lanes of rows MB .. 15 read row MB - 1 again, and every row >= M is
+// dropped at the store (an MFMA row depends on that row of A only).
+//
+// Exact parts.  The split truncates: h = x with the low 16 bits cleared, r =
+// x - h (exact: the low 16 bits of the significand), m = r truncated the
+// same way, l = r - m.  h, m and l hold 8 significant bits each, so each is
+// exactly a bf16 (the upper half of its fp32 pattern) and x = h + m + l.
+//
+// Codes.  (q - z) is formed as a normal fp16: a nibble in bits 0-3 of a half
+// ORed into 0x6400 (1024) reads as 1024 + q, a nibble in bits 4-7 ORed into
+// 0x5400 (64, mantissa unit 1/16) reads as 64 + q; subtracting 1024 + z or
+// 64 + z in packed fp16 leaves q - z exactly, which widens to fp32 and
+// narrows to bf16 exactly.  So no power of two is carried and each block sum
+// is scaled by s alone.
+template <int TPW, int NBLD>
+struct KQuadLoads {
+    u32x4_t w[TPW];        // codes of block 4 q + g (lane group g), per column tile
+    f32x4_t s[TPW];        // the quad's four block scales
+    uint32_t z[TPW];       // four zero-point nibbles (16 bits)
+    f32x4_t xa[NBLD][2];   // 8 activations per A image this lane builds
+};
+
+// (a & m) | o in one instruction.  VOP3 takes no literal on gfx950, so the
+// compiler would emit an AND and an OR with two literals; with m and o held
+// in registers (loop invariants) it is one v_and_or_b32.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(o));
+    return d;
+}
+
+__device__ __forceinline__ uint32_t hi16_pair(float lo, float hi) {
+    // (upper half of lo) | (upper half of hi) << 16: two truncated bf16
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi),
+                                 __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+__device__ __forceinline__ float trunc_rest(float v) {
+    // v minus v truncated to bf16 (exact)
+    return v - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u);
+}
+
+template <int MB, int TPW, int W, int D, bool H>
+__global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, int M, int K,
+                                                   const uint8_t *__restrict__ Pq,
+                                                   const void *__restrict__ Ps,
+                                                   const uint8_t *__restrict__ Pz, int N,
+                                                   const float *__restrict__ bias,
+                                                   const float *residual, int act, float *y) {
+    constexpr int ABLK = 16 / MB;  // blocks per A image: MB rows x ABLK blocks = 64 lanes x 8
+    constexpr int NBLD = 4 / ABLK;  // A images per quad
+    constexpr int TQ_BYTES = TPW * 64 * 16;
+    constexpr int PART_BYTES = ABLK * MB * 64;
+    constexpr int WAVE_BYTES = TQ_BYTES + 3 * PART_BYTES;
+    static_assert(WAVE_BYTES >= TPW * 64 * 16, "the wave partials fit the wave's area");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[W * WAVE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int NB = K / kBlock, NQ = K / (4 * kBlock), hk = K / 2;
+    const int n0 = blockIdx.x * (16 * TPW);
+    u32x4_t *tq = reinterpret_cast<u32x4_t *>(lds + wave * WAVE_BYTES);
+    unsigned char *img = lds + wave * WAVE_BYTES + TQ_BYTES;
+
+    uint32_t oq[TPW], os[TPW], oz[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int nl = min(n0 + 16 * t + c, N - 1);  // past N: re-read the last column
+        oq[t] = (uint32_t)nl * (uint32_t)hk + 16u * g;
+        os[t] = (uint32_t)nl * (uint32_t)NB;
+        oz[t] = (uint32_t)nl * (uint32_t)(NB / 2);
+    }
+    // A builder: lane = (row bm, image block bb, slot group bg), 8 activations
+    const int bm = lane / (4 * ABLK), bb = (lane >> 2) % ABLK, bg = lane & 3;
+    const uint32_t ox = (uint32_t)min(bm, M - 1) * (uint32_t)K + 32u * bb + 8u * bg;
+    uint32_t *const wimg = reinterpret_cast<uint32_t *>(img + (bb * MB + bm) * 64 + bg * 16);
+    // A reader: lane (g, c) takes row min(c, MB - 1), slots 8 g .. 8 g + 7
+    const int aoff = min(c, MB - 1) * 64 + g * 16;
+
+    const int nq = wave < NQ ? (NQ - 1 - wave) / W + 1 : 0;  // this wave's quads
+    // masks and fp16 bases of the code conversion, in registers
+    uint32_t kLoMask = 0x000F000Fu, kHiMask = 0x00F000F0u, kLoBase = 0x64006400u,
+             kHiBase = 0x54005400u;
+    asm volatile("" : "+v"(kLoMask), "+v"(kHiMask), "+v"(kLoBase), "+v"(kHiBase));
+
+    auto issue = [&](int i, KQuadLoads<TPW, NBLD> &R) {
+        const uint32_t q = (uint32_t)(wave + W * min(i, nq - 1));
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            R.w[t] = load_stream<u32x4_t>(Pq + (oq[t] + 64u * q));
+            if (H) {
+                const u32x2_t h =
+                    load_stream<u32x2_t>(static_cast<const char *>(Ps) + 2u * (os[t] + 4u * q));
+                R.s[t] = f32x4_t{f16_bits_to_f32((uint16_t)h.x), f16_bits_to_f32((uint16_t)(h.x >> 16)),
+                                 f16_bits_to_f32((uint16_t)h.y), f16_bits_to_f32((uint16_t)(h.y >> 16))};
+            } else {
+                R.s[t] = load_stream<f32x4_t>(static_cast<const char *>(Ps) + 4u * (os[t] + 4u * q));
+            }
+            R.z[t] = load_stream<uint16_t>(Pz + (oz[t] + 2u * q));
+        }
+#pragma unroll
+        for (int b = 0; b < NBLD; ++b) {
+            const char *xp = reinterpret_cast<const char *>(x) +
+                             4u * (ox + 128u * q + 32u * ABLK * b);
+            R.xa[b][0] = *reinterpret_cast<const f32x4_t *>(xp);
+            R.xa[b][1] = *reinterpret_cast<const f32x4_t *>(xp + 16);
+        }
+    };
+
+    f32x4v acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    const f32x4v zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    if (nq > 0) {
+        KQuadLoads<TPW, NBLD> L[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(d, L[d]);
+        for (int i0 = 0; i0 < nq; i0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (i0 + d >= nq) break;
+                KQuadLoads<TPW, NBLD> &R = L[d];
+                // codes: lane (g, c) holds block 4 q + g of its column; word g
+                // of block 4 q + blk is with lane (blk, c)
+                uint32_t wq[TPW][4];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    tq[t * 64 + lane] = R.w[t];
+                    const uint32_t *tw = reinterpret_cast<const uint32_t *>(tq + t * 64);
+#pragma unroll
+                    for (int blk = 0; blk < 4; ++blk) wq[t][blk] = tw[(blk * 16 + c) * 4 + g];
+                }
+#pragma unroll
+                for (int b = 0; b < NBLD; ++b) {
+                    // A image b: the three bf16 parts of this lane's 8 activations
+                    const float *f = reinterpret_cast<const float *>(&R.xa[b][0]);
+                    u32x4_t ph, pm, pl;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float a0 = f[2 * p], a1 = f[2 * p + 1];
+                        const float r0 = trunc_rest(a0), r1 = trunc_rest(a1);
+                        ph[p] = hi16_pair(a0, a1);
+                        pm[p] = hi16_pair(r0, r1);
+                        pl[p] = hi16_pair(trunc_rest(r0), trunc_rest(r1));
+                    }
+                    *reinterpret_cast<u32x4_t *>(wimg) = ph;
+                    *reinterpret_cast<u32x4_t *>(wimg + PART_BYTES / 4) = pm;
+                    *reinterpret_cast<u32x4_t *>(wimg + 2 * PART_BYTES / 4) = pl;
+#pragma unroll
+                    for (int ib = 0; ib < ABLK; ++ib) {
+                        const int blk = b * ABLK + ib;
+                        const unsigned char *ap = img + ib * MB * 64 + aoff;
+                        const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
+                        const bf16x8_t am = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PART_BYTES));
+                        const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + 2 * PART_BYTES));
+#pragma unroll
+                        for (int t = 0; t < TPW; ++t) {
+                            const uint32_t w = wq[t][blk];
+                            const uint32_t z = (R.z[t] >> (4 * blk)) & 15u;
+                            const half2_t zE = as_half2((0x6400u | z) * 0x00010001u);
+                            const half2_t zO = as_half2((0x5400u | (z << 4)) * 0x00010001u);
+                            const uint32_t hv = w >> 8;
+                            const half2_t e0 = as_half2(and_or(w, kLoMask, kLoBase)) - zE;   // k 0, 4
+                            const half2_t o0 = as_half2(and_or(w, kHiMask, kHiBase)) - zO;   // k 1, 5
+                            const half2_t e1 = as_half2(and_or(hv, kLoMask, kLoBase)) - zE;  // k 2, 6
+                            const half2_t o1 = as_half2(and_or(hv, kHiMask, kHiBase)) - zO;  // k 3, 7
+                            const u32x4_t bw = {pack_bf16((float)e0.x, (float)o0.x),
+                                                pack_bf16((float)e1.x, (float)o1.x),
+                                                pack_bf16((float)e0.y, (float)o0.y),
+                                                pack_bf16((float)e1.y, (float)o1.y)};
+                            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+                            f32x4v dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, zero4, 0, 0, 0);
+                            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bv, dd, 0, 0, 0);
+                            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, dd, 0, 0, 0);
+                            const float sc = R.s[t][blk];
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(sc, dd[v], acc[t][v]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(acc[t][v]));
+                if (i0 + d + D < nq) issue(i0 + d + D, R);
+            }
+        }
+    }
+
+    // Wave partials through LDS (over the waves' areas, once every wave is
+    // done with them), added in wave order.  Lane (g, c) of tile t holds
+    // rows 4 g .. 4 g + 3 of column 16 t + c.
+    __syncthreads();
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) red[(wave * TPW + t) * 64 + lane] = f32x4_t{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+    __syncthreads();
+    const float *rf = reinterpret_cast<const float *>(lds);
+    auto total = [&](int m, int nl) {
+        const int idx = ((nl >> 4) * 64 + (m >> 2) * 16 + (nl & 15)) * 4 + (m & 3);
+        float v = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) v += rf[w2 * TPW * 256 + idx];
+        return v;
+    };
+    constexpr int CW = 16 * TPW;
+    if (act == W4_ACT_SWIGLU) {
+        for (int o = tid; o < M * (CW / 2); o += 64 * W) {
+            const int m = o / (CW / 2), nl = 2 * (o % (CW / 2)), n = n0 + nl;
+            if (n >= N) continue;
+            const float gate = total(m, nl) + (bias ? bias[n] : 0.0f);
+            const float up = total(m, nl + 1) + (bias ? bias[n + 1] : 0.0f);
+            ep_store_glu(gate, up, residual, y, (size_t)m * (N / 2) + n / 2);
+        }
+    } else {
+        for (int o = tid; o < M * CW; o += 64 * W) {
+            const int m = o / CW, nl = o % CW, n = n0 + nl;
+            if (n >= N) continue;
+            ep_store(total(m, nl) + (bias ? bias[n] : 0.0f), act, residual, y, (size_t)m * N + n);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                         const void *Ps, bool f16, const uint8_t *Pz, int64_t N, const float *bias,
                         const float *residual, int act, float *y, void *workspace,
                         hipStream_t stream) {
+    if (p.kind == X3Plan::kFullK) {
+        const dim3 grid((unsigned)p.col_wgs);
+        bool done = false;
+#define W4_X3K(MBV, TPWV, WV, DV)                                                                  \
+    if (!done && p.mb == MBV && p.nt == TPWV && p.waves == WV) {                                    \
+        if (f16)                                                                                    \
+            hipLaunchKernelGGL((k_mm_x3k<MBV, TPWV, WV, DV, true>), grid, dim3(64 * WV), 0, stream, \
+                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);      \
+        else                                                                                        \
+            hipLaunchKernelGGL((k_mm_x3k<MBV, TPWV, WV, DV, false>), grid, dim3(64 * WV), 0, stream, \
+                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);      \
+        done = true;                                                                                \
+    }
+#define W4_X3K_W(MBV, TPWV, DV) W4_X3K(MBV, TPWV, 4, DV) W4_X3K(MBV, TPWV, 8, DV)
+        W4_X3K_W(4, 1, 4) W4_X3K_W(4, 2, 3) W4_X3K_W(8, 1, 3) W4_X3K_W(8, 2, 2)
+        W4_X3K_W(16, 1, 2) W4_X3K_W(16, 2, 2)
+        W4_X3K(4, 1, 16, 4) W4_X3K(8, 1, 16, 3) W4_X3K(16, 1, 16, 2)
+#undef W4_X3K_W
+#undef W4_X3K
+        if (!done) return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)p.col_wgs, (unsigned)p.splits, (unsigned)p.mgroups);
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     bool launched = false;
