@@ -252,7 +252,8 @@ def parse():
                         "a plain copy of known size for calibration")
     p.add_argument("--profile-run-mfma", action="store_true",
                    help="short eager run for matrix-core counters: `--steps` passes of the "
-                        "3.8B body at M=16 on both layouts and of the GPT-2 prefill at M=58")
+                        "3.8B body at M=4 (prepacked) and M=16 (both layouts) and of the "
+                        "GPT-2 prefill at M=58")
     p.add_argument("--summarize-profiles", metavar="DIR", default=None,
                    help="turn rocprofv3 CSV output under DIR into the profile summaries")
     p.add_argument("--out", default=PROFILE_DIR, help="where --summarize-profiles writes")
@@ -415,9 +416,11 @@ def main():
         # the bf16 kernel; canonical: fp32 MFMA), GPT-2 body at M = 58
         # (prepacked: the bf16 kernel)
         d16 = with_x(dense, synth.CFG_DENSE38, 16, outliers=True)
+        d4 = with_x(dense, synth.CFG_DENSE38, 4, outliers=True)
         gpt2 = build_body("gpt2", synth.CFG_GPT2_DECODE, 1, with_bias=True, outliers=False)
         pre = with_x(gpt2, synth.CFG_GPT2_PREFILL, synth.GPT2_PROMPT, outliers=False)
-        for mats, layout, what in ((d16, "kmajor", "3.8B M=16 prepacked"),
+        for mats, layout, what in ((d4, "kmajor", "3.8B M=4 prepacked"),
+                                   (d16, "kmajor", "3.8B M=16 prepacked"),
                                    (d16, "canonical", "3.8B M=16 canonical"),
                                    (pre, "kmajor", "GPT-2 M=58 prepacked")):
             run_pass(mats, layout=layout)
@@ -572,7 +575,9 @@ def main():
                           "TFLOP_s": round(flm / (msm * 1e-3) / 1e12, 3)}
                 if layout == "kmajor":
                     line_m["roofline"] = own_roofline(dm, msm, 16)
-                    line_m["kernel"] = "k_mm_x3 (bf16 x3 matrix cores, exact operands)"
+                    line_m["kernel"] = ("k_mm_x3k (whole-K, one launch per matmul; "
+                                        if Mb <= 8 else "k_mm_x3 (split-K + reduce; ") + \
+                        "bf16 x3 matrix cores, exact operands)"
                 else:
                     line_m["frac_fp32_mfma_peak"] = round(
                         flm / (msm * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
@@ -1016,14 +1021,16 @@ def summarize_profiles(src: str, out_dir: str):
         kern.setdefault(d["k"], []).append(d)
     lines = ["# Matrix-core utilisation of the M > 1 kernels", "", "Made by:", "", cmds, "",
              "Counters per dispatch of `--profile-run-mfma` (eager passes: the 3.8B body at "
-             "M = 16 on the prepacked and the canonical layout, the GPT-2 body at M = 58 "
-             "prepacked).  `MfmaUtil` is rocprofv3's derived metric: MFMA-busy cycles over "
-             "active cycles times SIMDs, in percent.  MFMA FLOP/s count the matrix-core "
-             "operations the kernel issued (MOPS x 512 over the dispatch's duration under "
-             "counter collection): `k_mm_x3` issues three bf16 MFMAs per fp32 product "
-             "(exact three-part splits of each activation) on whole 16-row tiles, so its "
-             "useful fp32 rate is at most a third of its bf16 rate; `k_mm_mfma` runs fp32 "
-             "MFMA.  Peaks: bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s (dense).", "",
+             "M = 4 prepacked, at M = 16 on the prepacked and the canonical layout, the "
+             "GPT-2 body at M = 58 prepacked).  `MfmaUtil` is rocprofv3's derived metric: "
+             "MFMA-busy cycles over active cycles times SIMDs, in percent.  MFMA FLOP/s "
+             "count the matrix-core operations the kernel issued (MOPS x 512 over the "
+             "dispatch's duration under counter collection): `k_mm_x3` (split-K) and "
+             "`k_mm_x3k` (whole-K, up to 8 rows) issue three bf16 MFMAs per fp32 product "
+             "(exact three-part splits of each activation) on whole 16-row tiles, so their "
+             "useful fp32 rate is at most a third of the bf16 rate, and at M = 4 a quarter "
+             "of that again; `k_mm_mfma` runs fp32 MFMA.  Peaks: bf16 2.5 PFLOP/s, fp32 "
+             "157.3 TFLOP/s (dense).", "",
              "| kernel | dispatches | MfmaUtil % (mean) | fp16 MFMA TFLOP/s | "
              "bf16 MFMA TFLOP/s | fp32 MFMA TFLOP/s | avg us |",
              "|---|---|---|---|---|---|---|"]
