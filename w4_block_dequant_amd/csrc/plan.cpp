@@ -260,11 +260,19 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
             p.kind = X3Plan::kFullK;
             p.mb = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
             p.nt = (int)tpw;
-            // 4 waves of 6 quads where K = 3072 at M <= 4 (fewer, longer waves
-            // hide the first loads better); otherwise 8 waves
-            p.waves = NQ <= 8 ? 4 : ((M <= 4 && NQ <= 24) ? 4 : 8);
+            // 8 waves, each loading one quad ahead of its arithmetic; 4 where K
+            // is short.  3.8B pass (128 launches) at M = 4 / 8: 4 quads ahead
+            // 1.68 / 1.93 ms, 2 ahead 1.55 / 1.85, 1 ahead 1.50 / 1.77 ms (4 or
+            // 16 waves at 1 ahead: 1.87 / 1.71 ms at M = 4): a deep prefetch
+            // makes every wave's first quad wait behind the others' later
+            // ones, while the arithmetic (about 6 VALU operations per weight)
+            // could have started.
+            p.waves = NQ <= 8 ? 4 : 8;
             if (env_waves == 4 || env_waves == 8 || env_waves == 16) p.waves = (int)env_waves;
             if (p.nt == 2 && p.waves == 16) p.waves = 8;  // 1024 threads leave too few registers
+            // quads of loads in flight per wave (0: the kernel's default for its row count)
+            static const int64_t env_d = env_int("W4_X3K_D");
+            p.dq = (env_d >= 1 && env_d <= 4) ? (int)env_d : 0;
             p.col_wgs = wgs;
             p.mgroups = 1;
             p.splits = 1;
@@ -288,8 +296,12 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     if (env_mt >= 1 && env_mt <= 4) p.mt = (int)(env_mt < cdiv(rows, 16) ? env_mt : cdiv(rows, 16));
     static const int64_t env_nt = env_int("W4_X3_NT");
     p.nt = (env_nt == 2 && p.mt <= 2) ? 2 : 1;
-    p.dq = p.mt <= 2 ? 3 : 2;
+    // quads of loads in flight ahead of the arithmetic (one 16-row tile: 2,
+    // 2.196 -> 2.175 ms per M = 16 3.8B pass against 3)
+    p.dq = p.mt == 1 && p.nt == 1 ? 2 : (p.mt <= 2 ? 3 : 2);
     if (p.mt == 2 && p.nt == 2) p.dq = 2;
+    static const int64_t env_dq = env_int("W4_X3_DQ");
+    if (p.mt == 1 && p.nt == 1 && env_dq >= 1 && env_dq <= 3) p.dq = (int)env_dq;
     p.col_wgs = cdiv(N, 64 * p.nt);
     p.mgroups = cdiv(M, 16 * p.mt);
     p.npad = p.col_wgs * 64 * p.nt;

@@ -511,7 +511,7 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
         const dim3 grid((unsigned)p.col_wgs);
         bool done = false;
 #define W4_X3K(MBV, TPWV, WV, DV)                                                                  \
-    if (!done && p.mb == MBV && p.nt == TPWV && p.waves == WV) {                                    \
+    if (!done && p.mb == MBV && p.nt == TPWV && p.waves == WV && (p.dq == DV || p.dq == 0)) {      \
         if (f16)                                                                                    \
             hipLaunchKernelGGL((k_mm_x3k<MBV, TPWV, WV, DV, true>), grid, dim3(64 * WV), 0, stream, \
                                x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);      \
@@ -521,9 +521,12 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
         done = true;                                                                                \
     }
 #define W4_X3K_W(MBV, TPWV, DV) W4_X3K(MBV, TPWV, 4, DV) W4_X3K(MBV, TPWV, 8, DV)
-        W4_X3K_W(4, 1, 4) W4_X3K_W(4, 2, 3) W4_X3K_W(8, 1, 3) W4_X3K_W(8, 2, 2)
-        W4_X3K_W(16, 1, 2) W4_X3K_W(16, 2, 2)
-        W4_X3K(4, 1, 16, 4) W4_X3K(8, 1, 16, 3) W4_X3K(16, 1, 16, 2)
+#define W4_X3K_W3(MBV, DV) W4_X3K(MBV, 1, 4, DV) W4_X3K(MBV, 1, 8, DV) W4_X3K(MBV, 1, 16, DV)
+        // the first instantiation of a row count is its default depth
+        W4_X3K_W3(4, 1) W4_X3K_W3(4, 2) W4_X3K_W3(4, 4) W4_X3K_W(4, 2, 3)
+        W4_X3K_W3(8, 1) W4_X3K_W3(8, 2) W4_X3K_W(8, 2, 2)
+        W4_X3K_W3(16, 1) W4_X3K_W3(16, 2) W4_X3K_W(16, 2, 2)
+#undef W4_X3K_W3
 #undef W4_X3K_W
 #undef W4_X3K
         if (!done) return hipErrorInvalidValue;
@@ -533,7 +536,7 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     bool launched = false;
 #define W4_X3(MTV, NTV, QV, DQV)                                                                \
-    if (!launched && p.mt == MTV && p.nt == NTV && p.quads_per_wg == QV) {                      \
+    if (!launched && p.mt == MTV && p.nt == NTV && p.quads_per_wg == QV && p.dq == DQV) {       \
         if (f16)                                                                                \
             hipLaunchKernelGGL((k_mm_x3<MTV, NTV, QV, DQV, true>), grid, dim3(256), 0, stream, x, \
                                (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y,       \
@@ -548,8 +551,8 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
     W4_X3(MTV, NTV, 1, DQV) W4_X3(MTV, NTV, 2, DQV) W4_X3(MTV, NTV, 3, DQV)                     \
     W4_X3(MTV, NTV, 4, DQV) W4_X3(MTV, NTV, 6, DQV) W4_X3(MTV, NTV, 8, DQV)                     \
     W4_X3(MTV, NTV, 12, DQV)
-    W4_X3_Q(1, 1, 3) W4_X3_Q(2, 1, 3) W4_X3_Q(3, 1, 2) W4_X3_Q(4, 1, 2)
-    W4_X3_Q(1, 2, 3) W4_X3_Q(2, 2, 2)
+    W4_X3_Q(1, 1, 2) W4_X3_Q(2, 1, 3) W4_X3_Q(3, 1, 2) W4_X3_Q(4, 1, 2)
+    W4_X3_Q(1, 2, 3) W4_X3_Q(2, 2, 2) W4_X3_Q(1, 1, 1) W4_X3_Q(1, 1, 3)
 #undef W4_X3_Q
 #undef W4_X3
     if (!launched) return hipErrorInvalidValue;
