@@ -174,7 +174,7 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
  * terms, so every product is exact and only the fp32 accumulation rounds;
  * the block's scale is applied once per block and column.  This holds for
  * any finite x, whatever its range.  Non-finite x gives NaN outputs on this
- * path.  Up to 8 rows with N >= 2033 one workgroup takes 16 columns over all
+ * path.  Up to 16 rows with N >= 2033 one workgroup takes 16 or 32 columns over all
  * of K (one launch, no workspace); otherwise it may split K across
  * workgroups and then needs a workspace of
  * w4_matmul_kmajor_workspace_bytes(M, K, N) bytes (0 when it does not):

@@ -631,16 +631,18 @@ def test_kmajor_matrix_cores_deterministic_with_dirty_workspace():
     assert_bits(y1, y2, "x3 repeat")
 
 
-# The whole-K matrix-core kernel (3 <= M <= 8 rows, N >= 2033: one
-# workgroup per 16 columns over all of K, no workspace).  K = 128 and 256
-# leave waves of a workgroup with no quads; 2050, 3080 and 2344 are ragged N;
-# 8192 gives 16 quads per wave; M = 3 and 5..8 exercise the row padding of
-# the 4- and 8-row activation images.
-WHOLE_K_SHAPES = [(128, 2048), (256, 2050), (384, 2344), (3072, 3080), (8192, 2064)]
+# The whole-K matrix-core kernel (3 <= M <= 16 rows, N >= 2033: one
+# workgroup per 16 columns, or 32 from 5 rows where N >= 16353, over all of
+# K, no workspace).  K = 128 and 256 leave waves of a workgroup with no
+# quads; 2050, 3080, 2344 and 16400 are ragged N (16400: two column tiles per
+# wave, a half-empty last workgroup); 8192 gives 8 quads per wave; M = 3,
+# 5..8 and 12 exercise the row padding of the 4-, 8- and 16-row images.
+WHOLE_K_SHAPES = [(128, 2048), (256, 2050), (384, 2344), (3072, 3080), (8192, 2064),
+                  (128, 16400)]
 
 
 @pytest.mark.parametrize("K,N", WHOLE_K_SHAPES)
-@pytest.mark.parametrize("M", [3, 4, 5, 6, 8])
+@pytest.mark.parametrize("M", [3, 4, 5, 6, 8, 12, 16])
 def test_kmajor_whole_k_kernel(M, K, N):
     assert w4.w4_matmul_kmajor_workspace_bytes(M, K, N) == 0
     note(f"kmajor whole-K M={M} K={K} N={N}")
@@ -657,9 +659,8 @@ def test_kmajor_whole_k_kernel(M, K, N):
 
 
 @pytest.mark.parametrize("act,res", [("gelu", False), ("swiglu", True), ("none", True)])
-@pytest.mark.parametrize("M", [4, 7])
-def test_kmajor_whole_k_epilogue(M, act, res):
-    K, N = 384, 2344
+@pytest.mark.parametrize("M,K,N", [(4, 384, 2344), (7, 384, 2344), (12, 128, 16400)])
+def test_kmajor_whole_k_epilogue(M, K, N, act, res):
     note(f"kmajor whole-K epilogue M={M} act={act} residual={res}")
     W = mixed_weights(K, N, cfg=243)
     x = synth.activations(M, K, cfg=243, slot=M, outliers=True)

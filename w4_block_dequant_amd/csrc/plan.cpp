@@ -242,19 +242,24 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     // K < 2^22: activation offsets within a row group stay below 2^32 bytes
     if (M < min_rows || K <= 0 || N <= 0 || K % 128 != 0 || K >= ((int64_t)1 << 22)) return p;
     const int64_t NQ = K / 128;
-    // Up to 8 rows, the whole-K kernel: one launch and no partial sums, as
+    // Up to 16 rows, the whole-K kernel: one launch and no partial sums, as
     // long as its workgroups (one per 16 nt columns) fill the chip.  Measured
-    // on the 3.8B shapes (kernel trace, per matmul): at M = 4 13.6 / 7.2 /
-    // 17.4 / 14.2 us against 15.9 / 10.8 / 22.6 / 16.2 for the split-K kernel
-    // and its reduce, at M = 8 60 against 67 us per layer; at M = 16 the
-    // split-K kernel is ahead (72 against 75 us per layer), since the whole-K
-    // workgroups each split all 16 activation rows for only 16 columns.
-    // W4_X3K=16 lets it take up to 16 rows, W4_X3K=0 turns it off.
-    static const int64_t env_k = env_int_or("W4_X3K", 8);
+    // on the 3.8B shapes (kernel trace, us per matmul for 3072x9216 /
+    // 3072x3072 / 3072x16384 / 8192x3072): at M = 8 14.8 / 6.9 / 17.2 / 14.4
+    // against 16.3 / 10.7 / 24.1 / 16.5 for the split-K kernel and its
+    // reduce; at M = 16 19.0 / 8.1 / 20.2 / 18.0 against 18.2 / 11.2 / 24.8 /
+    // 17.9.  W4_X3K=n caps it at n rows (0 turns it off).
+    static const int64_t env_k = env_int_or("W4_X3K", 16);
     static const int64_t env_tpw = env_int("W4_X3K_TPW");
     static const int64_t env_waves = env_int("W4_X3K_WAVES");
     if (M <= env_k && M <= 16) {
-        const int64_t tpw = env_tpw == 2 ? 2 : 1;
+        // two column tiles per wave (each activation split serves 32 columns)
+        // from 5 rows on, where that still leaves 512 workgroups: 3072x16384
+        // at M = 8 19.9 -> 17.2 us, at M = 16 25.4 -> 20.2; at M = 4 and on
+        // 3072x9216 (288 workgroups) one tile is ahead
+        int64_t tpw = (M > 4 && cdiv(N, 32) >= 512) ? 2 : 1;
+        if (env_tpw == 1 || env_tpw == 2) tpw = env_tpw;
+        if (tpw == 2 && cdiv(N, 32) < 128) tpw = 1;
         const int64_t wgs = cdiv(N, 16 * tpw);
         if (wgs >= 128) {
             p.kind = X3Plan::kFullK;

@@ -523,9 +523,9 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
 #define W4_X3K_W(MBV, TPWV, DV) W4_X3K(MBV, TPWV, 4, DV) W4_X3K(MBV, TPWV, 8, DV)
 #define W4_X3K_W3(MBV, DV) W4_X3K(MBV, 1, 4, DV) W4_X3K(MBV, 1, 8, DV) W4_X3K(MBV, 1, 16, DV)
         // the first instantiation of a row count is its default depth
-        W4_X3K_W3(4, 1) W4_X3K_W3(4, 2) W4_X3K_W3(4, 4) W4_X3K_W(4, 2, 3)
-        W4_X3K_W3(8, 1) W4_X3K_W3(8, 2) W4_X3K_W(8, 2, 2)
-        W4_X3K_W3(16, 1) W4_X3K_W3(16, 2) W4_X3K_W(16, 2, 2)
+        W4_X3K_W3(4, 1) W4_X3K_W3(4, 2) W4_X3K_W3(4, 4) W4_X3K_W(4, 2, 1) W4_X3K_W(4, 2, 3)
+        W4_X3K_W3(8, 1) W4_X3K_W3(8, 2) W4_X3K_W(8, 2, 1) W4_X3K_W(8, 2, 2)
+        W4_X3K_W3(16, 1) W4_X3K_W3(16, 2) W4_X3K_W(16, 2, 1) W4_X3K_W(16, 2, 2)
 #undef W4_X3K_W3
 #undef W4_X3K_W
 #undef W4_X3K
