@@ -169,8 +169,11 @@ __global__ __launch_bounds__(256) void k_head_fp32(const float *__restrict__ x, 
 // v_mfma_f32_16x16x32_bf16 forms exact products and only its fp32
 // accumulation rounds, as in the fp32 kernel; hs[n] is applied at the end.
 //
-// One wave owns 16 tokens (lane c = lane % 16 is token t0 + c) for all rows;
-// a workgroup of WAVES waves shares each tile's activation parts.
+// One wave owns 16 TT tokens (lane c = lane % 16 is token t0 + 16 tt + c of
+// token tile tt) for all rows; a workgroup of WAVES waves shares each row
+// tile's activation parts.  With TT = 2 every A read from LDS feeds the MFMAs
+// of both token tiles (half the LDS traffic per product); the codes then stay
+// in registers as the int8 bytes they are and are widened to bf16 per step.
 // Lane group g = lane / 16 owns the contiguous k range [g KQ, (g + 1) KQ) of
 // the padded K (KP = 4 KQ, a multiple of 64), 8 k per MFMA step: its codes
 // come in whole 16-byte loads, are turned into bf16 once and stay in
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256) void k_head_fp32(const float *__restrict__ x, 
 // spreads the rows over the LDS banks), built once per workgroup; the A
 // operand of step s for lane (g, r) is row r's parts at k = g KQ + 8 s.
 // Rows with a non-finite entry are flagged while they are built and give NaN.
-template <int SMAX, int WAVES>
+template <int SMAX, int WAVES, int TT>
 __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__restrict__ x, int M, int K,
                                                       const int8_t *__restrict__ Qt, int ldt,
                                                       const float *__restrict__ hs, int N,
@@ -193,13 +196,29 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
     uint16_t *ap = reinterpret_cast<uint16_t *>(aplane_v);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
-    const int t0 = (blockIdx.x * WAVES + wave) * 16;
+    const int t0 = (blockIdx.x * WAVES + wave) * 16 * TT;
     const int KP = (K + 63) / 64 * 64, KQ = KP / 4, S = KQ / 8, RS = KP + 8;
     const int n = min(t0 + c, N - 1);
 
-    // codes of this lane's token and k range, as bf16 pairs: step s uses b[s]
-    u32x4_t b[SMAX];
-    {
+    // TT = 2: the codes of both token tiles as loaded, 16 bytes per two steps
+    // (the compiler widens them to bf16 once, outside the row-tile loop)
+    u32x4_t qb[TT == 2 ? 2 : 1][TT == 2 ? SMAX / 2 : 1];
+    float hsn2[2] = {0.0f, 0.0f};
+    if (TT == 2) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int nt = min(t0 + 16 * tt + c, N - 1);
+            const int8_t *row = Qt + (size_t)nt * ldt;
+#pragma unroll
+            for (int j = 0; j < SMAX / 2; ++j)
+                if (2 * j < S)
+                    qb[tt][j] = *reinterpret_cast<const u32x4_t *>(row + min(g * KQ + 16 * j, ldt - 16));
+            hsn2[tt] = hs[nt];
+        }
+    }
+    // TT = 1: codes of this lane's token and k range, as bf16 pairs: step s uses b[s]
+    u32x4_t b[TT == 1 ? SMAX : 1];
+    if (TT == 1) {
         const int8_t *row = Qt + (size_t)n * ldt;
 #pragma unroll
         for (int j = 0; j < SMAX / 2; ++j) {
@@ -226,7 +245,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
             }
         }
     }
-    const float hsn = hs[n];
+    const float hsn = TT == 1 ? hs[n] : 0.0f;
+    // 8 int8 codes (two dwords) as four bf16 pairs
+    auto widen = [](uint32_t w0, uint32_t w1) {
+        const uint32_t w[2] = {w0, w1};
+        uint32_t o[4];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float lo = (float)(int)(int8_t)(w[d] >> (16 * h));
+                const float hi = (float)(int)(int8_t)(w[d] >> (16 * h + 8));
+                o[2 * d + h] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi),
+                                                     __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+            }
+        return u32x4_t{o[0], o[1], o[2], o[3]};
+    };
     const int K8 = KP / 8;  // 8-element pieces per row
 
     for (int m0 = 0; m0 < M; m0 += 16) {
@@ -269,8 +303,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
             *reinterpret_cast<u32x4_t *>(ap + (2 * 16 + r) * RS + k) = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
         }
         __syncthreads();
-        // two accumulators (even and odd steps): two independent MFMA chains
-        f32x4v acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // two accumulators per token tile (even and odd steps): independent
+        // MFMA chains
+        f32x4v acc2[TT][2];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc2[tt][0] = acc2[tt][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < SMAX; ++s) {
             if (s < S) {
@@ -278,21 +315,35 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
                 const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (2 * 16 + c) * RS + k));
                 const bf16x8_t am = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (1 * 16 + c) * RS + k));
                 const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (0 * 16 + c) * RS + k));
-                const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b[s]);
-                f32x4v &a = acc2[s & 1];
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, a, 0, 0, 0);
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bb, a, 0, 0, 0);
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, a, 0, 0, 0);
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+                    u32x4_t bw;
+                    if (TT == 1) {
+                        bw = b[s];
+                    } else {
+                        const u32x4_t v = qb[tt][s >> 1];
+                        bw = (s & 1) ? widen(v.z, v.w) : widen(v.x, v.y);
+                    }
+                    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bw);
+                    f32x4v &a = acc2[tt][s & 1];
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bb, a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, a, 0, 0, 0);
+                }
             }
         }
-        const f32x4v acc = acc2[0] + acc2[1];
-        // lane (g, c) holds D[4 g + v][c]: row m0 + 4 g + v, token t0 + c
-        const int t = t0 + c;
+        // lane (g, c) holds D[4 g + v][c]: row m0 + 4 g + v, token t0 + 16 tt + c
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = m0 + 4 * g + v;
-            if (m < M && t < N)
-                logits[(size_t)m * N + t] = rowbad[4 * g + v] ? __builtin_nanf("") : acc[v] * hsn;
+        for (int tt = 0; tt < TT; ++tt) {
+            const f32x4v acc = acc2[tt][0] + acc2[tt][1];
+            const int t = t0 + 16 * tt + c;
+            const float hv = TT == 1 ? hsn : hsn2[tt];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + 4 * g + v;
+                if (m < M && t < N)
+                    logits[(size_t)m * N + t] = rowbad[4 * g + v] ? __builtin_nanf("") : acc[v] * hv;
+            }
         }
     }
 }
@@ -363,25 +414,50 @@ hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const i
     const int64_t KP = (K + 63) / 64 * 64;
     if (M < 4 || KP > 1024) return launch_head_fp32(x, M, K, Qt, ldt, hs, N, logits, stream);
     const size_t shm = (size_t)3 * 16 * (KP + 8) * 2;
-    // 8 waves (128 tokens) per workgroup: each tile's activation parts are
-    // built once for twice the tokens of a 4-wave workgroup
-    constexpr int WV = 8;
-    const dim3 grid((unsigned)((N + 16 * WV - 1) / (16 * WV)));
+    // waves per workgroup and token tiles per wave (each tile's activation
+    // parts are built once per workgroup, each LDS read of them feeds TT
+    // token tiles).  58 x 768 x 50257: one tile, 8 waves 55.4 us; two tiles,
+    // 4 waves 41.4 us, 8 waves 37.9 us (130 rows: 105 -> 63 us).  The reads
+    // of the activation parts from LDS were the bound.
+    static const int env_tt = (int)(getenv("W4_HEAD_TT") ? atoi(getenv("W4_HEAD_TT")) : 2);
+    static const int env_wv = (int)(getenv("W4_HEAD_WAVES") ? atoi(getenv("W4_HEAD_WAVES")) : 8);
+    // two tiles hold the widened codes of at most 24 steps (K <= 768) in
+    // registers; four tiles (bytes widened per step, one wave per SIMD) took
+    // 50.1 us
+    const int TTv = (env_tt == 1 || KP > 768) ? 1 : 2;
+    const int WVv = env_wv == 8 ? 8 : 4;
+    const int tokens = 16 * TTv * WVv;
+    const dim3 grid((unsigned)((N + tokens - 1) / tokens));
     const int S = (int)(KP / 32);  // MFMA steps per lane group
     // more than 64 KB of dynamic LDS (K above 640) is allowed once per kernel
-#define W4_HR(SV)                                                                                 \
+#define W4_HR(SV, WV, TTV)                                                                        \
     do {                                                                                          \
         static const hipError_t attr = hipFuncSetAttribute(                                      \
-            reinterpret_cast<const void *>(&k_head_rows_x3<SV, WV>),                             \
+            reinterpret_cast<const void *>(&k_head_rows_x3<SV, WV, TTV>),                        \
             hipFuncAttributeMaxDynamicSharedMemorySize, 3 * 16 * (32 * SV + 8) * 2);             \
         if (attr != hipSuccess) return attr;                                                      \
-        hipLaunchKernelGGL((k_head_rows_x3<SV, WV>), grid, dim3(64 * WV), shm, stream, x,         \
+        hipLaunchKernelGGL((k_head_rows_x3<SV, WV, TTV>), grid, dim3(64 * WV), shm, stream, x,    \
                            (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits);                     \
     } while (0)
-    if (S <= 8) W4_HR(8);
-    else if (S <= 16) W4_HR(16);
-    else if (S <= 24) W4_HR(24);
-    else W4_HR(32);
+#define W4_HR_S(WV, TTV)                                                                          \
+    do {                                                                                          \
+        if (S <= 8) W4_HR(8, WV, TTV);                                                            \
+        else if (S <= 16) W4_HR(16, WV, TTV);                                                     \
+        else if (S <= 24) W4_HR(24, WV, TTV);                                                     \
+        else W4_HR(32, WV, TTV);                                                                  \
+    } while (0)
+    if (TTv == 1 && WVv == 8) W4_HR_S(8, 1);
+    else if (TTv == 1) W4_HR_S(4, 1);
+    else if (WVv == 8) {
+        if (S <= 8) W4_HR(8, 8, 2);
+        else if (S <= 16) W4_HR(16, 8, 2);
+        else W4_HR(24, 8, 2);
+    } else {
+        if (S <= 8) W4_HR(8, 4, 2);
+        else if (S <= 16) W4_HR(16, 4, 2);
+        else W4_HR(24, 4, 2);
+    }
+#undef W4_HR_S
 #undef W4_HR
     return hipGetLastError();
 }
