@@ -174,13 +174,16 @@ __global__ __launch_bounds__(256) void k_head_fp32(const float *__restrict__ x, 
 // tile's activation parts.  With TT = 2 every A read from LDS feeds the MFMAs
 // of both token tiles (half the LDS traffic per product); the codes then stay
 // in registers as the int8 bytes they are and are widened to bf16 per step.
-// Lane group g = lane / 16 owns the contiguous k range [g KQ, (g + 1) KQ) of
-// the padded K (KP = 4 KQ, a multiple of 64), 8 k per MFMA step: its codes
+// Lane group g = lane / 16 owns bytes 16 g .. 16 g + 15 of every 64-byte piece
+// of the padded K (KP, a multiple of 64), 8 k per MFMA step: its codes
 // come in whole 16-byte loads, are turned into bf16 once and stay in
 // registers (4 dwords per step).  The rows pass through LDS one 16-row tile
 // at a time as three bf16 part planes [part][row][KP + 8] (the 8-element pad
 // spreads the rows over the LDS banks), built once per workgroup; the A
-// operand of step s for lane (g, r) is row r's parts at k = g KQ + 8 s.
+// operand of step s for lane (g, r) is row r's parts at k = 64 (s / 2) +
+// 16 g + 8 (s % 2).  So a code load instruction reads 64 contiguous bytes of
+// each of 16 token rows (a lane group's quarter of K in one run would touch
+// 64 cache lines per instruction instead).
 // Rows with a non-finite entry are flagged while they are built and give NaN.
 template <int SMAX, int WAVES, int TT>
 __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__restrict__ x, int M, int K,
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int t0 = (blockIdx.x * WAVES + wave) * 16 * TT;
-    const int KP = (K + 63) / 64 * 64, KQ = KP / 4, S = KQ / 8, RS = KP + 8;
+    const int KP = (K + 63) / 64 * 64, S = KP / 32, RS = KP + 8;
     const int n = min(t0 + c, N - 1);
 
     // TT = 2: the codes of both token tiles as loaded, 16 bytes per two steps
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
 #pragma unroll
             for (int j = 0; j < SMAX / 2; ++j)
                 if (2 * j < S)
-                    qb[tt][j] = *reinterpret_cast<const u32x4_t *>(row + min(g * KQ + 16 * j, ldt - 16));
+                    qb[tt][j] = *reinterpret_cast<const u32x4_t *>(row + min(64 * j + 16 * g, ldt - 16));
             hsn2[tt] = hs[nt];
         }
     }
@@ -223,9 +226,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
 #pragma unroll
         for (int j = 0; j < SMAX / 2; ++j) {
             if (2 * j < S) {
-                const int k0 = min(g * KQ + 16 * j, ldt - 16);  // past K: a valid piece, zero A
-                // ordinary (cached) loads: one load instruction covers 16 bytes
-                // of 64 different lines, which the next ones finish
+                const int k0 = min(64 * j + 16 * g, ldt - 16);  // past K: a valid piece, zero A
+                // ordinary (cached) loads: a load instruction covers 64
+                // contiguous bytes of each of 16 rows
                 const u32x4_t v = *reinterpret_cast<const u32x4_t *>(row + k0);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
                 uint32_t o[8];
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
 #pragma unroll
         for (int s = 0; s < SMAX; ++s) {
             if (s < S) {
-                const int k = g * KQ + 8 * s;
+                const int k = 64 * (s >> 1) + 16 * g + 8 * (s & 1);
                 const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (2 * 16 + c) * RS + k));
                 const bf16x8_t am = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (1 * 16 + c) * RS + k));
                 const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + (0 * 16 + c) * RS + k));
