@@ -576,7 +576,7 @@ def main():
                 if layout == "kmajor":
                     line_m["roofline"] = own_roofline(dm, msm, 16)
                     line_m["kernel"] = ("k_mm_x3k (whole-K, one launch per matmul; "
-                                        if Mb <= 8 else "k_mm_x3 (split-K + reduce; ") + \
+                                        if Mb <= 16 else "k_mm_x3 (split-K + reduce; ") + \
                         "bf16 x3 matrix cores, exact operands)"
                 else:
                     line_m["frac_fp32_mfma_peak"] = round(
