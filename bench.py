@@ -473,17 +473,28 @@ def main():
         msf, _ = time_graph(gf, max(5, args.steps // 2), 2)
         del gf
         floor[L] = msf
-    del floor_bufs
-    torch.cuda.empty_cache()
     floor_L = min(floor, key=floor.get)
     floor_ms = floor[floor_L]
+    # per shape, as for the GEMV: graphs of one shape's 32 launches
+    floor_shape = {}
+    for K, N in synth.DENSE38_SHAPES:
+        bufs = [b for b, m in zip(floor_bufs, dense) if (m.K, m.N) == (K, N)]
+        gf = capture(lambda bufs=bufs: [w4.w4_read_bytes(b, floor_L, out=floor_out) for b in bufs])
+        msf, _ = time_graph(gf, max(5, args.steps // 2), 2)
+        del gf
+        us = 1e3 * msf / len(bufs)
+        floor_shape[f"{K}x{N}"] = {"us": round(us, 3),
+                                   "gemv_over_floor": round(per_shape[f"{K}x{N}"]["us"] / us, 3)}
     floor_line = {"ms": round(floor_ms, 5), "us_per_launch": round(1e3 * floor_ms / launches, 3),
                   "GB_s": round(pass_bytes / (floor_ms * 1e-3) / 1e9, 1),
                   "frac_hbm_peak": round(pass_bytes / (floor_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "loads_per_lane": floor_L,
                   "ms_by_loads_per_lane": {str(k): round(v, 5) for k, v in floor.items()},
+                  "per_shape": floor_shape,
                   "kernel": "w4_read_bytes (streaming read of each matrix's packed bytes, "
                             "one launch per matrix, same graph)"}
+    del floor_bufs
+    torch.cuda.empty_cache()
     log(f"launch floor: {floor_line}")
 
     # the same pass on the other layout, for comparison
@@ -739,6 +750,13 @@ def main():
                 "TFLOP_s": round(fp / (msp * 1e-3) / 1e12, 3),
                 "frac_own_roofline": round(t_pre / (msp * 1e-3), 4),
                 "own_roofline_ms": round(1e3 * t_pre, 4)}
+            if layout == "kmajor":
+                # the same 48 dependent launches plus the head at one row (the
+                # decode pass above and the token-major head): what launches
+                # alone cost here, against a roofline that ignores them
+                m1 = secondary["gpt2_decode_pass_kmajor"]["ms"] + head_times["token_major"]["us"] / 1e3
+                secondary[name]["same_launches_at_m1_ms"] = round(m1, 4)
+                secondary[name]["vs_same_launches_at_m1"] = round(msp / m1, 3)
 
     line = {
         "metric": METRIC,

@@ -146,13 +146,18 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // of one block per lane do not collide) then hands every lane its own
 // block.  A lane's own block's 128 bytes would otherwise come from 8 loads
 // that each touch 64 different cache lines.
+// NBLC: NBL as a compile-time constant (0: the argument).  The lane's slot
+// and the activation runs' blocks come from divisions by NBL before the first
+// weight load; by a constant they are a multiply and a shift (3.8B M=1 pass:
+// 101 -> 51..66 instructions before the first load, 0.763 -> 0.728 ms).
 template <int MR, int P, bool CHECK, int LM, bool H, bool EP, bool AFF = false,
-          bool XC = false>
+          bool XC = false, int NBLC = 0>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, const uint8_t *__restrict__ Pq, const void *__restrict__ Ps,
-    const void *__restrict__ Pz, int M, int K, int N, int G, int NBL,
+    const void *__restrict__ Pz, int M, int K, int N, int G, int NBL_arg,
     const float *__restrict__ bias, const float *residual, int act, float *y) {
     extern __shared__ float red[];  // [MR][CC][NBL]; XC: then 36 floats per lane
+    const int NBL = NBLC ? NBLC : NBL_arg;
     const int L = threadIdx.x;
     const int g = L / NBL, bl = L - g * NBL;
     const int NB = K / kBlock, hk = K / 2;
@@ -493,24 +498,32 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_ARGS                                                                              \
     x, Pq, Ps, Pz, (int)M, (int)K, (int)N, p.groups, p.lanes_per_col, bias, residual, act, y
-#define W4_KM_LAUNCH2(MRV, PV, CV, LV, XCV)                                                     \
+#define W4_KM_LAUNCH2(MRV, PV, CV, LV, XCV, NV)                                                 \
     if (affine)                                                                                 \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true, XCV>), grid,       \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true, XCV, NV>), grid,   \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else if (f16)                                                                               \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false, false, XCV>), grid,       \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false, false, XCV, NV>), grid,   \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else if (ep)                                                                                \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true, false, XCV>), grid,       \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true, false, XCV, NV>), grid,   \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
     else                                                                                        \
-        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV>), grid,      \
+        hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV, NV>), grid,  \
                            dim3(p.threads), shm, stream, W4_KM_ARGS)
+// one row with whole-run activation loads and 96 or 256 lanes per column (the
+// 3.8B shapes' K = 3072 and 8192): the constant-NBL instantiations
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
     if (MRV <= 2 && LV != 1 && xc) {                                                            \
-        W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1);                                    \
+        if constexpr (MRV == 1 && LV == 2) {                                                    \
+            if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 96); }            \
+            else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
+            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
+        } else {                                                                                \
+            W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1, 0);                             \
+        }                                                                                       \
     } else {                                                                                    \
-        W4_KM_LAUNCH2(MRV, PV, CV, LV, false);                                                  \
+        W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 0);                                               \
     }
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \
