@@ -319,6 +319,41 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         for (int r = 0; r < MR; ++r)
 #pragma unroll
             for (int p = 0; p < P; ++p) part[r][p] = sum32(part[r][p]);
+        if (NBLC == 32) {
+            // Each column slot is one 32-lane half (lanes past the column's
+            // blocks idle): its last lane holds the column's sum and stores
+            // it; no LDS and no barrier.  A SwiGLU pair (c, c + 1), c even, is
+            // slots g and g + 1 (G is even), the two halves of one wave.
+            float up[MR][P];
+#pragma unroll
+            for (int r = 0; r < MR; ++r)
+#pragma unroll
+                for (int p = 0; p < P; ++p) up[r][p] = __shfl_down(part[r][p], 32);
+            if (g < G && bl == 31) {
+#pragma unroll
+                for (int r = 0; r < MR; ++r)
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        const int n = n0 + p * G + g, m = m0 + r;
+                        if (n >= N || m >= M) continue;
+                        float v = part[r][p];
+                        if (EP) {
+                            if (bias) v += bias[n];
+                            if (act == W4_ACT_SWIGLU) {
+                                if ((g & 1) == 0) {
+                                    const float u = up[r][p] + (bias ? bias[n + 1] : 0.0f);
+                                    ep_store_glu(v, u, residual, y, (size_t)m * (N / 2) + n / 2);
+                                }
+                            } else {
+                                ep_store(v, act, residual, y, (size_t)m * N + n);
+                            }
+                        } else {
+                            y[(size_t)m * N + n] = bias ? v + bias[n] : v;
+                        }
+                    }
+            }
+            return;
+        }
         if (g < G && (bl & 31) == 31) {
 #pragma unroll
             for (int r = 0; r < MR; ++r)
@@ -511,19 +546,30 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     else                                                                                        \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV, NV>), grid,  \
                            dim3(p.threads), shm, stream, W4_KM_ARGS)
-// one row with whole-run activation loads and 96 or 256 lanes per column (the
-// 3.8B shapes' K = 3072 and 8192): the constant-NBL instantiations
+// Constant-NBL instantiations: one row with whole-run activation loads and
+// 96 or 256 lanes per column (the 3.8B shapes' K = 3072 and 8192); and one
+// or two rows with 32 lanes per column (K = 544 .. 1024), whose column sums
+// stay in registers and are stored by one lane of each half.
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
     if (MRV <= 2 && LV != 1 && xc) {                                                            \
         if constexpr (MRV == 1 && LV == 2) {                                                    \
             if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 96); }            \
             else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
+            else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }       \
+            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
+        } else if constexpr (MRV == 2 && LV == 2) {                                             \
+            if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }            \
             else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
         } else {                                                                                \
             W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1, 0);                             \
         }                                                                                       \
     } else {                                                                                    \
-        W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 0);                                               \
+        if constexpr (MRV <= 2 && LV == 2) {                                                    \
+            if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 32); }           \
+            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 0); }                                  \
+        } else {                                                                                \
+            W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 0);                                           \
+        }                                                                                       \
     }
 #define W4_KM_CASE(MRV, PV)                                                                     \
     if (p.rows == MRV && p.passes == PV) {                                                      \

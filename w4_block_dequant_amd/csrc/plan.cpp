@@ -150,7 +150,15 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
             threads = 64 * w;
             break;
         }
-    if (threads) {
+    static const int64_t env_half = env_int_or("W4_KMAJOR_HALF", 1);
+    if (env_half != 0 && p.rows <= 2 && NB > 16 && NB <= 32) {
+        // 17 to 32 blocks: one 32-lane half per column (the lanes past NB
+        // idle), whose sum stays in registers and is stored by its last
+        // lane: no LDS and no barrier for the sums.  GPT-2's K = 768.
+        p.threads = 256;
+        p.lanes_per_col = 32;
+        p.groups = 8;
+    } else if (threads) {
         p.threads = threads;
         // a column needs at least `rows` lanes for the final per-output sums;
         // for very short K the extra lanes idle (NB < 4 only)
