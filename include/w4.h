@@ -343,9 +343,12 @@ int i8_head_logits_kmajor(const float *x_last, int64_t K, const int8_t *Qt, int6
 
 /* Full-sequence logits (the page's export before the last-position slice of
  * step 4): logits[m, n] = hs[n] * sum_k x[m, k] * Qt[n, k] for every row m of
- * x [M, K] (fp32, row-major, 16-byte aligned), logits [M, N] fp32.  Same
- * arithmetic and bound as i8_head_logits_kmajor (a row with a non-finite
- * entry gives NaN logits for that row only).  K % 16 == 0, 16 <= K <= 8192;
+ * x [M, K] (fp32, row-major, 16-byte aligned), logits [M, N] fp32.  Every
+ * product is exact and only fp32 accumulation rounds (from 4 rows with K <=
+ * 1024 on the bf16 matrix cores, each activation split exactly into three
+ * bf16 parts; otherwise as i8_head_logits_kmajor), so the bound is that of
+ * i8_head_logits_kmajor (a row with a non-finite entry gives NaN logits for
+ * that row only).  K % 16 == 0, 16 <= K <= 8192;
  * N * ldt < 2^31.  One launch; no workspace is needed:
  * i8_head_rows_workspace_bytes returns 0 and `workspace` may be NULL.      */
 size_t i8_head_rows_workspace_bytes(int64_t M, int64_t K);
