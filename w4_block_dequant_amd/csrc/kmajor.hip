@@ -546,10 +546,10 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     else                                                                                        \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV, NV>), grid,  \
                            dim3(p.threads), shm, stream, W4_KM_ARGS)
-// Constant-NBL instantiations: one row with whole-run activation loads and
-// 96 or 256 lanes per column (the 3.8B shapes' K = 3072 and 8192); and one
-// or two rows with 32 lanes per column (K = 544 .. 1024), whose column sums
-// stay in registers and are stored by one lane of each half.
+// Constant-NBL instantiations: one or two rows with whole-run activation
+// loads and 96 or 256 lanes per column (the 3.8B shapes' K = 3072 and 8192);
+// and one or two rows with 32 lanes per column (K = 544 .. 1024), whose
+// column sums stay in registers and are stored by one lane of each half.
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
     if (MRV <= 2 && LV != 1 && xc) {                                                            \
         if constexpr (MRV == 1 && LV == 2) {                                                    \
@@ -559,6 +559,8 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
             else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
         } else if constexpr (MRV == 2 && LV == 2) {                                             \
             if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }            \
+            else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 96); }       \
+            else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
             else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
         } else {                                                                                \
             W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1, 0);                             \
