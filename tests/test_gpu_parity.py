@@ -803,6 +803,42 @@ def test_f16_matmul_kmajor(M, K, N):
     assert_bound(y, y_ref, bound, f"f16 kmajor M={M} {K}x{N}")
 
 
+# K = 3072 and N >= 3072 at M = 1 and 2: two column slots per workgroup read
+# the activations once and share them through LDS; at M = 1 4096 columns take
+# 4 passes (512 workgroups, no ragged tail) and 3080 take 3 passes with a
+# ragged last workgroup; at M = 2 both take 4 passes (3080: ragged).  Every
+# scale format and epilogue goes through that mode here.
+@pytest.mark.parametrize("N", [3080, 4096])
+@pytest.mark.parametrize("variant", ["plain", "f16", "g64", "gelu", "swiglu+res"])
+@pytest.mark.parametrize("M", [1, 2])
+def test_kmajor_shared_activations(M, variant, N):
+    K = 3072
+    note(f"shared activations {variant} M={M} K={K} N={N}")
+    W = mixed_weights_f16(K, N, cfg=271) if variant == "f16" else mixed_weights(K, N, cfg=271)
+    x = synth.activations(M, K, cfg=271, slot=M, outliers=True)
+    b = synth.bias(N, cfg=271)
+    if variant == "f16":
+        Wq, s16, z = ORC.quantize_pack_f16(W)
+        y_ref, bound = ORC.w4h_matmul(x, Wq, s16, z, b)
+        s_dev = torch.from_numpy(s16.view(np.float16)).to(DEV)
+        y = host(w4.w4_matmul_kmajor(dev(x), *w4.w4h_prepack_kmajor(dev(Wq), s_dev, dev(z)),
+                                     bias=dev(b)))
+    elif variant == "g64":
+        Wq, s, m = ORC.quantize_pack_g64(W)
+        y_ref, bound = ORC.w4g_matmul(x, Wq, s, m, b)
+        y = host(w4.w4g_matmul_kmajor(dev(x), *w4.w4g_prepack_kmajor(dev(Wq), dev(s), dev(m)),
+                                      bias=dev(b)))
+    else:
+        act = "gelu" if variant == "gelu" else ("swiglu" if variant.startswith("swiglu") else "none")
+        r = synth.activations(M, N // 2, cfg=272, slot=M) if variant.endswith("+res") else None
+        Wq, s, z = ORC.quantize_pack(W)
+        y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, b, r, act=act)
+        P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+        y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b), act=act,
+                                     residual=None if r is None else dev(r)))
+    assert_bound(y, y_ref, bound, f"shared activations {variant} {K}x{N}")
+
+
 # --------------------------------------------------------------------------
 # fused epilogues (GELU, SwiGLU on interleaved gate/up columns, residual add)
 # --------------------------------------------------------------------------

@@ -146,12 +146,22 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // of one block per lane do not collide) then hands every lane its own
 // block.  A lane's own block's 128 bytes would otherwise come from 8 loads
 // that each touch 64 different cache lines.
+// XC == 18 (two column slots per workgroup, NBL == NB): the two slots need
+// the same activations, so the workgroup reads each row once in coalesced
+// 16-byte chunks (thread t takes chunks t, t + T, t + 2T and t + 3T of the
+// row, T threads), stages it in LDS in 144-byte block slots, and one barrier
+// hands every lane its block (XC = 16 + column slots per workgroup).  The barrier's fence covers
+// LDS only: a full workgroup fence would wait for every weight load still in
+// flight, and all arithmetic would wait for the last of them.  It halves the
+// activation traffic of the wave-run mode above (3.8B shapes, us per
+// launch: 3072 x 9216 6.10 -> 5.62, 3072 x 16384 8.09 -> 7.89, 3072 x 3072
+// 3.72 -> 3.60, with the passes chosen for it).
 // NBLC: NBL as a compile-time constant (0: the argument).  The lane's slot
 // and the activation runs' blocks come from divisions by NBL before the first
 // weight load; by a constant they are a multiply and a shift (3.8B M=1 pass:
 // 101 -> 51..66 instructions before the first load, 0.763 -> 0.728 ms).
 template <int MR, int P, bool CHECK, int LM, bool H, bool EP, bool AFF = false,
-          bool XC = false, int NBLC = 0>
+          int XC = 0, int NBLC = 0>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, const uint8_t *__restrict__ Pq, const void *__restrict__ Ps,
     const void *__restrict__ Pz, int M, int K, int N, int G, int NBL_arg,
@@ -176,9 +186,21 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         for (int b = bl; LM == 1 ? b < NB : (b == bl && b < NB); b += NBL) {
             // activations of this block, for each of the MR rows
             float xr[MR][kBlock];
-            f32x4_t xg[XC ? MR : 1][XC ? kBlock / 4 : 1];  // XC: 16 bytes of each of 8 runs
+            f32x4_t xg[XC == 1 ? MR : 1][XC == 1 ? kBlock / 4 : 1];  // 16 bytes of each of 8 runs
+            constexpr int XG = XC > 16 ? XC - 16 : 1;  // shared mode: column slots
+            constexpr int XW = XC > 16 ? kBlock / 4 / XG : 1;  // chunks per thread and row
+            f32x4_t xw[XC > 16 ? MR : 1][XW];
             const int lw = L & 63;
-            if (XC) {
+            if (XC > 16) {
+#pragma unroll
+                for (int r = 0; r < MR; ++r) {
+                    const float *xrow = x + (size_t)min(m0 + r, M - 1) * K;
+#pragma unroll
+                    for (int i = 0; i < XW; ++i)
+                        xw[r][i] = *reinterpret_cast<const f32x4_t *>(xrow + 4 * (L + i * XG * NBL));
+                }
+            }
+            if (XC == 1) {
                 // run i: the 8 blocks of lane group i of this wave, from block
                 // bl(8 i); this lane takes block lw / 8 of it, bytes 16 (lw % 8)
 #pragma unroll
@@ -245,7 +267,32 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                 oz += sz;
             }
             __builtin_amdgcn_sched_barrier(0);  // every load in flight before the arithmetic
-            if (XC) {
+            if (XC > 16) {
+                // chunk c of row r to piece c % 8 of block slot c / 8
+                float *xs = red + MR * CC * NBL;
+#pragma unroll
+                for (int r = 0; r < MR; ++r)
+#pragma unroll
+                    for (int i = 0; i < XW; ++i) {
+                        const int c = L + i * XG * NBL;
+                        *reinterpret_cast<f32x4_t *>(xs + 36 * (r * NBL + (c >> 3)) + 4 * (c & 7)) = xw[r][i];
+                    }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+                for (int r = 0; r < MR; ++r)
+#pragma unroll
+                    for (int i = 0; i < kBlock / 4; ++i) {
+                        const f32x4_t v =
+                            *reinterpret_cast<const f32x4_t *>(xs + 36 * (r * NBL + bl) + 4 * i);
+                        xr[r][4 * i + 0] = v.x;
+                        xr[r][4 * i + 1] = v.y;
+                        xr[r][4 * i + 2] = v.z;
+                        xr[r][4 * i + 3] = v.w;
+                    }
+            }
+            if (XC == 1) {
                 // run i's pieces to block slot 8 i + lw / 8 of this wave's
                 // staging area; then this lane's own block is slot lw
                 float *xstage = red + MR * CC * NBL + (L & ~63) * (36 * MR);
@@ -528,8 +575,12 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     // groups inside one column slot
     const bool xc = p.xc && p.rows <= 2 && p.lanes_per_col == K / kBlock &&
                     p.lanes_per_col % 8 == 0 && (int64_t)p.groups * p.lanes_per_col == p.threads;
+    // workgroup-shared activations: two column slots of one block per lane
+    // (LDS holds one 144-byte slot per block and row)
+    const bool xs = xc && p.xs == 2 && p.groups == 2;
     const size_t shm = (size_t)p.rows * C * p.lanes_per_col * sizeof(float) +
-                       (xc ? (size_t)p.threads * 36 * p.rows * sizeof(float) : 0);
+                       (xs ? (size_t)p.lanes_per_col * 36 * p.rows * sizeof(float)
+                           : xc ? (size_t)p.threads * 36 * p.rows * sizeof(float) : 0);
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_ARGS                                                                              \
     x, Pq, Ps, Pz, (int)M, (int)K, (int)N, p.groups, p.lanes_per_col, bias, residual, act, y
@@ -553,12 +604,14 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
 #define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
     if (MRV <= 2 && LV != 1 && xc) {                                                            \
         if constexpr (MRV == 1 && LV == 2) {                                                    \
-            if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 96); }            \
+            if (xs && p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, 18, 96); }        \
+            else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, 1, 96); }          \
             else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
             else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }       \
             else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
         } else if constexpr (MRV == 2 && LV == 2) {                                             \
-            if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }            \
+            if (xs && p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, 18, 96); }        \
+            else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }       \
             else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 96); }       \
             else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
             else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \

@@ -236,6 +236,31 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     static const int64_t env_xc = env_int("W4_KMAJOR_XC");
     const int64_t wgs = cdiv(N, (int64_t)p.groups * p.passes) * cdiv(M, p.rows);
     p.xc = env_xc == 1 || (env_xc != 2 && wgs >= 256);
+    // Two column slots per workgroup with one block per lane (K = 3072: 96
+    // lanes per column, 192 threads): the workgroup reads the activations
+    // once and shares them through LDS (xs), and then 4 passes where they
+    // leave at least 512 workgroups, else 3, 2 or 1 (3.8B M=1 shapes, us per
+    // launch: 3072 x 9216 4 passes 5.62 against 5.79 with 6; 3072 x 16384 4
+    // passes 7.89 against 8.53 with 8; 3072 x 3072 3 passes 3.60; the M=1
+    // pass 0.733 -> 0.711 ms).  Two rows keep their passes (M=2 pass 1.153
+    // -> 1.079 ms).  Four rows stay on the matrix cores: with the shared
+    // activations the four-row GEMV is bound by its arithmetic (M=4 pass
+    // 2.40 ms against 1.50).  W4_KMAJOR_XS=0 turns it off.
+    static const int64_t env_xs = env_int_or("W4_KMAJOR_XS", 1);
+    if (p.xc && env_xs != 0 && p.rows <= 2 && p.groups == 2 &&
+        p.lanes_per_col == NB && p.lanes_per_col % 8 == 0 && p.threads == 2 * p.lanes_per_col) {
+        if (env_p > 0 || p.rows != 1) {
+            p.xs = 2;
+        } else {
+            static const int shared_passes[] = {4, 3, 2, 1};
+            for (int P : shared_passes)
+                if (cdiv(N, 2 * (int64_t)P) >= 512) {
+                    p.passes = P;
+                    p.xs = 2;
+                    break;
+                }
+        }
+    }
     return p;
 }
 

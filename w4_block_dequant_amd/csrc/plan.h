@@ -69,6 +69,7 @@ struct KmajorPlan {
     enum Kind { kEmpty = 0, kBiasOnly = 1, kRun = 2 } kind;
     int rows = 1, passes = 1, groups = 1, lanes_per_col = 64, threads = 64;
     bool xc = true;  // activations in whole runs through LDS where the geometry allows
+    int xs = 0;      // 2: two column slots read the activations once per workgroup
 };
 
 // even_cols: a workgroup's column count (groups * passes) must be even, so
