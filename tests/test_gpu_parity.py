@@ -808,11 +808,10 @@ def test_f16_matmul_kmajor(M, K, N):
 # 4 passes (512 workgroups, no ragged tail) and 3080 take 3 passes with a
 # ragged last workgroup; at M = 2 both take 4 passes (3080: ragged).  Every
 # scale format and epilogue goes through that mode here.
-@pytest.mark.parametrize("N", [3080, 4096])
+@pytest.mark.parametrize("K,N", [(3072, 3080), (3072, 4096), (8192, 3080)])
 @pytest.mark.parametrize("variant", ["plain", "f16", "g64", "gelu", "swiglu+res"])
 @pytest.mark.parametrize("M", [1, 2])
-def test_kmajor_shared_activations(M, variant, N):
-    K = 3072
+def test_kmajor_shared_activations(M, variant, K, N):
     note(f"shared activations {variant} M={M} K={K} N={N}")
     W = mixed_weights_f16(K, N, cfg=271) if variant == "f16" else mixed_weights(K, N, cfg=271)
     x = synth.activations(M, K, cfg=271, slot=M, outliers=True)

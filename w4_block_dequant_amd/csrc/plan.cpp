@@ -245,20 +245,25 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     // pass 0.733 -> 0.711 ms).  Two rows keep their passes (M=2 pass 1.153
     // -> 1.079 ms).  Four rows stay on the matrix cores: with the shared
     // activations the four-row GEMV is bound by its arithmetic (M=4 pass
-    // 2.40 ms against 1.50).  W4_KMAJOR_XS=0 turns it off.
+    // 2.40 ms against 1.50).  K = 8192 keeps one 256-lane column slot per
+    // workgroup: two slots in 512 threads were slower (8192 x 3072 at M = 1:
+    // 5.67 against 5.47 us; M = 2: 10.3 against 7.5).  W4_KMAJOR_XS=0 turns
+    // it off.
     static const int64_t env_xs = env_int_or("W4_KMAJOR_XS", 1);
+    // passes for the shared mode (0: none qualifies)
+    auto shared_passes = [&]() -> int {
+        if (env_p > 0 || p.rows != 1) return p.passes;
+        static const int cand[] = {4, 3, 2, 1};
+        for (int P : cand)
+            if (cdiv(N, 2 * (int64_t)P) >= 512) return P;
+        return 0;
+    };
     if (p.xc && env_xs != 0 && p.rows <= 2 && p.groups == 2 &&
         p.lanes_per_col == NB && p.lanes_per_col % 8 == 0 && p.threads == 2 * p.lanes_per_col) {
-        if (env_p > 0 || p.rows != 1) {
+        const int P = shared_passes();
+        if (P > 0) {
+            p.passes = P;
             p.xs = 2;
-        } else {
-            static const int shared_passes[] = {4, 3, 2, 1};
-            for (int P : shared_passes)
-                if (cdiv(N, 2 * (int64_t)P) >= 512) {
-                    p.passes = P;
-                    p.xs = 2;
-                    break;
-                }
         }
     }
     return p;
