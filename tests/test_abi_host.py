@@ -147,6 +147,12 @@ def test_entry_points_reject_before_any_hip_call():
     assert w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072) == 0     # up to 16 rows
     assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 768) > 0        # too few columns: split-K
     assert w4.w4_matmul_kmajor_workspace_bytes(17, 3072, 3072) > 0      # 17 rows: split-K
+    # past 16 rows, small matrices (at most 2^22 weights): whole-K row groups
+    assert w4.w4_matmul_kmajor_workspace_bytes(58, 768, 2304) == 0
+    assert w4.w4_matmul_kmajor_workspace_bytes(58, 768, 768) == 0
+    assert w4.w4_matmul_kmajor_workspace_bytes(128, 3072, 768) == 0
+    assert w4.w4_matmul_kmajor_workspace_bytes(129, 768, 768) > 0     # past 128 rows: split-K
+    assert w4.w4_matmul_kmajor_workspace_bytes(58, 768, 16) > 0       # too few workgroups
     need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 768)
     assert need > 0
     assert w4.w4_matmul_kmajor_workspace_bytes(1, 3072, 3072) == 0

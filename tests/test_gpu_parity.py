@@ -838,6 +838,30 @@ def test_kmajor_shared_activations(M, variant, K, N):
     assert_bound(y, y_ref, bound, f"shared activations {variant} {K}x{N}")
 
 
+# 17 to 128 rows on small matrices: the whole-K matrix-core kernel in row
+# groups of 16 (grid.y) when the 48 column groups times the row groups reach
+# 128 workgroups (from 33 rows); 128 rows is the largest, 40 and 100 leave a
+# ragged last group, 3072 x 768 has 24 quads per column.  SwiGLU with the
+# residual updated in place, and the plain store with bias.
+@pytest.mark.parametrize("M", [40, 100, 128])
+@pytest.mark.parametrize("K,N", [(768, 768), (3072, 768)])
+@pytest.mark.parametrize("act", ["none", "swiglu"])
+def test_kmajor_whole_k_row_groups(M, K, N, act):
+    assert w4.w4_matmul_kmajor_workspace_bytes(M, K, N) == 0
+    note(f"row groups act={act} M={M} K={K} N={N}")
+    W = mixed_weights(K, N, cfg=281)
+    x = synth.activations(M, K, cfg=281, slot=M, outliers=True)
+    b = synth.bias(N, cfg=281)
+    nout = N // 2 if act == "swiglu" else N
+    r = synth.activations(M, nout, cfg=282, slot=M)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, b, r, act=act)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = dev(r)  # the residual stream, updated in place
+    w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b), act=act, residual=y, out=y)
+    assert_bound(host(y), y_ref, bound, f"row groups {act} M={M} {K}x{N}")
+
+
 # --------------------------------------------------------------------------
 # fused epilogues (GELU, SwiGLU on interleaved gate/up columns, residual add)
 # --------------------------------------------------------------------------

@@ -290,7 +290,19 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
     static const int64_t env_k = env_int_or("W4_X3K", 16);
     static const int64_t env_tpw = env_int("W4_X3K_TPW");
     static const int64_t env_waves = env_int("W4_X3K_WAVES");
-    if (M <= env_k && M <= 16) {
+    // Past 16 rows: row groups of 16 (grid.y) of the same kernel, each
+    // streaming the matrix again (from the caches), on small matrices (at
+    // most 2^22 weights), where the split-K kernel's second launch costs
+    // more than converting each code once per 16 rows: GPT-2 body (48
+    // matmuls) at M = 17 / 32 / 58 / 65 / 96 / 128: 0.357 / 0.377 / 0.375 /
+    // 0.447 / 0.467 / 0.503 -> 0.307 / 0.317 / 0.311 / 0.322 / 0.415 / 0.455
+    // ms.  On the 3.8B matrices the split-K kernel's 64-row tiles, which
+    // convert each code once for 64 rows, stay ahead (M = 17 / 58: 2.72 /
+    // 4.72 against 3.32 / 5.88 ms per pass).  W4_X3K_ROWS=n moves the row
+    // limit (0: never past 16 rows).
+    static const int64_t env_rows = env_int_or("W4_X3K_ROWS", 128);
+    const bool row_groups = M > 16 && M <= env_rows && K * N <= ((int64_t)1 << 22);
+    if (env_k != 0 && (M <= 16 ? M <= env_k : row_groups)) {
         // two column tiles per wave (each activation split serves 32 columns)
         // from 5 rows on, where that still leaves 512 workgroups: 3072x16384
         // at M = 8 19.9 -> 17.2 us, at M = 16 25.4 -> 20.2; at M = 4 and on
@@ -299,7 +311,8 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
         if (env_tpw == 1 || env_tpw == 2) tpw = env_tpw;
         if (tpw == 2 && cdiv(N, 32) < 128) tpw = 1;
         const int64_t wgs = cdiv(N, 16 * tpw);
-        if (wgs >= 128) {
+        const int64_t mgroups = cdiv(M, 16);
+        if (wgs * mgroups >= 128) {
             p.kind = X3Plan::kFullK;
             p.mb = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
             p.nt = (int)tpw;
@@ -317,7 +330,7 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
             static const int64_t env_d = env_int("W4_X3K_D");
             p.dq = (env_d >= 1 && env_d <= 4) ? (int)env_d : 0;
             p.col_wgs = wgs;
-            p.mgroups = 1;
+            p.mgroups = mgroups;
             p.splits = 1;
             p.workspace = 0;
             return p;

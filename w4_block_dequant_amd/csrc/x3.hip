@@ -326,6 +326,15 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
                                                    const uint8_t *__restrict__ Pz, int N,
                                                    const float *__restrict__ bias,
                                                    const float *residual, int act, float *y) {
+    // row group blockIdx.y: rows m0 .. m0 + MB - 1 (M > MB only with MB = 16)
+    {
+        const int m0 = blockIdx.y * MB;
+        const int nout = act == W4_ACT_SWIGLU ? N / 2 : N;
+        M = min(M - m0, MB);
+        x += (size_t)m0 * K;
+        y += (size_t)m0 * nout;
+        if (residual) residual += (size_t)m0 * nout;
+    }
     constexpr int ABLK = 16 / MB;  // blocks per A image: MB rows x ABLK blocks = 64 lanes x 8
     constexpr int NBLD = 4 / ABLK;  // A images per quad
     constexpr int TQ_BYTES = TPW * 64 * 16;
@@ -508,7 +517,7 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
                         const float *residual, int act, float *y, void *workspace,
                         hipStream_t stream) {
     if (p.kind == X3Plan::kFullK) {
-        const dim3 grid((unsigned)p.col_wgs);
+        const dim3 grid((unsigned)p.col_wgs, (unsigned)p.mgroups);
         bool done = false;
 #define W4_X3K(MBV, TPWV, WV, DV)                                                                  \
     if (!done && p.mb == MBV && p.nt == TPWV && p.waves == WV && (p.dq == DV || p.dq == 0)) {      \
