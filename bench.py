@@ -1044,7 +1044,8 @@ def summarize_profiles(src: str, out_dir: str):
              "MFMA-busy cycles over active cycles times SIMDs, in percent.  MFMA FLOP/s "
              "count the matrix-core operations the kernel issued (MOPS x 512 over the "
              "dispatch's duration under counter collection): `k_mm_x3` (split-K) and "
-             "`k_mm_x3k` (whole-K, up to 16 rows) issue three bf16 MFMAs per fp32 product "
+             "`k_mm_x3k` (whole-K, up to 16 rows; row groups of 16 up to 128 rows on small "
+             "matrices) issue three bf16 MFMAs per fp32 product "
              "(exact three-part splits of each activation) on whole 16-row tiles, so their "
              "useful fp32 rate is at most a third of the bf16 rate, and at M = 4 a quarter "
              "of that again; `k_mm_mfma` runs fp32 MFMA.  Peaks: bf16 2.5 PFLOP/s, fp32 "
