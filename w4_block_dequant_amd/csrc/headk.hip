@@ -185,6 +185,15 @@ __global__ __launch_bounds__(256) void k_head_fp32(const float *__restrict__ x, 
 // each of 16 token rows (a lane group's quarter of K in one run would touch
 // 64 cache lines per instruction instead).
 // Rows with a non-finite entry are flagged while they are built and give NaN.
+// With two token tiles (K <= 768) each row tile's activations reach LDS as
+// they are, by direct-to-LDS loads (global_load_lds_dwordx4: a wave writes
+// 1 KB of consecutive LDS per instruction, no registers) into a second
+// buffer [16][K] fp32 after the part planes: the first tile's before the
+// codes are loaded, each later tile's while the previous tile's MFMAs run;
+// the barriers fence LDS only, and a tile's logits are stored after the next
+// tile's wait.  That wait (vmcnt also counts stores) would otherwise drain
+// the stores just issued, and a full workgroup fence, or activation loads
+// queued behind the codes, would hold every build behind the code stream.
 template <int SMAX, int WAVES, int TT>
 __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__restrict__ x, int M, int K,
                                                       const int8_t *__restrict__ Qt, int ldt,
@@ -202,6 +211,52 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
     const int t0 = (blockIdx.x * WAVES + wave) * 16 * TT;
     const int KP = (K + 63) / 64 * 64, S = KP / 32, RS = KP + 8;
     const int n = min(t0 + c, N - 1);
+
+    // TT = 2: raw activations of a row tile, [16][K] fp32 after the planes
+    constexpr bool DMA = TT == 2;
+    float *xr = reinterpret_cast<float *>(ap + 3 * 16 * RS);
+    // rows m0 .. m0 + 15 of x (those below M) to xr: 1 KB chunk j of the
+    // tile (16 K floats, contiguous in x) by wave j % WAVES, lane l taking
+    // bytes 16 l of the chunk
+    const int tile_chunks = (16 * K * 4 + 1023) / 1024;
+    auto dma_tile = [&](int m0) {
+        const int valid = min(16, M - m0) * K * 4;  // bytes of the tile inside x
+        const char *src0 = reinterpret_cast<const char *>(x + (size_t)m0 * K);
+        for (int j = wave; j < tile_chunks; j += WAVES) {
+            const int off = 1024 * j + 16 * lane;
+            if (off < valid)
+                __builtin_amdgcn_global_load_lds(
+                    src0 + off,
+                    (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(xr) + 1024 * j),
+                    16, 0, 0);
+        }
+    };
+    auto lds_barrier = []() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    if (DMA) {
+        dma_tile(0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // DMA: the previous tile's logits (scaled), its row flags and first row
+    float pend[TT][4];
+    uint32_t pbad = 0;
+    int pm0 = -1;
+    auto store_pending = [&]() {
+        if (pm0 < 0) return;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int t = t0 + 16 * tt + c;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = pm0 + 4 * g + v;
+                if (m < M && t < N)
+                    logits[(size_t)m * N + t] = ((pbad >> v) & 1) ? __builtin_nanf("") : pend[tt][v];
+            }
+        }
+    };
 
     // TT = 2: the codes of both token tiles as loaded, 16 bytes per two steps
     // (the compiler widens them to bf16 once, outside the row-tile loop)
@@ -267,16 +322,28 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
     const int K8 = KP / 8;  // 8-element pieces per row
 
     for (int m0 = 0; m0 < M; m0 += 16) {
-        __syncthreads();  // the previous tile's reads are done
-        if (tid < 16) rowbad[tid] = 0;
-        __syncthreads();
+        if (DMA) {
+            // this wave's chunks of the tile are in LDS (and every load and
+            // store it issued before them is done); the barriers make every
+            // wave's chunks visible and end the previous tile's reads
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+            store_pending();
+            if (tid < 16) rowbad[tid] = 0;
+            lds_barrier();
+        } else {
+            __syncthreads();  // the previous tile's reads are done
+            if (tid < 16) rowbad[tid] = 0;
+            __syncthreads();
+        }
         // build: piece e = (row, 8 k) of the tile, three bf16 parts each
         for (int e = tid; e < 16 * K8; e += 64 * WAVES) {
             const int r = e / K8, k = 8 * (e - r * K8);
             float xv[8];
             const bool live = m0 + r < M && k < K;  // K % 16 == 0: a piece is all in or all out
             if (live) {
-                const f32x4_t *xp = reinterpret_cast<const f32x4_t *>(x + (size_t)(m0 + r) * K + k);
+                const f32x4_t *xp = DMA ? reinterpret_cast<const f32x4_t *>(xr + r * K + k)
+                                        : reinterpret_cast<const f32x4_t *>(x + (size_t)(m0 + r) * K + k);
                 const f32x4_t a0 = xp[0], a1 = xp[1];
                 xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
                 xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
@@ -305,7 +372,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
             *reinterpret_cast<u32x4_t *>(ap + (1 * 16 + r) * RS + k) = u32x4_t{pm[0], pm[1], pm[2], pm[3]};
             *reinterpret_cast<u32x4_t *>(ap + (2 * 16 + r) * RS + k) = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
         }
-        __syncthreads();
+        if (DMA) {
+            lds_barrier();  // the planes are built and the raw tile is read
+            if (m0 + 16 < M) dma_tile(m0 + 16);  // lands while this tile's MFMAs run
+        } else {
+            __syncthreads();
+        }
         // two accumulators per token tile (even and odd steps): independent
         // MFMA chains
         f32x4v acc2[TT][2];
@@ -336,6 +408,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
             }
         }
         // lane (g, c) holds D[4 g + v][c]: row m0 + 4 g + v, token t0 + 16 tt + c
+        if (DMA) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const f32x4v acc = acc2[tt][0] + acc2[tt][1];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) pend[tt][v] = acc[v] * hsn2[tt];
+            }
+            pbad = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pbad |= (rowbad[4 * g + v] ? 1u : 0u) << v;
+            pm0 = m0;
+            continue;
+        }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             const f32x4v acc = acc2[tt][0] + acc2[tt][1];
@@ -349,6 +434,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_rows_x3(const float *__rest
             }
         }
     }
+    if (DMA) store_pending();
 }
 
 }  // namespace
@@ -416,7 +502,7 @@ hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const i
     // the matrix cores; below, or for longer rows, the fp32 kernel
     const int64_t KP = (K + 63) / 64 * 64;
     if (M < 4 || KP > 1024) return launch_head_fp32(x, M, K, Qt, ldt, hs, N, logits, stream);
-    const size_t shm = (size_t)3 * 16 * (KP + 8) * 2;
+    const size_t shm_planes = (size_t)3 * 16 * (KP + 8) * 2;
     // waves per workgroup and token tiles per wave (each tile's activation
     // parts are built once per workgroup, each LDS read of them feeds TT
     // token tiles).  58 x 768 x 50257: one tile, 8 waves 55.4 us; two tiles,
@@ -428,6 +514,8 @@ hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const i
     // registers; four tiles (bytes widened per step, one wave per SIMD) took
     // 50.1 us
     const int TTv = (env_tt == 1 || KP > 768) ? 1 : 2;
+    // two tiles: the raw activation tile after the part planes
+    const size_t shm = shm_planes + (TTv == 2 ? (size_t)16 * K * sizeof(float) : 0);
     const int WVv = env_wv == 8 ? 8 : 4;
     const int tokens = 16 * TTv * WVv;
     const dim3 grid((unsigned)((N + tokens - 1) / tokens));
@@ -437,7 +525,8 @@ hipError_t launch_head_rows_kmajor(const float *x, int64_t M, int64_t K, const i
     do {                                                                                          \
         static const hipError_t attr = hipFuncSetAttribute(                                      \
             reinterpret_cast<const void *>(&k_head_rows_x3<SV, WV, TTV>),                        \
-            hipFuncAttributeMaxDynamicSharedMemorySize, 3 * 16 * (32 * SV + 8) * 2);             \
+            hipFuncAttributeMaxDynamicSharedMemorySize,                                          \
+            3 * 16 * (32 * SV + 8) * 2 + (TTV == 2 ? 16 * 32 * SV * 4 : 0));                     \
         if (attr != hipSuccess) return attr;                                                      \
         hipLaunchKernelGGL((k_head_rows_x3<SV, WV, TTV>), grid, dim3(64 * WV), shm, stream, x,    \
                            (int)M, (int)K, Qt, (int)ldt, hs, (int)N, logits);                     \
