@@ -146,22 +146,25 @@ __device__ __forceinline__ void fma_kpair(uint32_t v0, uint32_t v1, half2_t zE, 
 // of one block per lane do not collide) then hands every lane its own
 // block.  A lane's own block's 128 bytes would otherwise come from 8 loads
 // that each touch 64 different cache lines.
-// XC == 18 (two column slots per workgroup, NBL == NB): the two slots need
-// the same activations, so the workgroup reads each row once in coalesced
-// 16-byte chunks (thread t takes chunks t, t + T, t + 2T and t + 3T of the
-// row, T threads), stages it in LDS in 144-byte block slots, and one barrier
-// hands every lane its block (XC = 16 + column slots per workgroup).  The barrier's fence covers
-// LDS only: a full workgroup fence would wait for every weight load still in
-// flight, and all arithmetic would wait for the last of them.  It halves the
-// activation traffic of the wave-run mode above (3.8B shapes, us per
-// launch: 3072 x 9216 6.10 -> 5.62, 3072 x 16384 8.09 -> 7.89, 3072 x 3072
-// 3.72 -> 3.60, with the passes chosen for it).
+// XC selects how the activations arrive: kXcLane (0) each lane loads its own
+// block, kXcRuns (1) the wave runs above, kXcShared + G (G column slots per
+// workgroup, NBL == NB; G = 2 is instantiated): the slots need the same
+// activations, so the workgroup reads each row once in coalesced 16-byte
+// chunks (thread t takes chunks t, t + T, t + 2T and t + 3T of the row, T
+// threads), stages it in LDS in 144-byte block slots, and one barrier hands
+// every lane its block.  The barrier's fence covers LDS only: a full
+// workgroup fence would wait for every weight load still in flight, and all
+// arithmetic would wait for the last of them.  It halves the activation
+// traffic of the wave runs (3.8B shapes, us per launch: 3072 x 9216 6.10 ->
+// 5.62, 3072 x 16384 8.09 -> 7.89, 3072 x 3072 3.72 -> 3.60, with the
+// passes chosen for it).
 // NBLC: NBL as a compile-time constant (0: the argument).  The lane's slot
 // and the activation runs' blocks come from divisions by NBL before the first
 // weight load; by a constant they are a multiply and a shift (3.8B M=1 pass:
 // 101 -> 51..66 instructions before the first load, 0.763 -> 0.728 ms).
+constexpr int kXcLane = 0, kXcRuns = 1, kXcShared = 16;
 template <int MR, int P, bool CHECK, int LM, bool H, bool EP, bool AFF = false,
-          int XC = 0, int NBLC = 0>
+          int XC = kXcLane, int NBLC = 0>
 __global__ __launch_bounds__(256) void k_gemv_kmajor(
     const float *__restrict__ x, const uint8_t *__restrict__ Pq, const void *__restrict__ Ps,
     const void *__restrict__ Pz, int M, int K, int N, int G, int NBL_arg,
@@ -186,12 +189,13 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
         for (int b = bl; LM == 1 ? b < NB : (b == bl && b < NB); b += NBL) {
             // activations of this block, for each of the MR rows
             float xr[MR][kBlock];
-            f32x4_t xg[XC == 1 ? MR : 1][XC == 1 ? kBlock / 4 : 1];  // 16 bytes of each of 8 runs
-            constexpr int XG = XC > 16 ? XC - 16 : 1;  // shared mode: column slots
-            constexpr int XW = XC > 16 ? kBlock / 4 / XG : 1;  // chunks per thread and row
-            f32x4_t xw[XC > 16 ? MR : 1][XW];
+            constexpr bool RUNS = XC == kXcRuns, SHARED = XC > kXcShared;
+            f32x4_t xg[RUNS ? MR : 1][RUNS ? kBlock / 4 : 1];  // 16 bytes of each of 8 runs
+            constexpr int XG = SHARED ? XC - kXcShared : 1;    // column slots sharing the rows
+            constexpr int XW = SHARED ? kBlock / 4 / XG : 1;   // chunks per thread and row
+            f32x4_t xw[SHARED ? MR : 1][XW];
             const int lw = L & 63;
-            if (XC > 16) {
+            if (SHARED) {
 #pragma unroll
                 for (int r = 0; r < MR; ++r) {
                     const float *xrow = x + (size_t)min(m0 + r, M - 1) * K;
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                         xw[r][i] = *reinterpret_cast<const f32x4_t *>(xrow + 4 * (L + i * XG * NBL));
                 }
             }
-            if (XC == 1) {
+            if (RUNS) {
                 // run i: the 8 blocks of lane group i of this wave, from block
                 // bl(8 i); this lane takes block lw / 8 of it, bytes 16 (lw % 8)
 #pragma unroll
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                 }
             }
 #pragma unroll
-            for (int r = 0; r < (XC ? 0 : MR); ++r) {
+            for (int r = 0; r < (XC != kXcLane ? 0 : MR); ++r) {
                 const int m = min(m0 + r, M - 1);
                 const f32x4_t *xp = reinterpret_cast<const f32x4_t *>(x + (size_t)m * K + b * kBlock);
 #pragma unroll
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                 oz += sz;
             }
             __builtin_amdgcn_sched_barrier(0);  // every load in flight before the arithmetic
-            if (XC > 16) {
+            if (SHARED) {
                 // chunk c of row r to piece c % 8 of block slot c / 8
                 float *xs = red + MR * CC * NBL;
 #pragma unroll
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(256) void k_gemv_kmajor(
                         xr[r][4 * i + 3] = v.w;
                     }
             }
-            if (XC == 1) {
+            if (RUNS) {
                 // run i's pieces to block slot 8 i + lw / 8 of this wave's
                 // staging area; then this lane's own block is slot lw
                 float *xstage = red + MR * CC * NBL + (L & ~63) * (36 * MR);
@@ -584,59 +588,59 @@ hipError_t launch_gemv_kmajor(const KmajorPlan &p, const float *x, int64_t M, in
     const bool ep = act != W4_ACT_NONE || residual;  // fp32 scales only (checked by the caller)
 #define W4_KM_ARGS                                                                              \
     x, Pq, Ps, Pz, (int)M, (int)K, (int)N, p.groups, p.lanes_per_col, bias, residual, act, y
-#define W4_KM_LAUNCH2(MRV, PV, CV, LV, XCV, NV)                                                 \
-    if (affine)                                                                                 \
+#define W4_KM_LAUNCH2(MRV, PV, CV, LV, XCV, NV)                                                     \
+    if (affine)                                                                                     \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, true, XCV, NV>), grid,   \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
-    else if (f16)                                                                               \
+    else if (f16)                                                                                   \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, true, false, false, XCV, NV>), grid,   \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
-    else if (ep)                                                                                \
+    else if (ep)                                                                                    \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, true, false, XCV, NV>), grid,   \
                            dim3(p.threads), shm, stream, W4_KM_ARGS);                           \
-    else                                                                                        \
+    else                                                                                            \
         hipLaunchKernelGGL((k_gemv_kmajor<MRV, PV, CV, LV, false, false, false, XCV, NV>), grid,  \
                            dim3(p.threads), shm, stream, W4_KM_ARGS)
 // Constant-NBL instantiations: one or two rows with whole-run activation
 // loads and 96 or 256 lanes per column (the 3.8B shapes' K = 3072 and 8192);
 // and one or two rows with 32 lanes per column (K = 544 .. 1024), whose
 // column sums stay in registers and are stored by one lane of each half.
-#define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                           \
-    if (MRV <= 2 && LV != 1 && xc) {                                                            \
-        if constexpr (MRV == 1 && LV == 2) {                                                    \
-            if (xs && p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, 18, 96); }        \
-            else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, 1, 96); }          \
-            else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
-            else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }       \
-            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
-        } else if constexpr (MRV == 2 && LV == 2) {                                             \
-            if (xs && p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, 18, 96); }        \
-            else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 32); }       \
-            else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 96); }       \
-            else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 256); }     \
-            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, true, 0); }                                   \
-        } else {                                                                                \
-            W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1, 0);                             \
-        }                                                                                       \
-    } else {                                                                                    \
-        if constexpr (MRV <= 2 && LV == 2) {                                                    \
-            if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 32); }           \
-            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 0); }                                  \
-        } else {                                                                                \
-            W4_KM_LAUNCH2(MRV, PV, CV, LV, false, 0);                                           \
-        }                                                                                       \
+#define W4_KM_LAUNCH(MRV, PV, CV, LV)                                                               \
+    if (MRV <= 2 && LV != 1 && xc) {                                                                \
+        if constexpr (MRV == 1 && LV == 2) {                                                        \
+            if (xs && p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcShared + 2, 96); } \
+            else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 96); }        \
+            else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 256); }      \
+            else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 32); }        \
+            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 0); }                                    \
+        } else if constexpr (MRV == 2 && LV == 2) {                                                 \
+            if (xs && p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcShared + 2, 96); } \
+            else if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 32); }        \
+            else if (p.lanes_per_col == 96) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 96); }        \
+            else if (p.lanes_per_col == 256) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 256); }      \
+            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcRuns, 0); }                                    \
+        } else {                                                                                    \
+            W4_KM_LAUNCH2(MRV, PV, CV, LV, MRV <= 2 && LV != 1 ? kXcRuns : kXcLane, 0);             \
+        }                                                                                           \
+    } else {                                                                                        \
+        if constexpr (MRV <= 2 && LV == 2) {                                                        \
+            if (p.lanes_per_col == 32) { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcLane, 32); }             \
+            else { W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcLane, 0); }                                    \
+        } else {                                                                                    \
+            W4_KM_LAUNCH2(MRV, PV, CV, LV, kXcLane, 0);                                             \
+        }                                                                                           \
     }
 #define W4_KM_CASE(MRV, PV)                                                                     \
-    if (p.rows == MRV && p.passes == PV) {                                                      \
-        if (check) {                                                                            \
-            if (lm == 1) { W4_KM_LAUNCH(MRV, PV, true, 1); }                                    \
-            else if (lm == 2) { W4_KM_LAUNCH(MRV, PV, true, 2); }                               \
-            else { W4_KM_LAUNCH(MRV, PV, true, 0); }                                            \
-        } else {                                                                                \
-            if (lm == 1) { W4_KM_LAUNCH(MRV, PV, false, 1); }                                   \
-            else if (lm == 2) { W4_KM_LAUNCH(MRV, PV, false, 2); }                              \
-            else { W4_KM_LAUNCH(MRV, PV, false, 0); }                                           \
-        }                                                                                       \
+    if (p.rows == MRV && p.passes == PV) {                                                          \
+        if (check) {                                                                                \
+            if (lm == 1) { W4_KM_LAUNCH(MRV, PV, true, 1); }                                        \
+            else if (lm == 2) { W4_KM_LAUNCH(MRV, PV, true, 2); }                                   \
+            else { W4_KM_LAUNCH(MRV, PV, true, 0); }                                                \
+        } else {                                                                                    \
+            if (lm == 1) { W4_KM_LAUNCH(MRV, PV, false, 1); }                                       \
+            else if (lm == 2) { W4_KM_LAUNCH(MRV, PV, false, 2); }                                  \
+            else { W4_KM_LAUNCH(MRV, PV, false, 0); }                                               \
+        }                                                                                           \
         return hipGetLastError();                                                               \
     }
     W4_KM_CASE(1, 1) W4_KM_CASE(1, 2) W4_KM_CASE(1, 3) W4_KM_CASE(1, 4)
