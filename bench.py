@@ -456,8 +456,16 @@ def main():
         mss, _ = time_graph(gs, max(5, args.steps // 2), 2)
         del gs
         us = 1e3 * mss / len(sub)
+        # the same matrix replayed as often, so that it sits in the Infinity
+        # Cache: how much of a launch is its bytes, and how much fixed cost
+        gw = capture(lambda: run_pass([sub[0]] * len(sub), layout=args.kernel))
+        msw, _ = time_graph(gw, max(5, args.steps // 2), 2)
+        del gw
+        usw = 1e3 * msw / len(sub)
         per_shape[f"{K}x{N}"] = {"us": round(us, 3),
-                                 "GB_s": round(sub[0].bytes / (us * 1e-6) / 1e9, 1)}
+                                 "GB_s": round(sub[0].bytes / (us * 1e-6) / 1e9, 1),
+                                 "us_cache_warm": round(usw, 3),
+                                 "cold_over_warm": round(us / usw, 3)}
     log(f"GEMV per launch: {1e3 * avg_ms:.2f} us avg, {achieved:.1f} GB/s; {per_shape}")
     traffic, traffic_detail = committed_traffic()
     profile = committed_trace(avg_bytes, launches)
