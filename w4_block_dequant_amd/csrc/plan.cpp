@@ -242,7 +242,7 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     // leave at least 512 workgroups, else 3, 2 or 1 (3.8B M=1 shapes, us per
     // launch: 3072 x 9216 4 passes 5.62 against 5.79 with 6; 3072 x 16384 4
     // passes 7.89 against 8.53 with 8; 3072 x 3072 3 passes 3.60; the M=1
-    // pass 0.733 -> 0.711 ms).  Two rows keep their passes (M=2 pass 1.153
+    // pass 0.733 -> 0.711 ms), a multiple of 256 workgroups first (below).  Two rows keep their passes (M=2 pass 1.153
     // -> 1.079 ms).  Four rows stay on the matrix cores: with the shared
     // activations the four-row GEMV is bound by its arithmetic (M=4 pass
     // 2.40 ms against 1.50).  K = 8192 keeps one 256-lane column slot per
@@ -250,12 +250,19 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     // 5.67 against 5.47 us; M = 2: 10.3 against 7.5).  W4_KMAJOR_XS=0 turns
     // it off.
     static const int64_t env_xs = env_int_or("W4_KMAJOR_XS", 1);
-    // passes for the shared mode (0: none qualifies)
+    // passes for the shared mode (0: none qualifies): the most, up to 4, that
+    // leave at least 512 workgroups, preferring a count that is a multiple of
+    // the 256 compute units (3072 x 9216: 3 passes, 1536 workgroups, 5.55 us
+    // against 5.65 with 4 passes and 4.5 workgroups per compute unit;
+    // interleaved runs in one session)
     auto shared_passes = [&]() -> int {
         if (env_p > 0 || p.rows != 1) return p.passes;
         static const int cand[] = {4, 3, 2, 1};
-        for (int P : cand)
-            if (cdiv(N, 2 * (int64_t)P) >= 512) return P;
+        for (int even = 1; even >= 0; --even)
+            for (int P : cand) {
+                const int64_t wgs = cdiv(N, 2 * (int64_t)P);
+                if (wgs >= 512 && (!even || wgs % 256 == 0)) return P;
+            }
         return 0;
     };
     if (p.xc && env_xs != 0 && p.rows <= 2 && p.groups == 2 &&
