@@ -804,11 +804,12 @@ def test_f16_matmul_kmajor(M, K, N):
 
 
 # K = 3072 and N >= 3072 at M = 1 and 2: two column slots per workgroup read
-# the activations once and share them through LDS; at M = 1 4096 columns take
-# 4 passes (512 workgroups, no ragged tail) and 3080 take 3 passes with a
-# ragged last workgroup; at M = 2 both take 4 passes (3080: ragged).  Every
-# scale format and epilogue goes through that mode here.
-@pytest.mark.parametrize("K,N", [(3072, 3080), (3072, 4096), (8192, 3080)])
+# the activations once and share them through LDS.  At M = 1 4096 columns
+# take 4 passes (512 workgroups, no ragged tail), 3078 and 3080 take 3 (3080
+# with a ragged last workgroup); at M = 2 4096 take 4 passes and 3078 and
+# 3080 take 2 (3078 ragged).  K = 8192 keeps one column slot per workgroup.
+# Every scale format and epilogue goes through these modes here.
+@pytest.mark.parametrize("K,N", [(3072, 3078), (3072, 3080), (3072, 4096), (8192, 3080)])
 @pytest.mark.parametrize("variant", ["plain", "f16", "g64", "gelu", "swiglu+res"])
 @pytest.mark.parametrize("M", [1, 2])
 def test_kmajor_shared_activations(M, variant, K, N):

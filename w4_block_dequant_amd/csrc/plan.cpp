@@ -186,17 +186,19 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     p.passes = 1;
     bool found = false;
     if (env_p <= 0 && p.rows == 2) {
-        // Two rows: the most passes that still give a workgroup to every
-        // compute unit, whether or not the count divides evenly (3072 x 9216:
-        // 4 passes 11.2 us against 16.8 us for the even 2; 3072 x 3072: 6.2
-        // against 6.9 us)
-        for (int i = 0; i < nallowed && !found; ++i) {
-            const int P = allowed[i];
-            if (cdiv(N, (int64_t)p.groups * P) * cdiv(M, p.rows) >= 256) {
-                p.passes = P;
-                found = true;
+        // Two rows: the most passes that leave two workgroups per compute
+        // unit, else one, whether or not the count divides evenly (with the
+        // workgroup-shared activations, us per launch: 3072 x 3072 2 passes
+        // 4.42 against 4.81 with 4; 3072 x 9216, 3072 x 16384 and 8192 x
+        // 3072 keep 4: 7.97 / 11.0 / 7.47 against 8.12 / 11.7 / 9.75 with 2)
+        for (int64_t min_wgs = 512; min_wgs >= 256 && !found; min_wgs /= 2)
+            for (int i = 0; i < nallowed && !found; ++i) {
+                const int P = allowed[i];
+                if (cdiv(N, (int64_t)p.groups * P) * cdiv(M, p.rows) >= min_wgs) {
+                    p.passes = P;
+                    found = true;
+                }
             }
-        }
     }
     if (env_p <= 0) {
         // at least two workgroups per compute unit where that is possible
