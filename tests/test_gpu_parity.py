@@ -659,7 +659,8 @@ def test_kmajor_whole_k_kernel(M, K, N):
 
 
 @pytest.mark.parametrize("act,res", [("gelu", False), ("swiglu", True), ("none", True)])
-@pytest.mark.parametrize("M,K,N", [(4, 384, 2344), (7, 384, 2344), (12, 128, 16400)])
+@pytest.mark.parametrize("M,K,N", [(4, 384, 2344), (7, 384, 2344), (12, 128, 16400),
+                                   (4, 3072, 2064), (3, 8192, 2048)])
 def test_kmajor_whole_k_epilogue(M, K, N, act, res):
     note(f"kmajor whole-K epilogue M={M} act={act} residual={res}")
     W = mixed_weights(K, N, cfg=243)
@@ -675,9 +676,9 @@ def test_kmajor_whole_k_epilogue(M, K, N, act, res):
     assert_bound(y, y_ref, bound, f"kmajor whole-K epilogue {act} M={M}")
 
 
-@pytest.mark.parametrize("M", [3, 8])
-def test_kmajor_whole_k_special_inputs(M):
-    K, N = 768, 2304
+@pytest.mark.parametrize("M,K", [(3, 768), (8, 768), (4, 3072)])
+def test_kmajor_whole_k_special_inputs(M, K):
+    N = 2304
     W = mixed_weights(K, N, cfg=245)
     W[300, :] = 0.0
     Wq, s, z = ORC.quantize_pack(W)

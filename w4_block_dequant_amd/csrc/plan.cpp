@@ -324,6 +324,11 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
         if (wgs * mgroups >= 128) {
             p.kind = X3Plan::kFullK;
             p.mb = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+            // up to 4 rows the three bf16 parts of each row are rows of one
+            // MFMA (12 of its 16), instead of three MFMAs with 4 rows each
+            // (W4_X3K_P3=0: three MFMAs)
+            static const int64_t env_p3 = env_int_or("W4_X3K_P3", 1);
+            p.p3 = p.mb == 4 && env_p3 != 0;
             p.nt = (int)tpw;
             // 8 waves, each loading one quad ahead of its arithmetic; 4 where K
             // is short.  3.8B pass (128 launches) at M = 4 / 8: 4 quads ahead
@@ -338,6 +343,19 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
             // quads of loads in flight per wave (0: the kernel's default for its row count)
             static const int64_t env_d = env_int("W4_X3K_D");
             p.dq = (env_d >= 1 && env_d <= 4) ? (int)env_d : 0;
+            // Up to 4 rows with 3 or 8 quads per wave (K = 3072 or 8192): the
+            // straight-line kernel, every load of a quad in flight before its
+            // arithmetic (all three at K = 3072, two at a time at 8192); 3.8B
+            // pass at M = 4 1.481 -> 1.441 ms.  At 8 and 16 rows it is not
+            // faster (1.703 -> 1.730, 2.080 -> 2.123 ms at two ahead: the
+            // larger activation buffers cost occupancy).  W4_X3K_NQC=0 turns
+            // it off, =1 also allows it past 4 rows.
+            static const int64_t env_nqc = env_int_or("W4_X3K_NQC", 2);
+            if (env_nqc != 0 && (p.mb == 4 || env_nqc == 1) && p.waves == 8 && NQ % 8 == 0 &&
+                (NQ / 8 == 3 || NQ / 8 == 8)) {
+                p.nqc = (int)(NQ / 8);
+                if (p.dq == 0 && p.mb == 4 && p.nt == 1) p.dq = p.nqc == 3 ? 3 : 2;
+            }
             p.col_wgs = wgs;
             p.mgroups = mgroups;
             p.splits = 1;

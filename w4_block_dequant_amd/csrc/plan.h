@@ -87,6 +87,8 @@ struct X3Plan {
     enum Kind { kNone = 0, kRun = 1, kFullK = 2 } kind = kNone;
     int mt = 1, nt = 1, dq = 2;
     int mb = 4, waves = 4;  // kFullK: rows built, waves per workgroup
+    bool p3 = false;        // kFullK, mb == 4: the three parts share one MFMA
+    int nqc = 0;            // kFullK: quads per wave when fixed at compile time (3 or 8), else 0
     int64_t col_wgs = 0, mgroups = 0, splits = 1, quads_per_wg = 0, npad = 0;
     size_t workspace = 0;
 };

@@ -309,6 +309,20 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
     return d;
 }
 
+// c + (fp16 half of h) in fp32 with one rounding (v_fma_mix_f32, the half
+// widened exactly).  With h = 1024 + q or 64 + q (exact fp16 integers) and
+// c = -(1024 + z) or -(64 + z), the result is q - z exactly.
+__device__ __forceinline__ float mix_lo(uint32_t h, float c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(c));
+    return d;
+}
+__device__ __forceinline__ float mix_hi(uint32_t h, float c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(c));
+    return d;
+}
+
 __device__ __forceinline__ uint32_t hi16_pair(float lo, float hi) {
     // (upper half of lo) | (upper half of hi) << 16: two truncated bf16
     return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi),
@@ -319,7 +333,7 @@ __device__ __forceinline__ float trunc_rest(float v) {
     return v - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u);
 }
 
-template <int MB, int TPW, int W, int D, bool H>
+template <int MB, int TPW, int W, int D, bool H, bool P3, int NQC>
 __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, int M, int K,
                                                    const uint8_t *__restrict__ Pq,
                                                    const void *__restrict__ Ps,
@@ -339,7 +353,10 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
     constexpr int NBLD = 4 / ABLK;  // A images per quad
     constexpr int TQ_BYTES = TPW * 64 * 16;
     constexpr int PART_BYTES = ABLK * MB * 64;
-    constexpr int WAVE_BYTES = TQ_BYTES + 3 * PART_BYTES;
+    // part planes 16 bytes apart in the bank order under P3, where one read
+    // instruction takes rows of two planes at once (no two-way bank conflict)
+    constexpr int PSTRIDE = PART_BYTES + (P3 ? 16 : 0);
+    constexpr int WAVE_BYTES = TQ_BYTES + 3 * PSTRIDE;
     static_assert(WAVE_BYTES >= TPW * 64 * 16, "the wave partials fit the wave's area");
     __shared__ __attribute__((aligned(16))) unsigned char lds[W * WAVE_BYTES];
 
@@ -363,7 +380,12 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
     const uint32_t ox = (uint32_t)min(bm, M - 1) * (uint32_t)K + 32u * bb + 8u * bg;
     uint32_t *const wimg = reinterpret_cast<uint32_t *>(img + (bb * MB + bm) * 64 + bg * 16);
     // A reader: lane (g, c) takes row min(c, MB - 1), slots 8 g .. 8 g + 7
-    const int aoff = min(c, MB - 1) * 64 + g * 16;
+    // P3 (at most 4 rows): A row c is part c / 4 (h, m, l) of row c % 4, so
+    // one MFMA per block forms all three part sums (rows 12-15 repeat the l
+    // part and are never read); lane group p then holds part p's sums.
+    static_assert(!P3 || MB == 4, "three parts share one MFMA only for 4 rows");
+    const int aoff = P3 ? min(c >> 2, 2) * PSTRIDE + (c & 3) * 64 + g * 16
+                        : min(c, MB - 1) * 64 + g * 16;
 
     const int nq = wave < NQ ? (NQ - 1 - wave) / W + 1 : 0;  // this wave's quads
     // masks and fp16 bases of the code conversion, in registers
@@ -400,78 +422,109 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
     for (int t = 0; t < TPW; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
     const f32x4v zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    if (nq > 0) {
-        KQuadLoads<TPW, NBLD> L[D];
+    // one quad's arithmetic on loads already issued into R
+    auto process = [&](KQuadLoads<TPW, NBLD> &R) {
+        // codes: lane (g, c) holds block 4 q + g of its column; word g
+        // of block 4 q + blk is with lane (blk, c)
+        uint32_t wq[TPW][4];
 #pragma unroll
-        for (int d = 0; d < D; ++d) issue(d, L[d]);
-        for (int i0 = 0; i0 < nq; i0 += D) {
+        for (int t = 0; t < TPW; ++t) {
+            tq[t * 64 + lane] = R.w[t];
+            const uint32_t *tw = reinterpret_cast<const uint32_t *>(tq + t * 64);
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                if (i0 + d >= nq) break;
-                KQuadLoads<TPW, NBLD> &R = L[d];
-                // codes: lane (g, c) holds block 4 q + g of its column; word g
-                // of block 4 q + blk is with lane (blk, c)
-                uint32_t wq[TPW][4];
+            for (int blk = 0; blk < 4; ++blk) wq[t][blk] = tw[(blk * 16 + c) * 4 + g];
+        }
+#pragma unroll
+        for (int b = 0; b < NBLD; ++b) {
+            // A image b: the three bf16 parts of this lane's 8 activations
+            const float *f = reinterpret_cast<const float *>(&R.xa[b][0]);
+            u32x4_t ph, pm, pl;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float a0 = f[2 * p], a1 = f[2 * p + 1];
+                const float r0 = trunc_rest(a0), r1 = trunc_rest(a1);
+                ph[p] = hi16_pair(a0, a1);
+                pm[p] = hi16_pair(r0, r1);
+                pl[p] = hi16_pair(trunc_rest(r0), trunc_rest(r1));
+            }
+            *reinterpret_cast<u32x4_t *>(wimg) = ph;
+            *reinterpret_cast<u32x4_t *>(wimg + PSTRIDE / 4) = pm;
+            *reinterpret_cast<u32x4_t *>(wimg + 2 * PSTRIDE / 4) = pl;
+#pragma unroll
+            for (int ib = 0; ib < ABLK; ++ib) {
+                const int blk = b * ABLK + ib;
+                const unsigned char *ap = img + ib * MB * 64 + aoff;
+                const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
+                bf16x8_t am, al;
+                if (!P3) {
+                    am = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PSTRIDE));
+                    al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + 2 * PSTRIDE));
+                }
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
-                    tq[t * 64 + lane] = R.w[t];
-                    const uint32_t *tw = reinterpret_cast<const uint32_t *>(tq + t * 64);
-#pragma unroll
-                    for (int blk = 0; blk < 4; ++blk) wq[t][blk] = tw[(blk * 16 + c) * 4 + g];
-                }
-#pragma unroll
-                for (int b = 0; b < NBLD; ++b) {
-                    // A image b: the three bf16 parts of this lane's 8 activations
-                    const float *f = reinterpret_cast<const float *>(&R.xa[b][0]);
-                    u32x4_t ph, pm, pl;
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const float a0 = f[2 * p], a1 = f[2 * p + 1];
-                        const float r0 = trunc_rest(a0), r1 = trunc_rest(a1);
-                        ph[p] = hi16_pair(a0, a1);
-                        pm[p] = hi16_pair(r0, r1);
-                        pl[p] = hi16_pair(trunc_rest(r0), trunc_rest(r1));
+                    const uint32_t w = wq[t][blk];
+                    // -(1024 + z) and -(64 + z) as fp32 bit patterns (z
+                    // lands in the mantissa bits of unit 1)
+                    const uint32_t z = (R.z[t] >> (4 * blk)) & 15u;
+                    const float cE = __builtin_bit_cast(float, 0xC4800000u | (z << 13));
+                    const float cO = __builtin_bit_cast(float, 0xC2800000u | (z << 17));
+                    const uint32_t hv = w >> 8;
+                    const uint32_t e0 = and_or(w, kLoMask, kLoBase);   // 1024 + q, k 0 and 4
+                    const uint32_t o0 = and_or(w, kHiMask, kHiBase);   // 64 + q, k 1 and 5
+                    const uint32_t e1 = and_or(hv, kLoMask, kLoBase);  // k 2 and 6
+                    const uint32_t o1 = and_or(hv, kHiMask, kHiBase);  // k 3 and 7
+                    // q - z is a small integer: its fp32 pattern's upper
+                    // half is its bf16 pattern (pairs packed by v_perm)
+                    const u32x4_t bw = {hi16_pair(mix_lo(e0, cE), mix_lo(o0, cO)),
+                                        hi16_pair(mix_lo(e1, cE), mix_lo(o1, cO)),
+                                        hi16_pair(mix_hi(e0, cE), mix_hi(o0, cO)),
+                                        hi16_pair(mix_hi(e1, cE), mix_hi(o1, cO))};
+                    const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+                    f32x4v dd;
+                    if (P3) {
+                        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, zero4, 0, 0, 0);
+                    } else {
+                        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, zero4, 0, 0, 0);
+                        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bv, dd, 0, 0, 0);
+                        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, dd, 0, 0, 0);
                     }
-                    *reinterpret_cast<u32x4_t *>(wimg) = ph;
-                    *reinterpret_cast<u32x4_t *>(wimg + PART_BYTES / 4) = pm;
-                    *reinterpret_cast<u32x4_t *>(wimg + 2 * PART_BYTES / 4) = pl;
+                    const float sc = R.s[t][blk];
 #pragma unroll
-                    for (int ib = 0; ib < ABLK; ++ib) {
-                        const int blk = b * ABLK + ib;
-                        const unsigned char *ap = img + ib * MB * 64 + aoff;
-                        const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
-                        const bf16x8_t am = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PART_BYTES));
-                        const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + 2 * PART_BYTES));
-#pragma unroll
-                        for (int t = 0; t < TPW; ++t) {
-                            const uint32_t w = wq[t][blk];
-                            const uint32_t z = (R.z[t] >> (4 * blk)) & 15u;
-                            const half2_t zE = as_half2((0x6400u | z) * 0x00010001u);
-                            const half2_t zO = as_half2((0x5400u | (z << 4)) * 0x00010001u);
-                            const uint32_t hv = w >> 8;
-                            const half2_t e0 = as_half2(and_or(w, kLoMask, kLoBase)) - zE;   // k 0, 4
-                            const half2_t o0 = as_half2(and_or(w, kHiMask, kHiBase)) - zO;   // k 1, 5
-                            const half2_t e1 = as_half2(and_or(hv, kLoMask, kLoBase)) - zE;  // k 2, 6
-                            const half2_t o1 = as_half2(and_or(hv, kHiMask, kHiBase)) - zO;  // k 3, 7
-                            const u32x4_t bw = {pack_bf16((float)e0.x, (float)o0.x),
-                                                pack_bf16((float)e1.x, (float)o1.x),
-                                                pack_bf16((float)e0.y, (float)o0.y),
-                                                pack_bf16((float)e1.y, (float)o1.y)};
-                            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
-                            f32x4v dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, zero4, 0, 0, 0);
-                            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bv, dd, 0, 0, 0);
-                            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, dd, 0, 0, 0);
-                            const float sc = R.s[t][blk];
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(sc, dd[v], acc[t][v]);
-                        }
-                    }
+                    for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(sc, dd[v], acc[t][v]);
                 }
+            }
+        }
 #pragma unroll
-                for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(acc[t][v]));
-                if (i0 + d + D < nq) issue(i0 + d + D, R);
+            for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(acc[t][v]));
+    };
+
+    if (nq > 0) {
+        if constexpr (NQC > 0) {
+            // Every wave has exactly NQC quads (the plan checks it), so the
+            // loop unrolls into straight-line code: D quads in flight, each
+            // wait covers only the oldest quad's loads (a loop with the
+            // loads under a runtime condition gets a full wait at its head).
+            KQuadLoads<TPW, NBLD> L[D];
+#pragma unroll
+            for (int d = 0; d < D; ++d) issue(d, L[d]);
+#pragma unroll
+            for (int i = 0; i < NQC; ++i) {
+                process(L[i % D]);
+                if (i + D < NQC) issue(i + D, L[i % D]);
+            }
+        } else {
+            KQuadLoads<TPW, NBLD> L[D];
+#pragma unroll
+            for (int d = 0; d < D; ++d) issue(d, L[d]);
+            for (int i0 = 0; i0 < nq; i0 += D) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    if (i0 + d >= nq) break;
+                    process(L[d]);
+                    if (i0 + d + D < nq) issue(i0 + d + D, L[d]);
+                }
             }
         }
     }
@@ -486,10 +539,19 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
     __syncthreads();
     const float *rf = reinterpret_cast<const float *>(lds);
     auto total = [&](int m, int nl) {
-        const int idx = ((nl >> 4) * 64 + (m >> 2) * 16 + (nl & 15)) * 4 + (m & 3);
         float v = 0.0f;
+        if (P3) {  // m < 4: the h, m and l sums sit in lane groups 0, 1, 2
+            const int idx = ((nl >> 4) * 64 + (nl & 15)) * 4 + m;
 #pragma unroll
-        for (int w2 = 0; w2 < W; ++w2) v += rf[w2 * TPW * 256 + idx];
+            for (int w2 = 0; w2 < W; ++w2) {
+                const float *r = rf + w2 * TPW * 256 + idx;
+                v += r[0] + r[64] + r[128];
+            }
+        } else {
+            const int idx = ((nl >> 4) * 64 + (m >> 2) * 16 + (nl & 15)) * 4 + (m & 3);
+#pragma unroll
+            for (int w2 = 0; w2 < W; ++w2) v += rf[w2 * TPW * 256 + idx];
+        }
         return v;
     };
     constexpr int CW = 16 * TPW;
@@ -512,6 +574,43 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
 
 }  // namespace
 
+template <int MB, int TPW, int W, int D, bool H, int NQC>
+void launch_x3k_n(bool p3, dim3 grid, hipStream_t stream, const float *x, int64_t M, int64_t K,
+                  const uint8_t *Pq, const void *Ps, const uint8_t *Pz, int64_t N,
+                  const float *bias, const float *residual, int act, float *y) {
+    if constexpr (MB == 4) {
+        if (p3) {
+            hipLaunchKernelGGL((k_mm_x3k<MB, TPW, W, D, H, true, NQC>), grid, dim3(64 * W), 0, stream,
+                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_mm_x3k<MB, TPW, W, D, H, false, NQC>), grid, dim3(64 * W), 0, stream, x,
+                       (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);
+}
+
+template <int MB, int TPW, int W, int D, bool H>
+void launch_x3k(bool p3, int nqc, dim3 grid, hipStream_t stream, const float *x, int64_t M,
+                int64_t K, const uint8_t *Pq, const void *Ps, const uint8_t *Pz, int64_t N,
+                const float *bias, const float *residual, int act, float *y) {
+    // straight-line variants for 3 and 8 quads per wave (K = 3072 and 8192
+    // with 8 waves), fp32 scales
+    if constexpr (!H && W == 8 && D <= 3) {
+        if (nqc == 3) {
+            launch_x3k_n<MB, TPW, W, D, H, 3>(p3, grid, stream, x, M, K, Pq, Ps, Pz, N, bias,
+                                              residual, act, y);
+            return;
+        }
+        if (nqc == 8) {
+            launch_x3k_n<MB, TPW, W, D, H, 8>(p3, grid, stream, x, M, K, Pq, Ps, Pz, N, bias,
+                                              residual, act, y);
+            return;
+        }
+    }
+    launch_x3k_n<MB, TPW, W, D, H, 0>(p3, grid, stream, x, M, K, Pq, Ps, Pz, N, bias, residual,
+                                      act, y);
+}
+
 hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, const uint8_t *Pq,
                         const void *Ps, bool f16, const uint8_t *Pz, int64_t N, const float *bias,
                         const float *residual, int act, float *y, void *workspace,
@@ -522,17 +621,18 @@ hipError_t launch_mm_x3(const X3Plan &p, const float *x, int64_t M, int64_t K, c
 #define W4_X3K(MBV, TPWV, WV, DV)                                                                  \
     if (!done && p.mb == MBV && p.nt == TPWV && p.waves == WV && (p.dq == DV || p.dq == 0)) {      \
         if (f16)                                                                                    \
-            hipLaunchKernelGGL((k_mm_x3k<MBV, TPWV, WV, DV, true>), grid, dim3(64 * WV), 0, stream, \
-                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);      \
+            launch_x3k<MBV, TPWV, WV, DV, true>(p.p3, p.nqc, grid, stream, x, M, K, Pq, Ps, Pz, N, bias,    \
+                                                residual, act, y);                                  \
         else                                                                                        \
-            hipLaunchKernelGGL((k_mm_x3k<MBV, TPWV, WV, DV, false>), grid, dim3(64 * WV), 0, stream, \
-                               x, (int)M, (int)K, Pq, Ps, Pz, (int)N, bias, residual, act, y);      \
+            launch_x3k<MBV, TPWV, WV, DV, false>(p.p3, p.nqc, grid, stream, x, M, K, Pq, Ps, Pz, N, bias,   \
+                                                 residual, act, y);                                 \
         done = true;                                                                                \
     }
 #define W4_X3K_W(MBV, TPWV, DV) W4_X3K(MBV, TPWV, 4, DV) W4_X3K(MBV, TPWV, 8, DV)
 #define W4_X3K_W3(MBV, DV) W4_X3K(MBV, 1, 4, DV) W4_X3K(MBV, 1, 8, DV) W4_X3K(MBV, 1, 16, DV)
         // the first instantiation of a row count is its default depth
-        W4_X3K_W3(4, 1) W4_X3K_W3(4, 2) W4_X3K_W3(4, 4) W4_X3K_W(4, 2, 1) W4_X3K_W(4, 2, 3)
+        W4_X3K_W3(4, 1) W4_X3K_W3(4, 2) W4_X3K_W3(4, 4) W4_X3K(4, 1, 8, 3) W4_X3K_W(4, 2, 1)
+        W4_X3K_W(4, 2, 3)
         W4_X3K_W3(8, 1) W4_X3K_W3(8, 2) W4_X3K_W(8, 2, 1) W4_X3K_W(8, 2, 2)
         W4_X3K_W3(16, 1) W4_X3K_W3(16, 2) W4_X3K_W(16, 2, 1) W4_X3K_W(16, 2, 2)
 #undef W4_X3K_W3
