@@ -375,8 +375,10 @@ __global__ __launch_bounds__(64 * W) void k_mm_x3k(const float *__restrict__ x, 
         os[t] = (uint32_t)nl * (uint32_t)NB;
         oz[t] = (uint32_t)nl * (uint32_t)(NB / 2);
     }
-    // A builder: lane = (row bm, image block bb, slot group bg), 8 activations
-    const int bm = lane / (4 * ABLK), bb = (lane >> 2) % ABLK, bg = lane & 3;
+    // A builder: lane = (image block bb, row bm, slot group bg), 8 activations;
+    // lane l writes bytes 16 l .. 16 l + 15 of each part plane, so a write
+    // instruction covers consecutive LDS banks (no bank conflict)
+    const int bb = lane / (4 * MB), bm = (lane >> 2) % MB, bg = lane & 3;
     const uint32_t ox = (uint32_t)min(bm, M - 1) * (uint32_t)K + 32u * bb + 8u * bg;
     uint32_t *const wimg = reinterpret_cast<uint32_t *>(img + (bb * MB + bm) * 64 + bg * 16);
     // A reader: lane (g, c) takes row min(c, MB - 1), slots 8 g .. 8 g + 7
