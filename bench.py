@@ -83,6 +83,9 @@ PROFILE_COMMANDS = (
     "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_F32 --output-format csv "
     "-d /tmp/w4prof/mfma -o run "
     "-- python bench.py --profile-run-mfma --steps 2",
+    "timeout -s KILL 300 rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU "
+    "SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --output-format csv "
+    "-d /tmp/w4prof/sq -o run -- python bench.py --profile-run-mfma --steps 2",
     "python bench.py --summarize-profiles /tmp/w4prof --out profiles",
 )
 
@@ -1071,6 +1074,44 @@ def summarize_profiles(src: str, out_dir: str):
             continue
         lines.append(f"| `{_short(k)}` | {len(ds)} | {util:.1f} | {h16 / ns / 1e3:.1f} | "
                      f"{bf / ns / 1e3:.1f} | {f32 / ns / 1e3:.1f} | {ns / len(ds) / 1e3:.2f} |")
+    # issue and wait counters of the same passes (a run of their own)
+    sq = {}
+    for f in _csvs(os.path.join(src, "sq"), "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            d = sq.setdefault((f, r["Dispatch_Id"]), {
+                "k": r["Kernel_Name"], "c": {},
+                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    sqk = {}
+    for d in sq.values():
+        if d["c"].get("SQ_WAVES", 0.0) > 0 and ("x3" in d["k"] or "mfma" in d["k"]):
+            sqk.setdefault(d["k"], []).append(d)
+    if sqk:
+        lines += ["", "Issue and wait counters (`--pmc SQ_WAVES SQ_WAVE_CYCLES SQ_INSTS_VALU "
+                  "SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_INSTS_LDS "
+                  "SQ_LDS_BANK_CONFLICT`, same passes, summed over each kernel's "
+                  "dispatches).  VALU busy: SQ_ACTIVE_INST_VALU (one quad-cycle, 4 clocks, "
+                  "per wave64 instruction) over the 1024 SIMDs x 2.4 GHz x the dispatch "
+                  "durations.  Waiting to issue: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (the wave "
+                  "holds an instruction it cannot issue yet); at a wait count: SQ_WAIT_ANY / "
+                  "SQ_WAVE_CYCLES.", "",
+                  "| kernel | dispatches | VALU instr per wave | VALU busy % | waiting to "
+                  "issue % | at a wait count % | LDS bank-conflict cycles per LDS instr | "
+                  "avg us |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for k, ds in sorted(sqk.items(), key=lambda kv: -sum(d["ns"] for d in kv[1])):
+            c = {n: sum(d["c"].get(n, 0.0) for d in ds) for n in (
+                "SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+                "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT")}
+            ns = sum(d["ns"] for d in ds)
+            busy = 100.0 * c["SQ_ACTIVE_INST_VALU"] * 4 / (1024 * 2.4 * ns)
+            wc = max(c["SQ_WAVE_CYCLES"], 1.0)
+            lines.append(
+                f"| `{_short(k)}` | {len(ds)} | {c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.0f} | "
+                f"{busy:.0f} | {100 * c['SQ_WAIT_INST_ANY'] / wc:.0f} | "
+                f"{100 * c['SQ_WAIT_ANY'] / wc:.0f} | "
+                f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1.0):.2f} | "
+                f"{ns / len(ds) / 1e3:.2f} |")
     with open(os.path.join(out_dir, MFMA_SUMMARY), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(open(os.path.join(out_dir, MFMA_SUMMARY)).read())
