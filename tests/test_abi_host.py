@@ -108,7 +108,10 @@ def test_every_body_shape_is_planned():
     import synth
     for K, N in synth.GPT2_SHAPES + synth.DENSE38_SHAPES:
         assert check(1, K, N, ws=A, wsb=w4.w4_matmul_workspace_bytes(1, K, N)) == w4.W4_OK
-    assert w4.i8_head_workspace_bytes(768, 50257) > 0
+    # the GPT-2 head (K = 768) runs the one-launch whole-K kernel: no
+    # workspace; K off the whole-K sizes takes the split-K kernel and its planes
+    assert w4.i8_head_workspace_bytes(768, 50257) == 0
+    assert w4.i8_head_workspace_bytes(800, 50257) > 0
 
 
 @pytest.mark.skipif(not NO_GPU, reason="needs a machine without a GPU")
@@ -131,9 +134,9 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.i8_quantize_head(A, 768, 100, 99, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.i8_quantize_head(A, 768, 100, 100, A + 1, A, None, None) == w4.W4_ERR_MISALIGNED
     assert lib.i8_head_logits(A, 768, A, 50256, A, 50257, A, None, 0, None) == w4.W4_ERR_BAD_SHAPE
-    need = w4.i8_head_workspace_bytes(768, 50257)
-    assert lib.i8_head_logits(A, 768, A, 50257, A, 50257, A, None, 0, None) == w4.W4_ERR_WORKSPACE
-    assert lib.i8_head_logits(A, 768, A, 50257, A, 50257, A, A, need - 4, None) == w4.W4_ERR_WORKSPACE
+    need = w4.i8_head_workspace_bytes(800, 50257)   # K = 800: the split-K head
+    assert lib.i8_head_logits(A, 800, A, 50257, A, 50257, A, None, 0, None) == w4.W4_ERR_WORKSPACE
+    assert lib.i8_head_logits(A, 800, A, 50257, A, 50257, A, A, need - 4, None) == w4.W4_ERR_WORKSPACE
     assert lib.i8_embed(A, 4, A, 50257, A, 768, 50258, A, None, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.i8_embed(A + 4, 4, A, 50257, A, 768, 50257, A, None, None) == w4.W4_ERR_MISALIGNED
     km = lib.w4_check_matmul_kmajor_args

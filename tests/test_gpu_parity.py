@@ -272,7 +272,15 @@ def test_matmul_rejects_bad_device_pointers():
 # int8 head and token lookup
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("K,N,ldq", [(768, 50257, 50257), (768, 50257, 50272), (100, 37, 37),
-                                     (100, 37, 48), (64, 300, 301), (33, 1000, 1003)])
+                                     (100, 37, 48), (64, 300, 301), (33, 1000, 1003),
+                                     # the whole-K kernel: K = 64 L, L = 4, 8, 12, 16; a
+                                     # ragged last workgroup, chunks wholly past N, odd ldq;
+                                     # 128-column workgroups below N = 32768, 256 above
+                                     (256, 16400, 16401), (512, 16384, 16384),
+                                     (768, 16385, 16387), (1024, 20000, 20016),
+                                     (1024, 16513, 16513), (256, 32769, 32771),
+                                     (512, 33000, 33008), (1024, 40000, 40000),
+                                     (768, 32999, 32999)])
 def test_head(K, N, ldq):
     note(f"head K={K} N={N} ldq={ldq}")
     cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 220

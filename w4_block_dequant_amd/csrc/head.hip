@@ -210,6 +210,70 @@ __global__ __launch_bounds__(64 * WAVES) void k_head_logits(
     }
 }
 
+// One launch, no partial sums: a workgroup of WV waves owns 16 LPR columns
+// and all K = L WV 64 / LPR rows.  Lane (r, j) = (lane / LPR, lane % LPR) of
+// wave w takes the L consecutive rows k = (w 64 / LPR + r) L + i and, of
+// each, the 16 bytes of columns n0 + 16 j .. n0 + 16 j + 15, so the LPR lanes
+// of a row read 16 LPR contiguous bytes (with LPR = 8 one cache line) and a
+// load instruction covers 64 / LPR rows.  Every row's load is issued before
+// the first product.  The 16 column sums of a lane are added over the wave's
+// row lanes by a fixed xor butterfly (every lane ends with the same totals),
+// then over the waves in wave order in LDS.
+template <int L, bool ALIGNED, int LPR, int WV>
+__global__ __launch_bounds__(64 * WV) void k_head_whole(const float *__restrict__ x, int K,
+                                                        const int8_t *__restrict__ Q, int64_t ldq,
+                                                        const float *__restrict__ hs, int N,
+                                                        float *__restrict__ logits) {
+    constexpr int CW = 16 * LPR, RPI = 64 / LPR;  // columns per workgroup, rows per instruction
+    __shared__ float red[WV][CW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane / LPR, j = lane % LPR;
+    const int n0 = blockIdx.x * CW;
+    const int col = n0 + 16 * j;
+    // a chunk wholly past N re-reads the last chunk holding column N - 1
+    const int cc = col < N ? col : ((N - 1) & ~15);
+    const int k0 = (RPI * wave + r) * L;
+    const int64_t total = (int64_t)K * ldq;
+
+    float xr[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) xr[i] = x[k0 + i];
+    u32x4_t w[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) w[i] = load_row16<ALIGNED>(Q, (int64_t)(k0 + i) * ldq + cc, total);
+    __builtin_amdgcn_sched_barrier(0);  // every row in flight first
+
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        fma_i8_word(xr[i], w[i].x, acc + 0);
+        fma_i8_word(xr[i], w[i].y, acc + 4);
+        fma_i8_word(xr[i], w[i].z, acc + 8);
+        fma_i8_word(xr[i], w[i].w, acc + 12);
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        float v = acc[c];
+#pragma unroll
+        for (int m = LPR; m < 64; m *= 2) v += __shfl_xor(v, m);
+        acc[c] = v;
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) red[wave][16 * j + c] = acc[c];
+    }
+    __syncthreads();
+    for (int t = tid; t < CW; t += 64 * WV) {
+        const int n = n0 + t;
+        float v = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < WV; ++w2) v += red[w2][t];
+        if (n < N) logits[n] = (v * 16777216.0f) * hs[n];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_head_quantize(const float *E, int64_t K, int64_t N, int64_t ldq, int8_t *Q,
@@ -235,6 +299,26 @@ hipError_t launch_head_logits(const HeadPlan &p, const float *x, int64_t K, cons
                               void *workspace, hipStream_t stream) {
     if (p.kind == HeadPlan::kEmpty) return hipSuccess;
     if (p.kind == HeadPlan::kZero) return launch_bias_fill(nullptr, 1, N, logits, stream);
+    if (p.kind == HeadPlan::kWhole) {
+        const int cw = 16 * p.lanes_per_row;
+        const dim3 grid((unsigned)((N + cw - 1) / cw));
+        const bool al = (ldq % 16) == 0;
+#define W4_HEAD_WHOLE(LV, LPRV, WVV)                                                            \
+    if (p.rows_per_lane == LV && p.lanes_per_row == LPRV && p.waves == WVV) {                   \
+        if (al)                                                                                 \
+            hipLaunchKernelGGL((k_head_whole<LV, true, LPRV, WVV>), grid, dim3(64 * WVV), 0,      \
+                               stream, x, (int)K, Q, ldq, hs, (int)N, logits);                  \
+        else                                                                                    \
+            hipLaunchKernelGGL((k_head_whole<LV, false, LPRV, WVV>), grid, dim3(64 * WVV), 0,     \
+                               stream, x, (int)K, Q, ldq, hs, (int)N, logits);                  \
+        return hipGetLastError();                                                               \
+    }
+        W4_HEAD_WHOLE(4, 16, 16) W4_HEAD_WHOLE(8, 16, 16) W4_HEAD_WHOLE(12, 16, 16)
+        W4_HEAD_WHOLE(16, 16, 16)
+        W4_HEAD_WHOLE(4, 8, 8) W4_HEAD_WHOLE(8, 8, 8) W4_HEAD_WHOLE(12, 8, 8) W4_HEAD_WHOLE(16, 8, 8)
+#undef W4_HEAD_WHOLE
+        return hipErrorInvalidValue;
+    }
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const dim3 grid((unsigned)(p.tiles * p.splits));
     const bool aligned = (ldq % 16) == 0;

@@ -74,6 +74,27 @@ HeadPlan plan_head(int64_t K, int64_t N) {
         p.kind = HeadPlan::kZero;
         return p;
     }
+    // The whole-K kernel wherever K is 256, 512, 768 or 1024 (L = K / 64 rows
+    // per lane): 16 waves per 256 columns (16 lanes per row) where that forms
+    // at least 128 workgroups, else 8 waves per 128 columns (8 lanes per row).
+    // GPT-2's 768 x 50257 (8 cold copies read in turn, us per head for
+    // ldq 50257 / 50272): split-K kernel and its reduce 18.9 / 15.9; whole-K
+    // with (lanes per row, waves) = (8, 8) 14.5 / 12.8, (4, 8) 20.3 / 18.3,
+    // (16, 8) 12.3 / 10.9, (8, 16) 14.1 / 12.8, (8, 4) 15.8 / 14.4, (4, 16)
+    // 20.8 / 19.3, (16, 16) 11.4 / 10.2: wider rows per instruction win.
+    // W4_HEAD_WHOLE=0: the split-K kernel always.
+    static const int64_t env_whole = env_int_or("W4_HEAD_WHOLE", 1);
+    const int64_t L = K / 64;
+    if (env_whole != 0 && K % 64 == 0 && (L == 4 || L == 8 || L == 12 || L == 16) &&
+        N >= 128 * 128 && N < ((int64_t)1 << 31)) {
+        const bool wide = N >= 128 * 256;
+        p.kind = HeadPlan::kWhole;
+        p.rows_per_lane = (int)L;
+        p.lanes_per_row = wide ? 16 : 8;
+        p.waves = wide ? 16 : 8;
+        p.workspace = 0;
+        return p;
+    }
     static const int64_t env_waves = env_int("W4_HEAD_WAVES");
     p.kind = HeadPlan::kRun;
     p.waves = (env_waves == 1 || env_waves == 2 || env_waves == 4) ? (int)env_waves : 1;

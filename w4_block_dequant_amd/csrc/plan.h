@@ -34,10 +34,14 @@ GemvPlan plan_gemv(int64_t K, int64_t N);
 // ---- int8 head logits (last row) -------------------------------------------
 // Same geometry as the GEMV: a lane owns 16 columns (16 bytes of a row) and
 // 32 rows; 16 lanes make a 256-column tile; 4 lane groups per wave.
+// kWhole: one workgroup of `waves` waves per 16 * lanes_per_row columns over
+// all K = rows_per_lane * waves * 64 / lanes_per_row rows, one launch, no
+// workspace.
 struct HeadPlan {
-    enum Kind { kEmpty = 0, kZero = 1, kRun = 2 } kind;
+    enum Kind { kEmpty = 0, kZero = 1, kRun = 2, kWhole = 3 } kind;
     int64_t tiles = 0, splits = 1, rows_per_wg = 0, npad = 0;
     int waves = 1;
+    int rows_per_lane = 0, lanes_per_row = 8;
     size_t workspace = 0;
 };
 
