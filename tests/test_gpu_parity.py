@@ -399,6 +399,33 @@ def test_head_kmajor_isolated_outlier(factor):
         assert_bound(got[m], ref, bound, f"head rows outlier x{factor:g} row {m}")
 
 
+@pytest.mark.parametrize("ldq", [32771, 32784])
+def test_head_whole_special_inputs(ldq):
+    """The [K, ldq] table's one-launch kernel (K = 768, 256-column workgroups)
+    on special activations: exact zeros, tiny and huge magnitudes, decades of
+    spread, and one entry 1e12 above the rest on a code row that is zero for
+    half the tokens."""
+    K, N = 768, 32769
+    E = synth.head_table(K, N, cfg=233)
+    E[100, : N // 2] = 0.0
+    Q, hs = ORC.i8_quantize_head(E, ldq=ldq)
+    base = synth.activations(1, K, cfg=234)[0]
+    spread = base.copy()
+    spread[::7] *= np.float32(1000.0)
+    spread[3::7] *= np.float32(1e-3)
+    outlier = base.copy()
+    outlier[100] *= np.float32(1e12)
+    cases = {"zeros": np.zeros(K, np.float32), "tiny": base * np.float32(1e-30),
+             "huge": base * np.float32(1e30), "spread": spread, "isolated outlier": outlier,
+             "one-hot": np.eye(1, K, 17, dtype=np.float32)[0]}
+    Qd, hsd = dev(Q), dev(hs)
+    for name, x in cases.items():
+        note(f"head whole ldq={ldq} x={name}")
+        logits = host(w4.i8_head_logits(dev(x.astype(np.float32)), Qd, hsd))
+        ref, bound = ORC.i8_head_logits(x.astype(np.float32), Q, hs)
+        assert_bound(logits, ref, bound, f"head whole ldq={ldq} x={name}")
+
+
 def test_head_kmajor_nonfinite_gives_nan():
     K, N = 128, 50
     Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=228), ldq=N)
