@@ -1014,9 +1014,13 @@ def summarize_profiles(src: str, out_dir: str):
              "`k_gemv_kmajor<rows, passes, ragged, lane mode, fp16 scales, epilogue, affine, "
              "whole-run x>` the K-major GEMV (lane mode 2: 32-lane halves summed in "
              "registers), `k_mm_x3<MT, NT, QPW, DQ, fp16 scales>` the bf16 matrix-core "
-             "matmul for M >= 3 with MT tiles of 16 rows, `k_gemv_fast` + `k_splitk_reduce` the "
+             "matmul for M >= 3 with MT tiles of 16 rows (split-K), `k_mm_x3k<row block, "
+             "column tiles per wave, waves, quads ahead, fp16 scales, three parts in one MFMA, "
+             "quads per wave if fixed>` its whole-K form, `k_gemv_fast` + `k_splitk_reduce` the "
              "canonical-layout GEMV, `k_mm_mfma` the canonical fp32 matrix-core matmul, "
-             "`k_head_fp32` the last-row head, `k_head_rows_x3` the full-sequence head, "
+             "`k_head_fp32` the token-major last-row head, `k_head_whole<rows per lane, "
+             "16-byte rows, lanes per row, waves>` the last-row head on the [K, ldq] table, "
+             "`k_head_rows_x3` the full-sequence head, "
              "`k_read_bytes` the launch floor's streaming read.", "",
              "| kernel | calls | avg us | p10 us | median us | p90 us | min us | max us | total ms |",
              "|---|---|---|---|---|---|---|---|---|"]
