@@ -175,9 +175,9 @@ int w4_prepack_kmajor(const uint8_t *Wq, const float *scales, const uint8_t *zer
  * the block's scale is applied once per block and column.  This holds for
  * any finite x, whatever its range.  Non-finite x gives NaN outputs on this
  * path.  One workgroup takes 16 or 32 columns of up to 16 rows over all of
- * K (one launch, no workspace) when M <= 16 and N >= 2033, and also for
+ * K (one launch, no workspace) when M <= 16 and N >= 497, and also for
  * 17 to 128 rows, in groups of 16, on matrices of at most 2^22 weights
- * whose column and row groups number at least 128; otherwise it may split K across
+ * whose column and row groups number at least 32; otherwise it may split K across
  * workgroups and then needs a workspace of
  * w4_matmul_kmajor_workspace_bytes(M, K, N) bytes (0 when it does not):
  * device memory, 256-byte aligned, any contents, not shared with a call in

@@ -148,7 +148,8 @@ def test_entry_points_reject_before_any_hip_call():
     assert w4.w4_matmul_kmajor_workspace_bytes(2, 3072, 3072) == 0      # M = 2: the GEMV
     assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 3072) == 0      # M = 3: whole-K matrix cores
     assert w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 3072) == 0     # up to 16 rows
-    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 768) > 0        # too few columns: split-K
+    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 768) == 0       # 48 workgroups: still whole-K
+    assert w4.w4_matmul_kmajor_workspace_bytes(3, 3072, 256) > 0        # too few columns: split-K
     assert w4.w4_matmul_kmajor_workspace_bytes(17, 3072, 3072) > 0      # 17 rows: split-K
     # past 16 rows, small matrices (at most 2^22 weights): whole-K row groups
     assert w4.w4_matmul_kmajor_workspace_bytes(58, 768, 2304) == 0
@@ -156,14 +157,14 @@ def test_entry_points_reject_before_any_hip_call():
     assert w4.w4_matmul_kmajor_workspace_bytes(128, 3072, 768) == 0
     assert w4.w4_matmul_kmajor_workspace_bytes(129, 768, 768) > 0     # past 128 rows: split-K
     assert w4.w4_matmul_kmajor_workspace_bytes(58, 768, 16) > 0       # too few workgroups
-    need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 768)
+    need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 256)
     assert need > 0
     assert w4.w4_matmul_kmajor_workspace_bytes(1, 3072, 3072) == 0
     assert w4.w4_matmul_kmajor_workspace_bytes(16, 3008, 3072) == 0   # K % 128 != 0: GEMV path
-    assert km(A, 16, 3072, A, A, A, 768, None, A, None, 0) == w4.W4_ERR_WORKSPACE
-    assert km(A, 16, 3072, A, A, A, 768, None, A, A, need - 1) == w4.W4_ERR_WORKSPACE
-    assert km(A, 16, 3072, A, A, A, 768, None, A, A + 64, need) == w4.W4_ERR_MISALIGNED
-    assert km(A, 16, 3072, A, A, A, 768, None, A, A, need) == w4.W4_OK
+    assert km(A, 16, 3072, A, A, A, 256, None, A, None, 0) == w4.W4_ERR_WORKSPACE
+    assert km(A, 16, 3072, A, A, A, 256, None, A, A, need - 1) == w4.W4_ERR_WORKSPACE
+    assert km(A, 16, 3072, A, A, A, 256, None, A, A + 64, need) == w4.W4_ERR_MISALIGNED
+    assert km(A, 16, 3072, A, A, A, 256, None, A, A, need) == w4.W4_OK
     assert lib.w4_prepack_kmajor(A, A, A, 96, 16, A, A, A, None) == w4.W4_ERR_BAD_SHAPE
     # empty work succeeds without a device
     assert lib.w4_matmul(None, 0, 768, None, None, None, 768, None, None, None, 0, None) == w4.W4_OK
@@ -257,10 +258,10 @@ def test_f16_variant_checks():
     assert km(A, 1, 3072, A, A, A, 3072, None, A, None, 0) == w4.W4_OK
     assert km(A, 1, 96, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_BAD_SHAPE
     assert km(A, 1, 128, A, A + 8, A, 16, None, A, None, 0) == w4.W4_ERR_MISALIGNED
-    need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 768)
+    need = w4.w4_matmul_kmajor_workspace_bytes(16, 3072, 256)
     assert need > 0
-    assert km(A, 16, 3072, A, A, A, 768, None, A, None, 0) == w4.W4_ERR_WORKSPACE
-    assert km(A, 16, 3072, A, A, A, 768, None, A, A, need) == w4.W4_OK
+    assert km(A, 16, 3072, A, A, A, 256, None, A, None, 0) == w4.W4_ERR_WORKSPACE
+    assert km(A, 16, 3072, A, A, A, 256, None, A, A, need) == w4.W4_OK
     assert km(A, 16, 3072, A, A, A, 3072, None, A, None, 0) == w4.W4_OK   # whole-K: none
     assert lib.w4h_quantize_pack(A, 100, 64, A, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.w4h_quantize_pack(A, 64, 64, A, A + 2, A, None, None) == w4.W4_ERR_MISALIGNED

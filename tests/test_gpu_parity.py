@@ -653,7 +653,7 @@ def test_large_scales_do_not_overflow(M):
 
 
 def test_kmajor_matrix_cores_deterministic_with_dirty_workspace():
-    K, N, M = 3072, 768, 16
+    K, N, M = 3072, 256, 16   # 16 column tiles: the split-K kernel
     W = mixed_weights(K, N, cfg=234)
     P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
     x = dev(synth.activations(M, K, cfg=234))
@@ -666,7 +666,7 @@ def test_kmajor_matrix_cores_deterministic_with_dirty_workspace():
     assert_bits(y1, y2, "x3 repeat")
 
 
-# The whole-K matrix-core kernel (3 <= M <= 16 rows, N >= 2033: one
+# The whole-K matrix-core kernel (3 <= M <= 16 rows, N >= 497: one
 # workgroup per 16 columns, or 32 from 5 rows where N >= 16353, over all of
 # K, no workspace).  K = 128 and 256 leave waves of a workgroup with no
 # quads; 2050, 3080, 2344 and 16400 are ragged N (16400: two column tiles per

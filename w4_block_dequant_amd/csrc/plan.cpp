@@ -342,7 +342,13 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
         if (tpw == 2 && cdiv(N, 32) < 128) tpw = 1;
         const int64_t wgs = cdiv(N, 16 * tpw);
         const int64_t mgroups = cdiv(M, 16);
-        if (wgs * mgroups >= 128) {
+        // Narrow matrices form few workgroups; the whole-K kernel with more
+        // waves (below) still beats the split-K kernel and its reduce launch
+        // from 32 workgroups on (GPT-2 body, 12 x 4 matmuls: M = 4 0.260 ->
+        // 0.183 ms, M = 16 0.291 -> 0.238, M = 17 0.300 -> 0.256; 768 x 768
+        // and 3072 x 768 at M = 4, us per launch: 5.94 -> 3.17, 8.00 -> 5.79).
+        const int64_t nwg = wgs * mgroups;
+        if (nwg >= 32) {
             p.kind = X3Plan::kFullK;
             p.mb = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
             // up to 4 rows the three bf16 parts of each row are rows of one
@@ -359,6 +365,14 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
             // ones, while the arithmetic (about 6 VALU operations per weight)
             // could have started.
             p.waves = NQ <= 8 ? 4 : 8;
+            // Fewer than 256 workgroups: twice the waves, each with fewer
+            // quads, for grids below 128, for row groups and for short K
+            // (GPT-2 at M = 58, us per launch: 768 x 768 4.42 -> 3.92 with
+            // 8 waves, 3072 x 768 7.47 -> 7.13 with 16; at M = 4 768 x 2304
+            // 3.58 -> 3.24 with 8).  The 3.8B N = 3072 shapes (192 workgroups,
+            // K = 3072 or 8192) keep 8 (16 waves: 8192 x 3072 at M = 4 12.4 ->
+            // 14.0 us).
+            if (nwg < 256 && (nwg < 128 || M > 16 || NQ <= 8)) p.waves = NQ <= 8 ? 8 : 16;
             if (env_waves == 4 || env_waves == 8 || env_waves == 16) p.waves = (int)env_waves;
             if (p.nt == 2 && p.waves == 16) p.waves = 8;  // 1024 threads leave too few registers
             // quads of loads in flight per wave (0: the kernel's default for its row count)
