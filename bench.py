@@ -86,6 +86,10 @@ PROFILE_COMMANDS = (
     "timeout -s KILL 300 rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU "
     "SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --output-format csv "
     "-d /tmp/w4prof/sq -o run -- python bench.py --profile-run-mfma --steps 2",
+    "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/w4prof/fetch4 "
+    "-o run -- python bench.py --profile-run --profile-rows 4 --steps 2",
+    "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/w4prof/write4 "
+    "-o run -- python bench.py --profile-run --profile-rows 4 --steps 2",
     "python bench.py --summarize-profiles /tmp/w4prof --out profiles",
 )
 
@@ -253,6 +257,9 @@ def parse():
     p.add_argument("--profile-run", action="store_true",
                    help="short eager run for hardware counters: `--steps` M=1 passes, then "
                         "a plain copy of known size for calibration")
+    p.add_argument("--profile-rows", type=int, default=1,
+                   help="with --profile-run: rows of x in the profiled passes (4: the "
+                        "matrix-core kernels' traffic)")
     p.add_argument("--profile-run-mfma", action="store_true",
                    help="short eager run for matrix-core counters: `--steps` passes of the "
                         "3.8B body at M=4 (prepacked) and M=16 (both layouts) and of the "
@@ -397,11 +404,13 @@ def main():
 
     if args.profile_run:
         # eager passes (one dispatch per matmul), then the calibration copy
+        mats = dense if args.profile_rows == 1 else with_x(dense, synth.CFG_DENSE38,
+                                                           args.profile_rows, outliers=True)
         for _ in range(args.warmup):
-            run_pass(dense)
+            run_pass(mats)
         torch.cuda.synchronize()
         for i in range(args.steps):
-            run_pass(dense)
+            run_pass(mats)
             torch.cuda.synchronize()
             log(f"profile pass {i + 1} of {args.steps} done")
         src = torch.randn(COPY_FLOATS, device=dev)
@@ -411,6 +420,8 @@ def main():
             torch.neg(src, out=dst)      # reads and writes COPY_FLOATS * 4 bytes
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": True, "passes": args.steps, "launches_per_pass": len(dense),
+                          "rows": args.profile_rows,
+                          "bytes_per_pass": sum(m.bytes for m in mats),
                           "copy_bytes": COPY_FLOATS * 4}), flush=True)
         return
 
@@ -1116,6 +1127,36 @@ def summarize_profiles(src: str, out_dir: str):
                 f"{100 * c['SQ_WAIT_ANY'] / wc:.0f} | "
                 f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1.0):.2f} | "
                 f"{ns / len(ds) / 1e3:.2f} |")
+    # HBM traffic of the matrix-core kernels: the 3.8B pass at M = 4
+    # (`--profile-run --profile-rows 4`), FETCH_SIZE and WRITE_SIZE per
+    # dispatch scaled by the same run's copy kernel, against the pass's
+    # algorithmic bytes (weights once, x and y once) per launch
+    import synth
+    tr = {}
+    for sub, counter in (("fetch4", "FETCH_SIZE"), ("write4", "WRITE_SIZE")):
+        d = per_dispatch(sub, counter)
+        copy = [v for k, v in d if "neg_kernel" in k]
+        mm = [v for k, v in d if "k_mm_x3" in k]
+        if copy and mm:
+            factor = statistics.median(copy) * 1024.0 / copy_bytes
+            tr[sub] = (statistics.mean(mm) * 1024.0 / factor, len(mm), factor)
+    if len(tr) == 2:
+        shapes = synth.DENSE38_SHAPES
+        M4 = 4
+        alg = sum(K * N // 2 + (K // 32) * N * 4 + (K // 32) * N // 2 + 4 * M4 * K + 4 * M4 * N
+                  for K, N in shapes) / len(shapes)
+        fb, nf, ff = tr["fetch4"]
+        wb, _, wf = tr["write4"]
+        lines += ["", "HBM traffic of the matrix-core kernels, 3.8B pass at M = 4 "
+                  "(`--profile-run --profile-rows 4`: FETCH_SIZE, then WRITE_SIZE, per "
+                  "dispatch of `k_mm_x3k`, each scaled by the same run's copy kernel):", "",
+                  f"- dispatches_counted: {nf}",
+                  f"- fetch_factor: {ff:.5f}",
+                  f"- write_factor: {wf:.5f}",
+                  f"- fetch_bytes_per_launch: {fb:.0f}",
+                  f"- write_bytes_per_launch: {wb:.0f}",
+                  f"- algorithmic_bytes_per_launch: {alg:.0f}",
+                  f"- traffic_over_algorithmic: {(fb + wb) / alg:.4f}"]
     with open(os.path.join(out_dir, MFMA_SUMMARY), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(open(os.path.join(out_dir, MFMA_SUMMARY)).read())
