@@ -358,12 +358,13 @@ X3Plan plan_x3(int64_t M, int64_t K, int64_t N) {
             p.p3 = p.mb == 4 && env_p3 != 0;
             p.nt = (int)tpw;
             // 8 waves, each loading one quad ahead of its arithmetic; 4 where K
-            // is short.  3.8B pass (128 launches) at M = 4 / 8: 4 quads ahead
-            // 1.68 / 1.93 ms, 2 ahead 1.55 / 1.85, 1 ahead 1.50 / 1.77 ms (4 or
-            // 16 waves at 1 ahead: 1.87 / 1.71 ms at M = 4): a deep prefetch
-            // makes every wave's first quad wait behind the others' later
-            // ones, while the arithmetic (about 6 VALU operations per weight)
-            // could have started.
+            // is short.  3.8B pass (128 launches) at M = 4 / 8 in the runtime
+            // loop: 4 quads ahead 1.68 / 1.93 ms, 2 ahead 1.55 / 1.85, 1 ahead
+            // 1.50 / 1.77 ms (4 or 16 waves at 1 ahead: 1.87 / 1.71 ms at
+            // M = 4).  That loop waits for every load in flight at its head
+            // (its loads sit under a runtime condition), so depth there only
+            // costs registers; the straight-line kernels below (NQC) wait for
+            // each quad's own loads.
             p.waves = NQ <= 8 ? 4 : 8;
             // Fewer than 256 workgroups: twice the waves, each with fewer
             // quads, for grids below 128, for row groups and for short K
