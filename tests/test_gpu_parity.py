@@ -899,6 +899,28 @@ def test_kmajor_whole_k_row_groups(M, K, N, act):
     assert_bound(host(y), y_ref, bound, f"row groups {act} M={M} {K}x{N}")
 
 
+# Around the whole-K kernel's grid threshold (32 workgroups of 16 columns per
+# row group): 31 column tiles take the split-K kernel and its workspace, 32 the
+# whole-K kernel (with 8 or 16 waves on these narrow grids); M = 20 forms two
+# row groups of 16.
+@pytest.mark.parametrize("M,K,N,whole", [(4, 768, 496, False), (4, 768, 498, True),
+                                         (16, 3072, 496, False), (16, 3072, 528, True),
+                                         (20, 768, 240, False), (20, 768, 256, True),
+                                         (3, 8192, 512, True)])
+def test_kmajor_grid_threshold(M, K, N, whole):
+    ws = w4.w4_matmul_kmajor_workspace_bytes(M, K, N)
+    assert (ws == 0) == whole, f"workspace {ws} for M={M} K={K} N={N}"
+    note(f"grid threshold M={M} K={K} N={N} whole={whole}")
+    W = mixed_weights(K, N, cfg=283)
+    x = synth.activations(M, K, cfg=283, slot=M, outliers=True)
+    b = synth.bias(N, cfg=283)
+    Wq, s, z = ORC.quantize_pack(W)
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z, b)
+    P = w4.w4_prepack_kmajor(dev(Wq), dev(s), dev(z))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P, bias=dev(b)))
+    assert_bound(y, y_ref, bound, f"grid threshold M={M} {K}x{N}")
+
+
 # --------------------------------------------------------------------------
 # fused epilogues (GELU, SwiGLU on interleaved gate/up columns, residual add)
 # --------------------------------------------------------------------------
