@@ -244,7 +244,12 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
     // loads per column and cost nothing while at least 128 workgroups remain
     // (GPT-2 768 x 2304, 768 x 3072, 3072 x 768: 3.6-3.9 -> 3.3-3.4 us; at
     // 768 x 768 two passes would leave 48 workgroups and are slower)
-    if (env_p <= 0 && p.rows == 1 && p.passes == 1 &&
+    // Not where two column slots can share one read of the activations at
+    // one pass with at least 256 workgroups (below): GPT-2 3072 x 768 3.45 us
+    // with two passes, 3.28 with one pass and the shared activations.
+    const bool shared1 = p.groups == 2 && p.lanes_per_col == NB && NB % 8 == 0 &&
+                         p.threads == 2 * p.lanes_per_col && cdiv(N, 2) >= 256;
+    if (env_p <= 0 && p.rows == 1 && p.passes == 1 && !shared1 &&
         cdiv(N, (int64_t)p.groups * 2) * cdiv(M, p.rows) >= 128)
         p.passes = 2;
     // an odd column count only arises with one column slot and 1 or 3 passes
@@ -286,7 +291,7 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
                 const int64_t wgs = cdiv(N, 2 * (int64_t)P);
                 if (wgs >= 512 && (!even || wgs % 256 == 0)) return P;
             }
-        return 0;
+        return cdiv(N, 2) >= 256 ? 1 : 0;  // small N: one pass, still shared
     };
     if (p.xc && env_xs != 0 && p.rows <= 2 && p.groups == 2 &&
         p.lanes_per_col == NB && p.lanes_per_col % 8 == 0 && p.threads == 2 * p.lanes_per_col) {
