@@ -171,8 +171,10 @@ KmajorPlan plan_kmajor(int64_t M, int64_t K, int64_t N, bool even_cols) {
             threads = 64 * w;
             break;
         }
-    static const int64_t env_half = env_int_or("W4_KMAJOR_HALF", 1);
-    if (env_half != 0 && p.rows <= 2 && NB > 16 && NB <= 32) {
+    // (Always, for 17 to 32 blocks: the general branch below would give
+    // K = 1024 64-thread workgroups of two 32-lane column slots, a layout
+    // that produced wrong results in parity tests and is not used.)
+    if (p.rows <= 2 && NB > 16 && NB <= 32) {
         // 17 to 32 blocks: one 32-lane half per column (the lanes past NB
         // idle), whose sum stays in registers and is stored by its last
         // lane: no LDS and no barrier for the sums.  GPT-2's K = 768.
