@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary]
                     [--kernel kmajor|canonical]   (or W4_KERNEL=...)
+    python bench.py --probes      (launch cost and streaming-read rates only)
 
 The step is one decode body pass of the 3.8B-dense-shaped model at M = 1:
 32 layers x 4 W4 matmuls (3072x9216 QKV, 3072x3072 out, 3072x16384
@@ -267,7 +268,60 @@ def parse():
     p.add_argument("--summarize-profiles", metavar="DIR", default=None,
                    help="turn rocprofv3 CSV output under DIR into the profile summaries")
     p.add_argument("--out", default=PROFILE_DIR, help="where --summarize-profiles writes")
+    p.add_argument("--probes", action="store_true",
+                   help="only the machine probes behind the launch-cost and streaming-rate "
+                        "figures: near-empty launches in a graph, and one streaming-read "
+                        "launch per buffer at 6 MiB to 1 GiB (one JSON line)")
     return p.parse_args()
+
+
+PROBE_MIB = (6, 16, 32, 64, 256, 1024)
+PROBE_POOL_BYTES = 2 << 30     # buffers rotated per size: 8x the 256 MB Infinity Cache
+
+
+def probes(w4, torch, dev, capture, time_graph, log, args):
+    """Launch cost and single-launch streaming rate, with the library's own
+    streaming-read kernel (w4_read_bytes), so that the figures the design
+    notes quote can be measured again from committed code."""
+    words = max(w4._lib.w4_read_bytes_words(n << 20, L) for n in PROBE_MIB for L in FLOOR_LOADS)
+    out = torch.empty(words, dtype=torch.int32, device=dev)
+    steps = max(5, args.steps // 2)
+
+    # a launch that reads 16 bytes (one workgroup): the fixed cost of a graph node
+    tiny = torch.zeros(16, dtype=torch.uint8, device=dev)
+    launch = {}
+    for n in (1, 32, 128):
+        g = capture(lambda n=n: [w4.w4_read_bytes(tiny, 4, out=out) for _ in range(n)])
+        ms, _ = time_graph(g, steps, 2)
+        del g
+        launch[str(n)] = round(1e3 * ms / n, 3)
+    log(f"near-empty launch, us per node by graph length: {launch}")
+
+    stream = {}
+    for mib in PROBE_MIB:
+        nbytes = mib << 20
+        nbuf = max(2, PROBE_POOL_BYTES // nbytes)
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        best = None
+        for L in FLOOR_LOADS:
+            g = capture(lambda L=L: [w4.w4_read_bytes(b, L, out=out) for b in bufs])
+            ms, _ = time_graph(g, steps, 2)
+            del g
+            us = 1e3 * ms / nbuf
+            if best is None or us < best[0]:
+                best = (us, L)
+        del bufs
+        torch.cuda.empty_cache()
+        us, L = best
+        stream[f"{mib}MiB"] = {"us_per_launch": round(us, 3), "loads_per_lane": L,
+                               "TB_s": round(nbytes / (us * 1e-6) / 1e12, 3),
+                               "buffers_rotated": nbuf}
+        log(f"streaming read {mib} MiB: {stream[f'{mib}MiB']}")
+    line = {"probes": "w4_read_bytes", "device": torch.cuda.get_device_name(dev),
+            "graph_replays": steps,
+            "near_empty_launch_us_per_node": launch,
+            "streaming_read_one_launch": stream}
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -396,6 +450,10 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
+
+    if args.probes:
+        probes(w4, torch, dev, capture, time_graph, log, args)
+        return
 
     log("building the 3.8B-dense-shaped body (2.32 GB packed) ...")
     t = time.perf_counter()
