@@ -755,9 +755,11 @@ def test_kmajor_whole_k_large_scales_and_f16():
 
 
 @pytest.mark.parametrize("slot", range(4))
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
 def test_dense38_kmajor_full_size_sampled(slot, M):
-    """Full-size 3.8B-dense shapes on the K-major path the benchmark times."""
+    """Full-size 3.8B-dense shapes on the K-major path the benchmark times
+    (M = 1, 4 and 16), and at 2 rows (the two-row GEMV) and 8 (the whole-K
+    kernel's 8-row blocks)."""
     K, N = synth.DENSE38_SHAPES[slot]
     note(f"dense38 kmajor slot {slot} M={M} K={K} N={N} (sampled columns)")
     W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=0, slot=slot)
