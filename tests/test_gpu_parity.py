@@ -773,6 +773,54 @@ def test_dense38_kmajor_full_size_sampled(slot, M):
     assert_bound(y[:, cols], y_ref, bound, f"dense38 kmajor {K}x{N} M={M}")
 
 
+@pytest.mark.parametrize("slot", range(4))
+@pytest.mark.parametrize("M", [1, 4])
+def test_f16_dense38_full_size_sampled(slot, M):
+    """The fp16-scale format at the full 3.8B-dense shapes the benchmark times:
+    the GPU quantizer's sampled bytes bit-exact, the matmul within the bound."""
+    K, N = synth.DENSE38_SHAPES[slot]
+    note(f"f16 dense38 slot {slot} M={M} K={K} N={N} (sampled columns)")
+    W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=0, slot=slot)
+    x = synth.activations(M, K, cfg=synth.CFG_DENSE38, layer=0, slot=slot, outliers=True)
+    Wq_d, s_d, z_d = w4.w4h_quantize_pack(dev(W))
+    y = host(w4.w4_matmul_kmajor(dev(x), *w4.w4h_prepack_kmajor(Wq_d, s_d, z_d)))
+    pairs = sample_pairs(N, 48, seed=30 + slot)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    Wq, s16, z = ORC.quantize_pack_f16(W[:, cols])
+    assert_bits(host(Wq_d)[:, pairs], Wq, "sampled Wq (fp16 scales)")
+    assert_bits(f16_bits(s_d)[:, cols], s16, "sampled fp16 scales")
+    assert_bits(host(z_d)[:, pairs], z, "sampled zeros (fp16 scales)")
+    y_ref, bound = ORC.w4h_matmul(x, Wq, s16, z)
+    assert_bound(y[:, cols], y_ref, bound, f"f16 dense38 {K}x{N} M={M}")
+
+
+# The benchmark's fused-epilogue pass at full size: SwiGLU on the gate+up
+# matrix (interleaved gate/up columns, half as many outputs), the residual
+# added in place on the out- and down-projections.
+@pytest.mark.parametrize("slot,act,res", [(2, "swiglu", False), (1, "none", True),
+                                          (3, "none", True)])
+def test_ep_dense38_full_size_sampled(slot, act, res):
+    K, N = synth.DENSE38_SHAPES[slot]
+    note(f"epilogue dense38 slot {slot} act={act} residual={res} K={K} N={N} (sampled columns)")
+    W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=0, slot=slot)
+    x = synth.activations(1, K, cfg=synth.CFG_DENSE38, layer=0, slot=slot, outliers=True)
+    P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
+    pairs = sample_pairs(N, 48, seed=40 + slot)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    if act == "swiglu":
+        y = host(w4.w4_matmul_kmajor(dev(x), *P, act="swiglu"))
+        assert y.shape == (1, N // 2)
+        r_s, y_s = None, y[:, pairs]
+    else:
+        r = synth.activations(1, N, cfg=synth.CFG_DENSE38, layer=1, slot=slot)
+        yr = dev(r)
+        w4.w4_matmul_kmajor(dev(x), *P, residual=yr, out=yr)
+        r_s, y_s = r[:, cols], host(yr)[:, cols]
+    Wq, s, z = ORC.quantize_pack(W[:, cols])
+    y_ref, bound = ORC.w4_matmul_ep(x, Wq, s, z, None, r_s, act=act)
+    assert_bound(y_s, y_ref, bound, f"epilogue dense38 {act} {K}x{N}")
+
+
 def test_kmajor_rejects_bad_shapes():
     lib = w4.library()
     A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
