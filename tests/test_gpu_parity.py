@@ -192,7 +192,7 @@ def sample_pairs(N, count, seed):
 
 
 @pytest.mark.parametrize("slot", range(4))
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 4, 16])
 def test_dense38_full_size_sampled(slot, M):
     """Full-size 3.8B-dense shapes in the benchmark's launch configuration."""
     K, N = synth.DENSE38_SHAPES[slot]
