@@ -303,3 +303,14 @@ def test_g64_checks():
         assert lib.w4g_matmul_kmajor(A, 1, 64, A, A, A, 8, None, A, None) == w4.W4_ERR_DEVICE
     assert lib.w4g_quantize_pack(A, 96, 8, A, A, A, None, None) == w4.W4_ERR_BAD_SHAPE
     assert lib.w4g_dequantize(A, A, A, 64, 8, A + 4, None) == w4.W4_ERR_MISALIGNED
+
+
+def test_kmajor_index_limit():
+    """The K-major path indexes in 32 bits: K * N, M * K and M * N below 2^31
+    are accepted and 2^31 is refused, before any HIP call."""
+    km = w4.library().w4_check_matmul_kmajor_args
+    K = 8192
+    assert km(A, 1, K, A, A, A, 262128, None, A, None, 0) == w4.W4_OK      # K N = 2^31 - 131072
+    assert km(A, 4, K, A, A, A, 262128, None, A, None, 0) == w4.W4_OK      # whole-K: no workspace
+    assert km(A, 1, K, A, A, A, 262144, None, A, None, 0) == w4.W4_ERR_BAD_SHAPE  # K N = 2^31
+    assert km(A, 262144, K, A, A, A, 16, None, A, None, 0) == w4.W4_ERR_BAD_SHAPE  # M K = 2^31

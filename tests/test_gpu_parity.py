@@ -821,6 +821,38 @@ def test_ep_dense38_full_size_sampled(slot, act, res):
     assert_bound(y_s, y_ref, bound, f"epilogue dense38 {act} {K}x{N}")
 
 
+# At the 32-bit indexing limit of the K-major kernels: K N = 2^31 - 131072
+# (K = 8192, N = 262128).  The weights (8.6 GB of fp32) are drawn on the
+# device from a seeded torch generator, quantized and prepacked on the GPU,
+# and checked on sampled column pairs, the last pair included: the sampled
+# bytes bit-exact, the outputs within the bound.
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_kmajor_index_limit_sampled(M):
+    K, N = 8192, 262128
+    assert K * N < 2 ** 31 and K * (N + 16) >= 2 ** 31 - 2 ** 16
+    note(f"kmajor index limit M={M} K={K} N={N} (sampled columns)")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1_000_003)
+    W_d = torch.randn((K, N), generator=g, device=DEV, dtype=torch.float32).mul_(0.02)
+    Wq_d, s_d, z_d = w4.w4_quantize_pack(W_d)
+    pairs = sample_pairs(N, 48, seed=50)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    pairs_t = torch.from_numpy(pairs).to(DEV)
+    cols_t = torch.from_numpy(cols).to(DEV)
+    W = host(W_d[:, cols_t])
+    del W_d
+    Wq, s, z = ORC.quantize_pack(W)
+    assert_bits(host(Wq_d[:, pairs_t]), Wq, "sampled Wq at the index limit")
+    assert_bits(host(s_d[:, cols_t]), s, "sampled scales at the index limit")
+    assert_bits(host(z_d[:, pairs_t]), z, "sampled zeros at the index limit")
+    P = w4.w4_prepack_kmajor(Wq_d, s_d, z_d)
+    del Wq_d, s_d, z_d
+    x = synth.activations(M, K, cfg=synth.CFG_DENSE38, layer=2, slot=M, outliers=True)
+    y = host(w4.w4_matmul_kmajor(dev(x), *P))
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    assert_bound(y[:, cols], y_ref, bound, f"kmajor index limit M={M}")
+
+
 def test_kmajor_rejects_bad_shapes():
     lib = w4.library()
     A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
