@@ -337,6 +337,42 @@ def test_head_prepack_bit_exact(K, N, ldq, ldt):
     assert_bits(host(Qt), token_major(Q, N, ldt), f"head token-major {K}x{N}")
 
 
+# The int8 head at its largest token count: the token-major table Qt [N, 768]
+# one row short of 2^31 bytes (N = 2^31 / 768 - 1), and the [K, ldq] table
+# past 2^31 bytes (64-bit offsets; ldq odd or a multiple of 16).  The fp32
+# table (8.6 GB) is drawn on the device from a seeded torch generator; the
+# quantizer's sampled bytes and scales are bit-exact, both heads' sampled
+# logits within the bound (the last 20 tokens always among the samples).
+@pytest.mark.parametrize("pad", [16, 23])
+def test_head_index_limit_sampled(pad):
+    K, N = 768, 2 ** 31 // 768 - 1
+    ldq = N + pad
+    assert N * K < 2 ** 31 and K * ldq > 2 ** 31
+    note(f"head index limit K={K} N={N} ldq={ldq} (sampled tokens)")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2_000_003 + pad)
+    E_d = torch.randn((K, N), generator=g, device=DEV, dtype=torch.float32).mul_(0.02)
+    Q_d, hs_d = w4.i8_quantize_head(E_d, ldq=ldq)
+    rng = np.random.default_rng(60 + pad)
+    idx = np.unique(np.concatenate([rng.choice(N, 76, replace=False),
+                                    np.arange(N - 20, N), [0]])).astype(np.int64)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    E = host(E_d[:, idx_t])
+    del E_d
+    Q, hs = ORC.i8_quantize_head(E, ldq=len(idx))
+    assert_bits(host(Q_d[:, idx_t]), Q, "sampled head codes at the index limit")
+    assert_bits(host(hs_d[idx_t]), hs, "sampled head scales at the index limit")
+    x = synth.activations(58, K, cfg=synth.CFG_HEAD, outliers=True)[-1]
+    ref, bound = ORC.i8_head_logits(x, Q, hs)
+    logits = host(w4.i8_head_logits(dev(x), Q_d, hs_d))
+    assert_bound(logits[idx], ref, bound, f"[K, ldq] head at the index limit, ldq={ldq}")
+    Qt = w4.i8_prepack_head(Q_d, N, ldt=K)
+    del Q_d
+    assert_bits(host(Qt[idx_t]), np.ascontiguousarray(Q.T), "sampled token-major rows")
+    logits_t = host(w4.i8_head_logits_kmajor(dev(x), Qt, hs_d, K))
+    assert_bound(logits_t[idx], ref, bound, "token-major head at the index limit")
+
+
 def head_kmajor_case(K, N, ldt, x, label):
     cfg = synth.CFG_HEAD if (K, N) == (768, 50257) else 222
     E = synth.head_table(K, N, cfg=cfg)
