@@ -212,6 +212,36 @@ def test_dense38_full_size_sampled(slot, M):
     assert_bound(y[:, cols], y_ref, bound, f"dense38 {K}x{N} M={M}")
 
 
+# The canonical layout indexes in 64 bits: a matrix past 2^31 weights
+# (K = 8192, N = 262160, a ragged last 256-column tile), drawn on the device
+# from a seeded torch generator (8.6 GB of fp32), checked on sampled column
+# pairs (the last pair included): packed bytes bit-exact, outputs within the
+# bound, through the decode GEMV (M = 1) and the fp32 matrix cores (M = 4).
+@pytest.mark.parametrize("M", [1, 4])
+def test_canonical_past_2_31_sampled(M):
+    K, N = 8192, 262160
+    assert K * N > 2 ** 31
+    note(f"canonical past 2^31 M={M} K={K} N={N} (sampled columns)")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3_000_017)
+    W_d = torch.randn((K, N), generator=g, device=DEV, dtype=torch.float32).mul_(0.02)
+    Wq_d, s_d, z_d = w4.w4_quantize_pack(W_d)
+    pairs = sample_pairs(N, 48, seed=70)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    pairs_t = torch.from_numpy(pairs).to(DEV)
+    cols_t = torch.from_numpy(cols).to(DEV)
+    W = host(W_d[:, cols_t])
+    del W_d
+    Wq, s, z = ORC.quantize_pack(W)
+    assert_bits(host(Wq_d[:, pairs_t]), Wq, "sampled Wq past 2^31")
+    assert_bits(host(s_d[:, cols_t]), s, "sampled scales past 2^31")
+    assert_bits(host(z_d[:, pairs_t]), z, "sampled zeros past 2^31")
+    x = synth.activations(M, K, cfg=synth.CFG_DENSE38, layer=3, slot=M, outliers=True)
+    y = host(w4.w4_matmul(dev(x), Wq_d, s_d, z_d))
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    assert_bound(y[:, cols], y_ref, bound, f"canonical past 2^31 M={M}")
+
+
 def test_matmul_empty_and_bias_only():
     K, N = 64, 32
     W = synth.weights(K, N, cfg=212)
