@@ -1273,3 +1273,35 @@ def test_read_bytes_xor_words(nbytes, loads):
     want = np.zeros(words, np.uint32)
     np.bitwise_xor.at(want, grp, np.bitwise_xor.reduce(pieces, axis=1))
     assert np.array_equal(out[:words].view(np.uint32), want)
+
+
+def test_empty_inputs_on_every_entry_point():
+    """Zero rows, columns, K or tokens: every entry point returns empty (or
+    bias-only) results of the right shape and enqueues no failing work."""
+    K, N = 128, 64
+    W = synth.weights(K, N, cfg=290)
+    # the quantizer and the K-major prepack on no rows and on no columns
+    Wq0, s0, z0 = w4.w4_quantize_pack(torch.zeros((0, N), device=DEV))
+    assert (Wq0.shape, s0.shape, z0.shape) == ((0, N // 2), (0, N), (0, N // 2))
+    WqN, sN, zN = w4.w4_quantize_pack(torch.zeros((K, 0), device=DEV))
+    assert (WqN.shape, sN.shape, zN.shape) == ((K, 0), (K // 32, 0), (K // 32, 0))
+    P0 = w4.w4_prepack_kmajor(WqN, sN, zN)
+    assert tuple(p.shape[0] for p in P0) == (0, 0, 0)
+    # the K-major matmul on no rows and on no columns
+    P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
+    assert w4.w4_matmul_kmajor(torch.zeros((0, K), device=DEV), *P).shape == (0, N)
+    assert w4.w4_matmul_kmajor(torch.zeros((16, K), device=DEV), *P0).shape == (16, 0)
+    assert w4.w4_matmul(torch.zeros((2, K), device=DEV), WqN, sN, zN).shape == (2, 0)
+    # the int8 head: no tokens in the table, no rows, no tokens to look up
+    E = synth.head_table(K, 40, cfg=290)
+    Q, hs = w4.i8_quantize_head(dev(E))
+    Qz, hz = w4.i8_quantize_head(torch.zeros((K, 0), device=DEV))
+    assert Qz.shape == (K, 0) and hz.shape == (0,)
+    x = dev(synth.activations(1, K, cfg=290)[0])
+    assert w4.i8_head_logits(x, Qz, hz).shape == (0,)
+    Qt = w4.i8_prepack_head(Q, 40)
+    assert w4.i8_head_logits_rows(torch.zeros((0, K), device=DEV), Qt, hs).shape == (0, 40)
+    tok = torch.zeros(0, dtype=torch.int64, device=DEV)
+    assert w4.i8_embed(tok, Q, hs).shape == (0, K)
+    assert w4.i8_embed_kmajor(tok, Qt, hs, K).shape == (0, K)
+    torch.cuda.synchronize()
