@@ -919,6 +919,34 @@ def test_kmajor_index_limit_sampled(M):
     assert_bound(y[:, cols], y_ref, bound, f"kmajor index limit M={M}")
 
 
+# The fp16-scale and group-64 affine formats at the same indexing limit
+# (M = 1, the decode GEMV's instantiations for those formats).
+@pytest.mark.parametrize("fmt", ["fp16 scales", "group-64 affine"])
+def test_formats_index_limit_sampled(fmt):
+    K, N = 8192, 262128
+    note(f"{fmt} index limit K={K} N={N} (sampled columns)")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4_000_037)
+    W_d = torch.randn((K, N), generator=g, device=DEV, dtype=torch.float32).mul_(0.02)
+    pairs = sample_pairs(N, 48, seed=80)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    W = host(W_d[:, torch.from_numpy(cols).to(DEV)])
+    x = synth.activations(1, K, cfg=synth.CFG_DENSE38, layer=4, slot=0, outliers=True)
+    if fmt == "fp16 scales":
+        P = w4.w4h_prepack_kmajor(*w4.w4h_quantize_pack(W_d))
+        del W_d
+        y = host(w4.w4_matmul_kmajor(dev(x), *P))
+        Wq, s16, z = ORC.quantize_pack_f16(W)
+        y_ref, bound = ORC.w4h_matmul(x, Wq, s16, z)
+    else:
+        P = w4.w4g_prepack_kmajor(*w4.w4g_quantize_pack(W_d))
+        del W_d
+        y = host(w4.w4g_matmul_kmajor(dev(x), *P))
+        Wq, sg, mg = ORC.quantize_pack_g64(W)
+        y_ref, bound = ORC.w4g_matmul(x, Wq, sg, mg)
+    assert_bound(y[:, cols], y_ref, bound, f"{fmt} at the index limit")
+
+
 def test_kmajor_rejects_bad_shapes():
     lib = w4.library()
     A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
