@@ -522,6 +522,25 @@ def test_head_rows(M, K, N, ldt):
     assert_bound(got, ref, bound, f"head rows {M}x{K}x{N}")
 
 
+# A long prefill through the full-sequence head: 1024 rows (and a ragged
+# 1000) of the GPT-2 head, checked against the oracle on sampled tokens (the
+# last 20 among them) for every row.
+@pytest.mark.parametrize("M", [1024, 1000])
+def test_head_rows_long_sequence_sampled(M):
+    K, N = 768, 50257
+    note(f"head rows long sequence M={M} K={K} N={N} (sampled tokens)")
+    Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=synth.CFG_HEAD), ldq=N)
+    x = synth.activations(M, K, cfg=291, outliers=True)
+    got = host(w4.i8_head_logits_rows(dev(x), dev(token_major(Q, N, K)), dev(hs)))
+    assert got.shape == (M, N)
+    rng = np.random.default_rng(291)
+    idx = np.unique(np.concatenate([rng.choice(N, 60, replace=False), np.arange(N - 20, N), [0]]))
+    Qs, hss = np.ascontiguousarray(Q[:, idx]), np.ascontiguousarray(hs[idx])
+    for m in range(M):
+        ref, bound = ORC.i8_head_logits(x[m], Qs, hss)
+        assert_bound(got[m, idx], ref, bound, f"head rows long sequence row {m}")
+
+
 def test_head_rows_special_rows():
     K, N, M = 768, 2000, 6
     Q, hs = ORC.i8_quantize_head(synth.head_table(K, N, cfg=230), ldq=N)
