@@ -966,6 +966,23 @@ def test_formats_index_limit_sampled(fmt):
     assert_bound(y[:, cols], y_ref, bound, f"{fmt} at the index limit")
 
 
+# A long prefill on the K-major matrix cores: 1024 rows (and a ragged 1000)
+# of the 3.8B QKV shape, sampled columns checked for every row.
+@pytest.mark.parametrize("M", [1024, 1000])
+def test_kmajor_long_prefill_sampled(M):
+    K, N = synth.DENSE38_SHAPES[0]
+    note(f"kmajor long prefill M={M} K={K} N={N} ws={w4.w4_matmul_kmajor_workspace_bytes(M, K, N)}")
+    W = synth.weights(K, N, cfg=synth.CFG_DENSE38, layer=5, slot=0)
+    x = synth.activations(M, K, cfg=synth.CFG_DENSE38, layer=5, slot=0, outliers=True)
+    P = w4.w4_prepack_kmajor(*w4.w4_quantize_pack(dev(W)))
+    y = host(w4.w4_matmul_kmajor(dev(x), *P))
+    pairs = sample_pairs(N, 32, seed=90)
+    cols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+    Wq, s, z = ORC.quantize_pack(W[:, cols])
+    y_ref, bound = ORC.w4_matmul(x, Wq, s, z)
+    assert_bound(y[:, cols], y_ref, bound, f"kmajor long prefill M={M}")
+
+
 def test_kmajor_rejects_bad_shapes():
     lib = w4.library()
     A = torch.zeros(64, dtype=torch.uint8, device=DEV).data_ptr()
